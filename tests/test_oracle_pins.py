@@ -1,0 +1,461 @@
+"""Pins for the CPU oracle: it is checked against what the pages and the
+mathematics fix, never against itself.
+
+Each pin_* function takes an oracle-like namespace, so the same pins also run
+against deliberately broken copies of oracle functions (planted on the CPU, at
+the bottom of this file) to show that a plausible mistake - a swapped nibble, a
+dropped term, a transposed operand, an off-by-one - fails at least one pin.
+"""
+from __future__ import annotations
+
+import math
+import os
+import types
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.exact import F16, F32, rint_half_even, round_rne
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rows(name):
+    out = []
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                out.append(line)
+    return out
+
+
+def _f16_from_bits(rng, n, lo_exp=-10, hi_exp=4):
+    """Random finite fp16 values with exponents in [lo_exp, hi_exp], both signs."""
+    e = rng.integers(lo_exp, hi_exp + 1, size=n)
+    frac = rng.integers(0, 1024, size=n)
+    sign = rng.integers(0, 2, size=n)
+    bits = (sign << 15) | ((e + 15) << 10) | frac
+    return bits.astype(np.uint16).view(np.float16)
+
+
+# ----------------------------------------------------------------------------
+# Pins. Each raises AssertionError (or any exception) on a wrong oracle.
+# ----------------------------------------------------------------------------
+def pin_nibble_golden(o):
+    for line in _rows("nibble_order.txt"):
+        b, even, odd = line.split()
+        byte = np.array([[int(b, 16)]], dtype=np.uint8)
+        codes = o.unpack_q4(byte)
+        assert codes.tolist() == [[int(even), int(odd)]], (b, codes)
+        assert o.pack_q4(np.array([[int(even), int(odd)]])).tolist() == [[int(b, 16)]]
+
+
+def pin_pack_roundtrip(o):
+    allbytes = np.arange(256, dtype=np.uint8).reshape(16, 16)
+    assert np.array_equal(o.pack_q4(o.unpack_q4(allbytes)), allbytes)
+    a, b = np.meshgrid(np.arange(16), np.arange(16), indexing="ij")
+    pairs = np.stack([a.ravel(), b.ravel()], axis=1)            # [256, 2] codes
+    assert np.array_equal(o.unpack_q4(o.pack_q4(pairs)), pairs)
+    # a longer row keeps order across bytes: codes 0..15,15..0
+    row = np.concatenate([np.arange(16), np.arange(15, -1, -1)])[None, :]
+    assert np.array_equal(o.unpack_q4(o.pack_q4(row)), row)
+
+
+def pin_q4_dequant_golden(o):
+    for line in _rows("q4_dequant_examples.txt"):
+        b, s, m, w0, w1 = line.split()
+        payload = np.zeros((1, 16), dtype=np.uint8)
+        payload[0, 0] = int(b, 16)
+        pairs = np.array([[[float(s), float(m)]]], dtype=np.float16)
+        W = o.dequant_q4(payload, pairs)
+        assert W.dtype == np.float32 and W.shape == (1, 32)
+        assert W[0, 0] == np.float32(w0) and W[0, 1] == np.float32(w1), (line, W[0, :2])
+        assert np.all(W[0, 2:] == np.float32(m))                 # zero bytes give the min
+
+
+def pin_q4_dequant_identity_probe(o):
+    rng = np.random.default_rng(1)
+    payload = rng.integers(0, 256, size=(5, 48), dtype=np.uint8)   # K = 96, 3 groups
+    pairs = np.zeros((5, 3, 2), dtype=np.float16)
+    pairs[..., 0] = 1.0
+    W = o.dequant_q4(payload, pairs)
+    assert np.array_equal(W, o.unpack_q4(payload).astype(np.float32))
+
+
+def pin_q4_dequant_rational(o):
+    rng = np.random.default_rng(2)
+    N, K = 3, 64
+    payload = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    pairs = np.stack([_f16_from_bits(rng, N * 2), _f16_from_bits(rng, N * 2)], axis=1).reshape(N, 2, 2)
+    W = o.dequant_q4(payload, pairs)
+    for n in range(N):
+        for j in range(K // 2):
+            byte = int(payload[n, j])
+            for k, code in ((2 * j, byte & 15), (2 * j + 1, byte >> 4)):
+                s = Fraction(float(pairs[n, k // 32, 0]))
+                m = Fraction(float(pairs[n, k // 32, 1]))
+                want = round_rne(code * s + m, F32)
+                assert float(W[n, k]) == want, (n, k, float(W[n, k]), want)
+
+
+def pin_q8_dequant_rational(o):
+    rng = np.random.default_rng(3)
+    N, K = 4, 40
+    q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    scale = (rng.standard_normal(N) * 0.01).astype(np.float32)
+    W = o.dequant_q8(q, scale)
+    for n in range(N):
+        for k in range(K):
+            want = round_rne(Fraction(int(q[n, k])) * Fraction(float(scale[n])), F32)
+            assert float(W[n, k]) == want
+
+
+def pin_q8_golden(o):
+    for line in _rows("q8_examples.txt"):
+        vals, sc, qs = [p.split() for p in line.split(";")]
+        W = np.array([[float(v) for v in vals]], dtype=np.float32)
+        q, scale = o.quantize_q8(W)
+        assert scale.dtype == np.float32 and q.dtype == np.int8
+        assert float(scale[0]) == float(sc[0]), (line, scale)
+        assert q[0].tolist() == [int(v) for v in qs], (line, q)
+
+
+def pin_q8_closed_form(o):
+    W = synth.weight(0, 0, 0, "wo", 24, 96, heavy="rows")
+    W[3, :] = 0.0                                               # an all-zero row
+    q, scale = o.quantize_q8(W)
+    for n in range(W.shape[0]):
+        amax = max(abs(Fraction(float(v))) for v in W[n])
+        want = round_rne(amax / 127, F32)
+        assert float(scale[n]) == want, (n, float(scale[n]), want)
+        if want == 0.0:
+            assert not q[n].any()
+            continue
+        arg = int(np.argmax(np.abs(W[n])))
+        assert int(q[n, arg]) == (127 if W[n, arg] > 0 else -127)
+        sc = Fraction(want)
+        for k in range(W.shape[1]):
+            assert -127 <= int(q[n, k]) <= 127
+            err = abs(int(q[n, k]) * sc - Fraction(float(W[n, k])))
+            assert err <= sc * (Fraction(1, 2) + Fraction(1, 2**40)), (n, k)
+            # the code is the nearest integer to w/scale (ties to even)
+            assert int(q[n, k]) == max(-127, min(127, rint_half_even(Fraction(float(W[n, k])) / sc)))
+
+
+def pin_q4_recon_bound(o):
+    W = synth.weight(0, 0, 0, "wq", 8, 128, heavy="cols")
+    payload, pairs = o.quantize_q4(W)
+    codes = o.unpack_q4(payload)
+    checked = 0
+    for n in range(W.shape[0]):
+        for k in range(W.shape[1]):
+            s = Fraction(float(pairs[n, k // 32, 0]))
+            m = Fraction(float(pairs[n, k // 32, 1]))
+            w = Fraction(float(W[n, k]))
+            assert 0 <= int(codes[n, k]) <= 15
+            if s > 0 and m <= w <= m + 15 * s:
+                err = abs(int(codes[n, k]) * s + m - w)
+                assert err <= s * (Fraction(1, 2) + Fraction(1, 2**40)), (n, k, float(err), float(s))
+                checked += 1
+    assert checked > 0.8 * W.size
+
+
+def pin_q4_grid_roundtrip(o):
+    """Weights already on a 16-level grid with fp16 (s, m) come back exactly,
+    with alpha = 1.0 chosen and zero reconstruction error."""
+    rng = np.random.default_rng(4)
+    N, G = 6, 4
+    s = (2.0 ** rng.integers(-8, -4, size=(N, G))) * rng.integers(1, 8, size=(N, G))
+    m = -(2.0 ** rng.integers(-6, -2, size=(N, G))) * rng.integers(1, 4, size=(N, G))
+    codes = rng.integers(0, 16, size=(N, G, 32))
+    codes[..., 0] = 0
+    codes[..., 1] = 15
+    Wexact = codes * s[..., None] + m[..., None]
+    W = Wexact.reshape(N, G * 32).astype(np.float32)
+    assert np.array_equal(W.astype(np.float64), Wexact.reshape(N, G * 32))  # exact in fp32
+    payload, pairs, alpha = o.quantize_q4(W, return_alpha=True)
+    assert np.all(alpha == 0)
+    assert np.array_equal(pairs[..., 0].astype(np.float64), s)
+    assert np.array_equal(pairs[..., 1].astype(np.float64), m)
+    assert np.array_equal(o.unpack_q4(payload), codes.reshape(N, G * 32))
+    assert np.array_equal(o.dequant_q4(payload, pairs), W)
+
+
+def _brute_alpha(w32):
+    """Independent clip search for one group: pure Python, exact-rational MSE."""
+    wmin, wmax = min(w32), max(w32)
+    best, best_err = None, None
+    for idx, alpha in enumerate((1.00, 0.95, 0.90, 0.85, 0.80)):
+        lo, hi = alpha * wmin, alpha * wmax
+        s16 = round_rne(Fraction((hi - lo) / 15.0), F16)
+        m16 = round_rne(Fraction(lo), F16)
+        err = Fraction(0)
+        for w in w32:
+            q = 0 if s16 <= 0 else max(0, min(15, round((w - m16) / s16)))
+            err += (q * Fraction(s16) + Fraction(m16) - Fraction(w)) ** 2
+        if best_err is None or err < best_err:
+            best, best_err = idx, err
+    return best
+
+
+def pin_q4_clip_argmin(o):
+    W = np.concatenate([synth.weight(0, 0, 0, "w1", 6, 64),
+                        synth.weight(0, 0, 0, "w3", 6, 64, heavy="cols")], axis=0)
+    _, _, alpha = o.quantize_q4(W, return_alpha=True)
+    for n in range(W.shape[0]):
+        for g in range(W.shape[1] // 32):
+            w32 = [float(v) for v in W[n, 32 * g:32 * g + 32]]
+            assert int(alpha[n, g]) == _brute_alpha(w32), (n, g)
+
+
+def pin_q4_degenerate(o):
+    W = np.zeros((3, 64), dtype=np.float32)
+    W[1, :32] = 0.3
+    W[2, 32:] = -1.5
+    payload, pairs = o.quantize_q4(W)
+    assert not o.unpack_q4(payload).any()
+    assert np.all(pairs[..., 0] == 0)
+    assert pairs[1, 0, 1] == np.float16(0.3) and pairs[2, 1, 1] == np.float16(-1.5)
+    assert np.array_equal(o.dequant_q4(payload, pairs)[0], np.zeros(64, np.float32))
+
+
+def _loop_gemm(x, W):
+    M, K = x.shape
+    N = W.shape[0]
+    y = [[0.0] * N for _ in range(M)]
+    for i in range(M):
+        for j in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(x[i, k]) * float(W[j, k])
+            y[i][j] = acc
+    return np.array(y)
+
+
+def pin_gemm_triple_loop(o):
+    for (M, N, K) in ((1, 1, 32), (3, 5, 64), (7, 9, 96), (4, 4, 32)):
+        g = np.random.default_rng(M * 100 + N)
+        x = g.standard_normal((M, K)).astype(np.float32)
+        W = g.standard_normal((N, K)).astype(np.float32)
+        y = o.gemm_ref(x, W)
+        assert y.shape == (M, N)
+        ref = _loop_gemm(x, W)
+        assert np.allclose(y, ref, rtol=1e-12, atol=1e-12), (M, N, K)
+
+
+def pin_gemm_exact_integer(o):
+    """Integer x and dyadic dequantized weights: every product and sum is exact,
+    so the projection equals integer arithmetic exactly."""
+    M, N, K = 5, 7, 64
+    x = synth.uniform_ints(1, (M, K), -4, 4).astype(np.float32)
+    payload = synth.uniform_bytes(2, (N, K // 2))
+    pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
+    pairs[..., 0] = 0.25
+    pairs[..., 1] = -2.0
+    y = o.project_q4(x, payload, pairs)
+    for i in range(M):
+        for j in range(N):
+            acc = Fraction(0)
+            for k in range(K):
+                byte = int(payload[j, k // 2])
+                code = byte & 15 if k % 2 == 0 else byte >> 4
+                acc += int(x[i, k]) * (Fraction(code, 4) - 2)
+            assert Fraction(float(y[i, j])) == acc, (i, j)
+
+
+PINS = [pin_nibble_golden, pin_pack_roundtrip, pin_q4_dequant_golden, pin_q4_dequant_identity_probe,
+        pin_q4_dequant_rational, pin_q8_dequant_rational, pin_q8_golden, pin_q8_closed_form,
+        pin_q4_recon_bound, pin_q4_grid_roundtrip, pin_q4_clip_argmin, pin_q4_degenerate,
+        pin_gemm_triple_loop, pin_gemm_exact_integer]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin):
+    pin(oracle)
+
+
+# ----------------------------------------------------------------------------
+# The library primitives the oracle leans on.
+# ----------------------------------------------------------------------------
+@pytest.mark.filterwarnings("ignore:overflow encountered")
+def test_numpy_f64_to_f16_is_correctly_rounded():
+    rng = np.random.default_rng(5)
+    vals = list(rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000))
+    ulp1 = 2.0 ** -10
+    vals += [1 + ulp1 / 2, 1 + 3 * ulp1 / 2, 1 + ulp1 / 2 + 2 ** -40, 1 + ulp1 / 2 - 2 ** -40,
+             2 ** -24, 2 ** -25, 2 ** -25 + 2 ** -60, 3 * 2 ** -25, 65504.0, 65519.99, 65520.0,
+             6.0e-5, -2 ** -14 * (1 - 2 ** -11), 0.0]
+    for v in vals:
+        assert float(np.float64(v).astype(np.float16)) == round_rne(Fraction(v), F16), v
+
+
+def test_numpy_fp32_matmul_meets_tolerance():
+    """fp32 arithmetic reaches the 1e-5 relative-Frobenius bar with margin, so the
+    bar is a fair test of an fp32 GEMM."""
+    for K in (512, 2048):
+        x = synth.activation(9, 0, "x_attn", 80, K)
+        W = synth.weight(9, 0, 0, "wq", 512, K)
+        y32 = x @ W.T
+        assert oracle.rel_fro(y32, oracle.gemm_ref(x, W)) < 1e-6
+
+
+def test_recipe_matches_int4_card():
+    # int4 card, "Quantization format": int4 for wq/wk/wv/wg and ffn.w1/w3,
+    # int8 for the residual-writing wo and ffn.w2.
+    assert {k for k, v in oracle.RECIPE_MIXED.items() if v == "q4"} == {"wq", "wk", "wv", "wg", "w1", "w3"}
+    assert {k for k, v in oracle.RECIPE_MIXED.items() if v == "q8"} == {"wo", "w2"}
+    assert set(oracle.RECIPE_ALL_Q8.values()) == {"q8"}
+
+
+def test_byte_accounting():
+    """q4 stores 0.5 B payload + 4 B per 32 weights (5 bits/weight); q8 1 B per
+    weight + 4 B per row. One RT-J block (mixed recipe) is 3,280,896 bytes."""
+    total = 0
+    for name in synth.PROJ_ORDER:
+        N, K, _ = synth.BLOCK_SHAPES[name]
+        W = np.zeros((N, K), dtype=np.float32)
+        if oracle.RECIPE_MIXED[name] == "q4":
+            p, s = oracle.quantize_q4(W)
+        else:
+            p, s = oracle.quantize_q8(W)
+        total += p.nbytes + s.nbytes
+    assert total == 3_280_896
+
+
+# ----------------------------------------------------------------------------
+# Planted mistakes: each broken copy must fail at least one pin.
+# ----------------------------------------------------------------------------
+def _mut_unpack_swapped(payload):
+    q = oracle.unpack_q4(payload)
+    return q.reshape(q.shape[0], -1, 2)[:, :, ::-1].reshape(q.shape).copy()
+
+
+def _mut_dequant_q4_no_min(payload, pairs):
+    p = np.array(pairs, dtype=np.float16, copy=True)
+    p[..., 1] = 0
+    return oracle.dequant_q4(payload, p)
+
+
+def _mut_dequant_q4_pair_swapped(payload, pairs):
+    return oracle.dequant_q4(payload, np.asarray(pairs)[..., ::-1])
+
+
+def _mut_dequant_q4_group_shift(payload, pairs):
+    return oracle.dequant_q4(payload, np.roll(np.asarray(pairs), 1, axis=1))
+
+
+def _mut_dequant_q4_fp16_rounded(payload, pairs):
+    return oracle.dequant_q4(payload, pairs).astype(np.float16).astype(np.float32)
+
+
+def _mut_dequant_q8_row_shift(q, scale):
+    return oracle.dequant_q8(q, np.roll(np.asarray(scale), 1))
+
+
+def _mut_quantize_q8_div128(W):
+    W = np.asarray(W, dtype=np.float32)
+    scale = (np.abs(W).max(axis=1).astype(np.float64) / 128.0).astype(np.float32)
+    q = np.zeros(W.shape)
+    live = scale > 0
+    q[live] = np.clip(np.rint(W[live] / scale[live, None].astype(np.float64)), -127, 127)
+    return q.astype(np.int8), scale
+
+
+def _mut_quantize_q8_trunc(W):
+    q, scale = oracle.quantize_q8(W)
+    W64 = np.asarray(W, dtype=np.float64)
+    live = scale > 0
+    qt = np.zeros(W64.shape)
+    qt[live] = np.clip(np.trunc(W64[live] / scale[live, None]), -127, 127)
+    return qt.astype(np.int8), scale
+
+
+def _mut_quantize_q4_no_search(W, return_alpha=False):
+    orig = oracle.rtq_oracle.CLIP_GRID
+    try:
+        oracle.rtq_oracle.CLIP_GRID = (1.0,)
+        return oracle.quantize_q4(W, return_alpha=return_alpha)
+    finally:
+        oracle.rtq_oracle.CLIP_GRID = orig
+
+
+def _mut_quantize_q4_midpoint_shrink(W, return_alpha=False):
+    orig = oracle.rtq_oracle._q4_candidate
+
+    def cand(w, wmin, wmax, alpha):
+        mid = 0.5 * (wmin + wmax)
+        return orig(w, mid + alpha * (wmin - mid), mid + alpha * (wmax - mid), 1.0)
+    try:
+        oracle.rtq_oracle._q4_candidate = cand
+        return oracle.quantize_q4(W, return_alpha=return_alpha)
+    finally:
+        oracle.rtq_oracle._q4_candidate = orig
+
+
+def _mut_quantize_q4_floor(W, return_alpha=False):
+    orig = np.rint
+    try:
+        oracle.rtq_oracle.np.rint = np.floor
+        return oracle.quantize_q4(W, return_alpha=return_alpha)
+    finally:
+        oracle.rtq_oracle.np.rint = orig
+
+
+def _mut_gemm_no_transpose(x, W):
+    return np.asarray(x, np.float64) @ np.asarray(W, np.float64)
+
+
+def _mut_gemm_drop_last_k(x, W):
+    return np.asarray(x, np.float64)[:, :-1] @ np.asarray(W, np.float64)[:, :-1].T
+
+
+def _mut_gemm_fp32(x, W):
+    return (np.asarray(x, np.float32) @ np.asarray(W, np.float32).T).astype(np.float16).astype(np.float64)
+
+
+def _mut_project_q4_transposed(x, payload, pairs):
+    W = oracle.dequant_q4(payload, pairs)
+    return np.asarray(x, np.float64) @ W.astype(np.float64)[:, ::-1].T
+
+
+MUTANTS = {
+    "unpack_swapped": {"unpack_q4": _mut_unpack_swapped},
+    "dequant_q4_no_min": {"dequant_q4": _mut_dequant_q4_no_min},
+    "dequant_q4_pair_swapped": {"dequant_q4": _mut_dequant_q4_pair_swapped},
+    "dequant_q4_group_shift": {"dequant_q4": _mut_dequant_q4_group_shift},
+    "dequant_q4_fp16_rounded": {"dequant_q4": _mut_dequant_q4_fp16_rounded},
+    "dequant_q8_row_shift": {"dequant_q8": _mut_dequant_q8_row_shift},
+    "quantize_q8_div128": {"quantize_q8": _mut_quantize_q8_div128},
+    "quantize_q8_trunc": {"quantize_q8": _mut_quantize_q8_trunc},
+    "quantize_q4_no_search": {"quantize_q4": _mut_quantize_q4_no_search},
+    "quantize_q4_midpoint_shrink": {"quantize_q4": _mut_quantize_q4_midpoint_shrink},
+    "quantize_q4_floor": {"quantize_q4": _mut_quantize_q4_floor},
+    "gemm_no_transpose": {"gemm_ref": _mut_gemm_no_transpose},
+    "gemm_drop_last_k": {"gemm_ref": _mut_gemm_drop_last_k},
+    "gemm_low_precision": {"gemm_ref": _mut_gemm_fp32},
+    "project_q4_transposed": {"project_q4": _mut_project_q4_transposed},
+}
+
+
+def _namespace(overrides):
+    mod = oracle.rtq_oracle
+    ns = types.SimpleNamespace(**{k: getattr(mod, k) for k in dir(mod) if not k.startswith("__")})
+    for k, v in overrides.items():
+        setattr(ns, k, v)
+    return ns
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name):
+    ns = _namespace(MUTANTS[name])
+    failed = []
+    for pin in PINS:
+        try:
+            pin(ns)
+        except Exception:                                      # noqa: BLE001 - any failure counts
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
