@@ -1,0 +1,136 @@
+/*
+ * rtq.h - C ABI of the quantized-resident projection GEMM for AMD MI355X (gfx950).
+ *
+ * The operation: y = x . W^T, with fp32 activations x [M, K] (row-major), fp32
+ * output y [M, N] (row-major) and weights W [N, K] that stay in their packed,
+ * weight-only quantized form in device memory and are dequantized inside the
+ * GEMM ("RT-J - int4 (Q4-style, mixed-precision) quantized checkpoints",
+ * opening paragraph: the kernels dequantize inside the GEMM, so weight traffic
+ * is the packed payload).
+ *
+ * Storage formats (the checkpoints' tensors, one payload plus one companion):
+ *
+ *   int4 ("RT-J - int4 ... quantized checkpoints", section "Quantization
+ *   format"): uint4 codes in groups of 32 along the input dimension K.
+ *     payload  uint8   [N][K/2]     byte j of row o holds code W[o][2j] in its
+ *                                   low nibble and W[o][2j+1] in its high nibble
+ *     pairs    float16 [N][K/32][2] per group: [0] = scale, [1] = min,
+ *                                   passed as uint16_t bit patterns
+ *     W[o][i] = code * scale + min   (evaluated in fp32; exact product, one rounding)
+ *
+ *   int8 ("RT-J - int8 (Q8_0-style) quantized checkpoints", section
+ *   "Quantization format"): symmetric, one fp32 scale per output row.
+ *     payload  int8    [N][K]
+ *     scale    float32 [N]          scale[o] = max|W[o][:]| / 127
+ *     W[o][i] = q[o][i] * scale[o]
+ *
+ * Conventions for every call below:
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library
+ *     never allocates, frees or retains device memory and keeps no state
+ *     besides a thread-local error string.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
+ *     selects the null stream). Nothing is synchronized. Faults during
+ *     execution surface at the caller's next synchronization.
+ *   - Arguments are validated on the host before any HIP call; a failed check
+ *     returns its status and launches nothing. rtq_last_error() then holds a
+ *     message naming the argument.
+ *   - M == 0 is a no-op returning RTQ_OK. N >= 1 and K >= 1 are required;
+ *     M, N, K must each be below 2^31.
+ *   - Base pointers must be 16-byte aligned (4-byte for scale / pair arrays).
+ *   - The output must not overlap any input. Inputs may alias each other.
+ *   - Launch failures return RTQ_ERR_HIP with the runtime's message copied
+ *     into rtq_last_error().
+ */
+#ifndef RTQ_H_
+#define RTQ_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rtq_status {
+    RTQ_OK = 0,
+    RTQ_ERR_NULL = 1,     /* a required pointer is NULL */
+    RTQ_ERR_SHAPE = 2,    /* M/N/K (or n_blocks) out of range, K not a multiple of 32 for int4 */
+    RTQ_ERR_ALIGN = 3,    /* a pointer is not aligned as required */
+    RTQ_ERR_FORMAT = 4,   /* unknown format code in a block descriptor */
+    RTQ_ERR_HIP = 5,      /* the HIP runtime reported an error */
+    RTQ_ERR_OVERLAP = 6   /* the output range overlaps an input range */
+} rtq_status;
+
+#define RTQ_Q4_GROUP 32
+#define RTQ_MAX_BLOCKS 64
+
+enum { RTQ_FMT_NONE = 0, RTQ_FMT_Q4 = 1, RTQ_FMT_Q8 = 2 };
+
+/* int4 projection: y[M][N] = x[M][K] . dequant(payload, pairs)^T.
+ * K must be a multiple of 32 (the group size). */
+rtq_status rtq_gemm_q4(const float* x, const uint8_t* payload, const uint16_t* pairs,
+                       float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* int8 projection: y[M][N] = x[M][K] . dequant(q, scale)^T. Any K >= 1. */
+rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale,
+                       float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* One RT-J block's projections (names of the int4 card, section "Quantization
+ * format"; the block count and widths of the "Backends" page, section "Meta").
+ * fmt is RTQ_FMT_Q4 or RTQ_FMT_Q8 (so both the mixed int4/int8 recipe and the
+ * all-int8 recipe are expressible); payload == NULL skips the projection (for
+ * example a checkpoint without the attention gate wg). `scale` is the pairs
+ * array for int4 and the per-row scale for int8. Each projection reads its own
+ * x [M][K] and writes its own y [M][N]; projections may share x. */
+typedef struct rtq_proj {
+    int32_t fmt;
+    int32_t N;
+    int32_t K;
+    int32_t reserved;          /* must be 0 */
+    const void* payload;
+    const void* scale;
+    const float* x;
+    float* y;
+} rtq_proj;
+
+typedef struct rtq_block {
+    rtq_proj wq, wk, wv, wg, wo, w1, w3, w2;
+} rtq_block;
+
+/* Runs every projection of n_blocks blocks (1..RTQ_MAX_BLOCKS) at batch M in
+ * as few grouped launches as the kernel-argument limit allows, on one stream.
+ * `blocks` is a HOST array; it may be freed as soon as the call returns. The y
+ * of one projection must not overlap any input or any other projection's y. */
+rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream);
+
+/* Dequantize to a dense fp32 W [N][K], element by element, with the same
+ * arithmetic the GEMM uses (bit-exact check of unpacking and dequantization). */
+rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w,
+                          int64_t N, int64_t K, void* stream);
+rtq_status rtq_dequant_q8(const int8_t* q, const float* scale, float* w,
+                          int64_t N, int64_t K, void* stream);
+
+/* Quantize a dense fp32 W [N][K] into the int4 format: per 32-group min-MSE
+ * clip search over the shrink factors {1.00, 0.95, 0.90, 0.85, 0.80} applied
+ * to both ends of the group range ("RT-J - int4 ... quantized checkpoints",
+ * section "Quantization format"). Arithmetic in fp64, fp16 pair rounded to
+ * nearest even, codes rounded half to even and clamped to 0..15; ties keep the
+ * larger factor. Inputs must be finite with |W| <= 65504. */
+rtq_status rtq_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs,
+                           int64_t N, int64_t K, void* stream);
+
+/* Quantize a dense fp32 W [N][K] into the int8 format: scale[o] =
+ * max|W[o][:]| / 127 rounded to fp32, q = clamp(rint(W / scale), -127, 127)
+ * (fp64 quotient, half to even); an all-zero row gets scale 0 and q 0
+ * ("RT-J - int8 ... quantized checkpoints", section "Quantization format"). */
+rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale,
+                           int64_t N, int64_t K, void* stream);
+
+const char* rtq_status_string(rtq_status status);
+const char* rtq_last_error(void);   /* thread-local; valid until the next call on this thread */
+const char* rtq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RTQ_H_ */

@@ -1,0 +1,158 @@
+"""CPU-side checks of the C-ABI library: it loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call.
+No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import weight_only_quantized_rtq_amd as rtq  # noqa: E402
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rtq.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_FORMAT, ERR_HIP, ERR_OVERLAP = range(7)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(rtq.LIB_PATH):
+        pytest.fail("librtq.so is not built; run `python -m weight_only_quantized_rtq_amd.build`")
+    return rtq.load_library()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(rtq_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert declared_symbols() == sorted(rtq.EXPORTS)
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings(lib):
+    assert rtq.version().startswith("rtq ")
+    for s in range(7):
+        assert lib.rtq_status_string(s)
+    assert lib.rtq_status_string(99) == b"unknown status"
+
+
+def test_missing_library_fails_loudly(tmp_path, monkeypatch):
+    monkeypatch.setattr(rtq, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        rtq.load_library(str(tmp_path / "nope.so"))
+
+
+A = 0x7f0000000000   # fake, 256-byte aligned device addresses: never dereferenced
+B = 0x7f1000000000
+C = 0x7f2000000000
+D = 0x7f3000000000
+
+
+def call_q4(lib, x=A, p=B, s=C, y=D, M=80, N=512, K=512):
+    return lib.rtq_gemm_q4(x, p, s, y, M, N, K, None)
+
+
+def call_q8(lib, x=A, p=B, s=C, y=D, M=80, N=512, K=512):
+    return lib.rtq_gemm_q8(x, p, s, y, M, N, K, None)
+
+
+def test_shape_errors(lib):
+    assert call_q4(lib, K=48) == ERR_SHAPE
+    assert b"multiple" in lib.rtq_last_error()
+    assert call_q4(lib, N=0) == ERR_SHAPE
+    assert call_q4(lib, K=0) == ERR_SHAPE
+    assert call_q4(lib, M=-1) == ERR_SHAPE
+    assert call_q4(lib, M=2**31) == ERR_SHAPE
+    assert call_q8(lib, N=2**31) == ERR_SHAPE
+
+
+def test_m_zero_is_a_noop(lib):
+    assert call_q4(lib, M=0, x=None, y=None) == OK
+    assert call_q8(lib, M=0, x=None, y=None) == OK
+
+
+def test_null_errors(lib):
+    assert call_q4(lib, x=None) == ERR_NULL
+    assert call_q4(lib, p=None) == ERR_NULL
+    assert call_q8(lib, s=None) == ERR_NULL
+    assert call_q8(lib, y=None) == ERR_NULL
+    assert b"y is NULL" in lib.rtq_last_error()
+
+
+def test_alignment_errors(lib):
+    assert call_q4(lib, x=A + 4) == ERR_ALIGN
+    assert call_q4(lib, y=D + 8) == ERR_ALIGN
+    assert call_q8(lib, p=B + 1) == ERR_ALIGN
+    assert call_q8(lib, s=C + 2) == ERR_ALIGN
+
+
+def test_overlap_errors(lib):
+    # y = [A, A + 80*512*4) overlaps x
+    assert call_q4(lib, y=A + 1024) == ERR_OVERLAP
+    assert call_q8(lib, y=B) == ERR_OVERLAP
+    # adjacent but disjoint ranges are fine up to the launch, which needs a GPU:
+    # not exercised here.
+
+
+def _block(fmt=rtq.FMT_Q4, N=512, K=512, x=A, p=B, s=C, y=D, reserved=0):
+    blk = rtq._Block()
+    d = blk.wq
+    d.fmt, d.N, d.K, d.reserved = fmt, N, K, reserved
+    d.payload, d.scale, d.x, d.y = p, s, x, y
+    return blk
+
+
+def test_block_project_validation(lib):
+    arr = (rtq._Block * 1)(_block())
+    assert lib.rtq_block_project(arr, 0, 80, None) == ERR_SHAPE
+    assert lib.rtq_block_project(arr, 65, 80, None) == ERR_SHAPE
+    assert lib.rtq_block_project(None, 1, 80, None) == ERR_NULL
+    assert lib.rtq_block_project((rtq._Block * 1)(_block(fmt=7)), 1, 80, None) == ERR_FORMAT
+    assert lib.rtq_block_project((rtq._Block * 1)(_block(K=40)), 1, 80, None) == ERR_SHAPE
+    assert lib.rtq_block_project((rtq._Block * 1)(_block(reserved=1)), 1, 80, None) == ERR_SHAPE
+    assert lib.rtq_block_project((rtq._Block * 1)(_block(y=A)), 1, 80, None) == ERR_OVERLAP
+    # two projections writing the same output
+    blk = _block()
+    blk.wk = blk.wq
+    assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 80, None) == ERR_OVERLAP
+    # an output overlapping another projection's input
+    blk = _block()
+    blk.wo.fmt, blk.wo.N, blk.wo.K = rtq.FMT_Q8, 512, 512
+    blk.wo.payload, blk.wo.scale, blk.wo.x, blk.wo.y = B + 2**24, C + 2**24, D, A + 2**30
+    assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 80, None) == ERR_OVERLAP
+    # an empty block (no payloads) and M = 0 are no-ops
+    assert lib.rtq_block_project((rtq._Block * 1)(), 1, 80, None) == OK
+    assert lib.rtq_block_project(arr, 1, 0, None) == OK
+
+
+def test_quantize_dequant_validation(lib):
+    assert lib.rtq_quantize_q4(A, B, C, 4, 40, None) == ERR_SHAPE
+    assert lib.rtq_quantize_q4(A, B, None, 4, 64, None) == ERR_NULL
+    assert lib.rtq_quantize_q4(A + 4, B, C, 4, 64, None) == ERR_ALIGN
+    assert lib.rtq_quantize_q8(A, B, C, -1, 64, None) == ERR_SHAPE
+    assert lib.rtq_dequant_q4(B, C, A, 4, 33, None) == ERR_SHAPE
+    assert lib.rtq_dequant_q8(None, C, A, 4, 64, None) == ERR_NULL
+    assert lib.rtq_dequant_q8(B, C, A, 0, 64, None) == OK
+
+
+def test_struct_layout_matches_header():
+    # rtq_proj: 4 x int32 then 4 pointers; rtq_block: 8 of them in name order.
+    assert ctypes.sizeof(rtq._Proj) == 48
+    assert rtq._Proj.payload.offset == 16 and rtq._Proj.y.offset == 40
+    assert ctypes.sizeof(rtq._Block) == 8 * 48
+    assert [f[0] for f in rtq._Block._fields_] == list(rtq.PROJ_NAMES)
+
+
+def test_recipes_agree_with_names():
+    assert set(rtq.RECIPE_MIXED) == set(rtq.PROJ_NAMES)
+    assert {n for n, f in rtq.RECIPE_MIXED.items() if f == "q8"} == {"wo", "w2"}

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars: bit-exact for the quantizers' codes/pairs/scales, for unpacking and for
+dequantized weights; relative Frobenius error <= 1e-5 for the fp32-activation
+GEMM output against the fp64 oracle.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+import weight_only_quantized_rtq_amd as rtq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def gpu_quantize(W: np.ndarray, fmt: str):
+    return rtq.quantize(dev(W), fmt)
+
+
+def assert_same_quant(wg, ref, fmt):
+    if fmt == "q4":
+        p, s = ref
+        assert np.array_equal(host(wg.payload), p), "int4 codes differ"
+        assert np.array_equal(host(wg.pairs).view(np.uint16), s.view(np.uint16)), "int4 pairs differ"
+    else:
+        q, s = ref
+        assert np.array_equal(host(wg.payload), q), "int8 codes differ"
+        assert np.array_equal(host(wg.scale).view(np.uint32), s.view(np.uint32)), "int8 scales differ"
+
+
+# ----------------------------------------------------------------------------
+# Quantizers: bit-exact.
+# ----------------------------------------------------------------------------
+def _edge_weights(N, K, seed):
+    W = synth.weight(7, seed, 0, "wq", N, K)
+    W[0, :] = 0.0                                  # all-zero row / groups
+    W[1, :32] = 0.125                              # constant group
+    W[2, :] *= 1e-6                                # tiny: fp16 subnormal scales
+    W[3, :] = np.float32(2.0 ** -30)               # below fp16 range
+    W[4, ::2] *= 500.0                             # large dynamic range
+    if K >= 64:
+        W[5, 32:64] = np.linspace(-1, 1, 32, dtype=np.float32)   # exact grid-ish
+    return W
+
+
+@pytest.mark.parametrize("N,K,heavy", [(512, 512, None), (64, 2048, "rows"), (96, 512, "cols"), (7, 32, None)])
+def test_quantize_q4_bit_exact(N, K, heavy):
+    say(f"quantize_q4 N={N} K={K} heavy={heavy}")
+    W = synth.weight(1, 0, 0, "w1", N, K, heavy=heavy)
+    assert_same_quant(gpu_quantize(W, "q4"), oracle.quantize_q4(W), "q4")
+
+
+def test_quantize_q4_edge_cases():
+    W = _edge_weights(16, 128, 3)
+    assert_same_quant(gpu_quantize(W, "q4"), oracle.quantize_q4(W), "q4")
+
+
+@pytest.mark.parametrize("N,K,heavy", [(512, 512, None), (512, 2048, "rows"), (33, 100, None), (5, 7, None)])
+def test_quantize_q8_bit_exact(N, K, heavy):
+    say(f"quantize_q8 N={N} K={K} heavy={heavy}")
+    W = synth.weight(2, 0, 0, "wo", N, K, heavy=heavy)
+    assert_same_quant(gpu_quantize(W, "q8"), oracle.quantize_q8(W), "q8")
+
+
+def test_quantize_q8_edge_cases():
+    W = _edge_weights(16, 96, 4)
+    W[6, :] = np.float32(1e-39)                    # subnormal fp32 row
+    W[7, :4] = [127, -63.5, 1, 0.25]               # halves round to even
+    assert_same_quant(gpu_quantize(W, "q8"), oracle.quantize_q8(W), "q8")
+
+
+# ----------------------------------------------------------------------------
+# Unpacking and dequantization: bit-exact.
+# ----------------------------------------------------------------------------
+def _random_pairs(seed, shape):
+    bits = synth.uniform_ints(seed, shape, 0, 0xFFFF).astype(np.uint16)
+    exp = (bits >> 10) & 0x1F
+    bits = np.where(exp == 0x1F, bits & ~np.uint16(0x4000), bits)    # no inf/nan
+    return bits.view(np.float16)
+
+
+@pytest.mark.parametrize("N,K", [(512, 512), (3, 32), (130, 2048)])
+def test_dequant_q4_bit_exact(N, K):
+    payload = synth.uniform_bytes(N + K, (N, K // 2))
+    pairs = _random_pairs(N * K, (N, K // 32, 2))
+    got = host(rtq.dequant(rtq.Q4Weight(dev(payload), dev(pairs))))
+    want = oracle.dequant_q4(payload, pairs)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_unpack_probe_bit_exact():
+    """(scale, min) = (1, 0) makes the dequantized weight the raw nibble."""
+    payload = np.arange(256, dtype=np.uint8).reshape(16, 16).repeat(2, axis=0)   # [32, 16], K = 32
+    pairs = np.zeros((32, 1, 2), dtype=np.float16)
+    pairs[..., 0] = 1.0
+    got = host(rtq.dequant(rtq.Q4Weight(dev(payload), dev(pairs))))
+    assert np.array_equal(got, oracle.unpack_q4(payload).astype(np.float32))
+
+
+@pytest.mark.parametrize("N,K", [(512, 512), (5, 7), (64, 2048)])
+def test_dequant_q8_bit_exact(N, K):
+    q = synth.uniform_ints(N, (N, K), -127, 127).astype(np.int8)
+    scale = (synth.activation(5, 0, "x_o", 1, N)[0] * 0.01).astype(np.float32)
+    scale[0] = np.float32(1e-40)                    # subnormal scale
+    got = host(rtq.dequant(rtq.Q8Weight(dev(q), dev(scale))))
+    want = oracle.dequant_q8(q, scale)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ----------------------------------------------------------------------------
+# GEMM parity.
+# ----------------------------------------------------------------------------
+Q4_SHAPES = [(80, 512, 512), (1, 64, 32), (17, 40, 96), (77, 130, 544), (81, 200, 256),
+             (300, 129, 64), (129, 128, 1024), (256, 256, 2048)]
+Q8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (100, 50, 100), (5, 3, 7),
+             (200, 130, 96), (257, 129, 2048)]
+
+
+@pytest.mark.parametrize("M,N,K", Q4_SHAPES)
+def test_gemm_q4_parity(M, N, K):
+    say(f"gemm_q4 M={M} N={N} K={K}")
+    W = synth.weight(11, 0, 0, "wq", N, K)
+    x = synth.activation(11, 0, "x_attn", M, K)
+    ref = oracle.quantize_q4(W)
+    w = gpu_quantize(W, "q4")
+    assert_same_quant(w, ref, "q4")
+    y = host(rtq.gemm_q4(dev(x), w))
+    err = oracle.rel_fro(y, oracle.project_q4(x, *ref))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("M,N,K", Q8_SHAPES)
+def test_gemm_q8_parity(M, N, K):
+    say(f"gemm_q8 M={M} N={N} K={K}")
+    W = synth.weight(12, 0, 0, "w2", N, K, heavy="rows")
+    x = synth.activation(12, 0, "h", M, K)
+    ref = oracle.quantize_q8(W)
+    w = gpu_quantize(W, "q8")
+    assert_same_quant(w, ref, "q8")
+    y = host(rtq.gemm_q8(dev(x), w))
+    err = oracle.rel_fro(y, oracle.project_q8(x, *ref))
+    assert err <= TOL, err
+
+
+@pytest.mark.parametrize("fmt,K", [("q4", 64), ("q4", 96), ("q4", 512), ("q8", 64), ("q8", 160), ("q8", 40)])
+def test_gemm_identity_is_bit_exact(fmt, K):
+    """x = I_K gives y = W^T exactly: checks the in-GEMM unpack/dequant bit for bit."""
+    say(f"identity {fmt} K={K}")
+    N = 72
+    W = synth.weight(13, 0, 0, "wv", N, K, heavy="rows")
+    ref = oracle.quantize(W, fmt)
+    w = gpu_quantize(W, fmt)
+    assert_same_quant(w, ref, fmt)
+    y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), w))
+    want = oracle.dequant(fmt, *ref).T
+    assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K", [(80, 512, 512), (200, 96, 2048)])
+def test_gemm_exact_integer_arithmetic(M, N, K):
+    """Integer x and dyadic (scale, min): every partial sum is exact in fp32, so
+    any summation order must reproduce the oracle bit for bit."""
+    x = synth.uniform_ints(M, (M, K), -4, 4).astype(np.float32)
+    payload = synth.uniform_bytes(N, (N, K // 2))
+    pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
+    pairs[..., 0] = 0.25
+    pairs[..., 1] = -2.0
+    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs))))
+    want = oracle.project_q4(x, payload, pairs)
+    assert np.array_equal(y.astype(np.float64), want)
+    q = synth.uniform_ints(N + 1, (N, K), -127, 127).astype(np.int8)
+    scale = np.full(N, 0.5, dtype=np.float32)
+    y8 = host(rtq.gemm_q8(dev(x), rtq.Q8Weight(dev(q), dev(scale))))
+    assert np.array_equal(y8.astype(np.float64), oracle.project_q8(x, q, scale))
+
+
+def test_gemm_guard_bands_and_determinism():
+    """Outputs land only inside y (canaries around it survive) and a rerun is
+    bitwise identical (no atomics, fixed reduction order)."""
+    M, N, K = 77, 130, 512
+    W = synth.weight(14, 0, 0, "w3", N, K)
+    x = dev(synth.activation(14, 0, "x_ffn", M, K))
+    w = gpu_quantize(W, "q4")
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), 1234.5, dtype=torch.float32, device=DEV)
+    y = buf[guard:guard + M * N].view(M, N)
+    rtq.gemm_q4(x, w, y=y)
+    y1 = host(y).copy()
+    b = host(buf)
+    assert np.all(b[:guard] == 1234.5) and np.all(b[guard + M * N:] == 1234.5)
+    rtq.gemm_q4(x, w, y=y)
+    assert np.array_equal(host(y).view(np.uint32), y1.view(np.uint32))
+
+
+def test_gemm_m_zero_and_errors():
+    w = gpu_quantize(synth.weight(15, 0, 0, "wq", 64, 64), "q4")
+    y = rtq.gemm_q4(dev(np.zeros((0, 64), np.float32)), w)
+    assert tuple(y.shape) == (0, 64)
+    with pytest.raises(rtq.RtqError, match="ALIGN"):
+        xbig = torch.zeros(4 * 64 + 1, device=DEV)
+        rtq.load_library()
+        rtq._check(rtq.load_library().rtq_gemm_q4(xbig.data_ptr() + 4, w.payload.data_ptr(),
+                                                  w.pairs.data_ptr(), torch.empty(4, 64, device=DEV).data_ptr(),
+                                                  4, 64, 64, rtq._stream(None)))
+
+
+# ----------------------------------------------------------------------------
+# Block projection.
+# ----------------------------------------------------------------------------
+def make_block(cfg, set_, b, M, recipe, xs=None, heavy=None, skip=()):
+    """GPU-quantized weights of one block plus the oracle's own quantization."""
+    blk, refs = {}, {}
+    if xs is None:
+        xs = {n: synth.activation(cfg, b, n, M) for n in synth.INPUT_WIDTH}
+    dxs = {n: dev(v) for n, v in xs.items()}
+    for name in synth.PROJ_ORDER:
+        if name in skip:
+            continue
+        N, K, xin = synth.BLOCK_SHAPES[name]
+        W = synth.weight(cfg, set_, b, name, heavy=heavy)
+        fmt = recipe[name]
+        w = gpu_quantize(W, fmt)
+        refs[name] = (fmt, oracle.quantize(W, fmt), xin)
+        y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
+        blk[name] = rtq.Projection(w, dxs[xin], y)
+    return blk, refs, xs
+
+
+@pytest.mark.parametrize("recipe_name", ["mixed", "all_q8"])
+def test_block_project_one_block(recipe_name):
+    say(f"block_project one block recipe={recipe_name}")
+    recipe = rtq.RECIPE_MIXED if recipe_name == "mixed" else rtq.RECIPE_ALL_Q8
+    assert recipe == (oracle.RECIPE_MIXED if recipe_name == "mixed" else oracle.RECIPE_ALL_Q8)
+    M = 80
+    blk, refs, xs = make_block(3, 0, 0, M, recipe)
+    rtq.block_project([blk], M)
+    for name, (fmt, ref, xin) in refs.items():
+        assert_same_quant(blk[name].weight, ref, fmt)
+        err = oracle.rel_fro(host(blk[name].y), oracle.project(fmt, xs[xin], *ref))
+        assert err <= TOL, (name, err)
+
+
+def test_block_project_skips_missing_gate_and_runs_multi_tile():
+    """A block without wg (ungated attention) leaves nothing behind for it, and
+    M above one row tile goes through the per-projection launches."""
+    for M in (80, 333):
+        say(f"block_project two blocks M={M}")
+        blocks, refss, xss = [], [], []
+        for b in range(2):
+            blk, refs, xs = make_block(4, 0, b, M, rtq.RECIPE_MIXED, skip=("wg",) if b == 1 else ())
+            blocks.append(blk)
+            refss.append(refs)
+            xss.append(xs)
+        rtq.block_project(blocks, M)
+        for b in range(2):
+            assert ("wg" in blocks[b]) == (b == 0)
+            for name, (fmt, ref, xin) in refss[b].items():
+                err = oracle.rel_fro(host(blocks[b][name].y), oracle.project(fmt, xss[b][xin], *ref))
+                assert err <= TOL, (M, b, name, err)
+
+
+# ----------------------------------------------------------------------------
+# Full-size configurations, in the benchmark's launch configuration, checked on
+# sampled outputs the oracle computes one by one.
+# ----------------------------------------------------------------------------
+def _sampled_check(blocks, refs_w, xs_all, M, rng, n_rows=24, n_cols=24):
+    worst = 0.0
+    for b, blk in enumerate(blocks):
+        for name, p in blk.items():
+            N, K, xin = synth.BLOCK_SHAPES[name]
+            fmt, W = refs_w[b][name]
+            rows = np.sort(rng.choice(M, size=min(n_rows, M), replace=False))
+            cols = np.sort(rng.choice(N, size=min(n_cols, N), replace=False))
+            ref_w = oracle.quantize(W[cols], fmt)          # per-row quantization: rows are independent
+            got = host(p.weight.payload[torch.as_tensor(cols, device=DEV)])
+            assert np.array_equal(got, ref_w[0]), (b, name, "codes")
+            y_ref = oracle.project(fmt, xs_all[b][xin][rows], *ref_w)
+            y = host(p.y[torch.as_tensor(rows, device=DEV)][:, torch.as_tensor(cols, device=DEV)])
+            err = oracle.rel_fro(y, y_ref)
+            worst = max(worst, err)
+            assert err <= TOL, (b, name, err)
+    return worst
+
+
+@pytest.mark.parametrize("M,heavy", [(synth.M_GOLDEN, None), (synth.M_LARGE, "rows")])
+def test_full_size_twelve_blocks_sampled(M, heavy):
+    say(f"full-size 12 blocks M={M} heavy={heavy}")
+    cfg = 4 if M == synth.M_GOLDEN else 5
+    per_block = M == synth.M_GOLDEN          # as in the benchmark: own inputs per block at M=80
+    shared = None if per_block else {n: synth.activation(cfg, synth.SHARED_BLOCK, n, M) for n in synth.INPUT_WIDTH}
+    blocks, refs_w, xs_all = [], [], []
+    for b in range(synth.NUM_BLOCKS):
+        xs_host = {n: synth.activation(cfg, b, n, M) for n in synth.INPUT_WIDTH} if per_block else shared
+        xs_dev = {n: dev(v) for n, v in xs_host.items()} if (per_block or b == 0) else xs_dev
+        xs_all.append(xs_host)
+        blk, rw = {}, {}
+        for name in synth.PROJ_ORDER:
+            N, K, xin = synth.BLOCK_SHAPES[name]
+            W = synth.weight(cfg, 0, b, name, heavy=heavy)
+            fmt = rtq.RECIPE_MIXED[name]
+            blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), xs_dev[xin],
+                                       torch.empty((M, N), dtype=torch.float32, device=DEV))
+            rw[name] = (fmt, W)
+        blocks.append(blk)
+        refs_w.append(rw)
+    rtq.block_project(blocks, M)
+    torch.cuda.synchronize()
+    worst = _sampled_check(blocks, refs_w, xs_all, M, np.random.default_rng(M))
+    say(f"  worst sampled rel err {worst:.3e}")
+    del blocks
+    torch.cuda.empty_cache()

@@ -1,0 +1,303 @@
+"""Python binding of librtq.so, the quantized-resident projection GEMM for MI355X.
+
+Argument marshalling only: every step of the path (unpacking, dequantization,
+the contraction, the quantizers) runs in the library's HIP kernels. PyTorch
+supplies device memory and the current stream. There is no fallback: if the
+library is missing or fails to load, every call raises.
+
+Formats (RT-J int4 / int8 model cards, section "Quantization format"):
+  Q4Weight(payload uint8 [N, K/2], pairs float16 [N, K/32, 2])   (scale, min)
+  Q8Weight(payload int8 [N, K],    scale float32 [N])
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "librtq.so")
+
+FMT_NONE, FMT_Q4, FMT_Q8 = 0, 1, 2
+Q4_GROUP = 32
+MAX_BLOCKS = 64
+PROJ_NAMES = ("wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2")
+
+# Format routing. Mixed: the int4 card's recipe (int4 for wq/wk/wv/wg and
+# ffn.w1/w3, int8 for the residual-writing wo and ffn.w2). All-int8: the int8
+# card's recipe (every block projection int8).
+RECIPE_MIXED = {"wq": "q4", "wk": "q4", "wv": "q4", "wg": "q4",
+                "wo": "q8", "w1": "q4", "w3": "q4", "w2": "q8"}
+RECIPE_ALL_Q8 = {n: "q8" for n in PROJ_NAMES}
+
+STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN",
+          4: "RTQ_ERR_FORMAT", 5: "RTQ_ERR_HIP", 6: "RTQ_ERR_OVERLAP"}
+
+# Every symbol include/rtq.h declares.
+EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_block_project", "rtq_dequant_q4", "rtq_dequant_q8",
+           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_status_string", "rtq_last_error", "rtq_version")
+
+
+class RtqError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class _Proj(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("payload", ctypes.c_void_p), ("scale", ctypes.c_void_p),
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
+class _Block(ctypes.Structure):
+    _fields_ = [(n, _Proj) for n in PROJ_NAMES]
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads librtq.so (after torch, so both share torch's HIP runtime)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m weight_only_quantized_rtq_amd.build`")
+    lib = ctypes.CDLL(path)
+    i64, vp, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32
+    for name in ("rtq_gemm_q4", "rtq_gemm_q8"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        f.restype = ctypes.c_int
+    lib.rtq_block_project.argtypes = [ctypes.POINTER(_Block), i32, i64, vp]
+    lib.rtq_block_project.restype = ctypes.c_int
+    for name in ("rtq_dequant_q4", "rtq_dequant_q8", "rtq_quantize_q4", "rtq_quantize_q8"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, vp, i64, i64, vp]
+        f.restype = ctypes.c_int
+    lib.rtq_status_string.argtypes = [ctypes.c_int]
+    lib.rtq_status_string.restype = ctypes.c_char_p
+    lib.rtq_last_error.argtypes = []
+    lib.rtq_last_error.restype = ctypes.c_char_p
+    lib.rtq_version.argtypes = []
+    lib.rtq_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load_library().rtq_version().decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RtqError(status, load_library().rtq_last_error().decode())
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+@dataclass
+class Q4Weight:
+    payload: torch.Tensor   # uint8 [N, K/2]
+    pairs: torch.Tensor     # float16 [N, K/32, 2]: (scale, min)
+
+    @property
+    def N(self) -> int:
+        return self.payload.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.payload.shape[1] * 2
+
+    fmt = FMT_Q4
+
+    @property
+    def scale_tensor(self) -> torch.Tensor:
+        return self.pairs
+
+    def validate(self) -> None:
+        _need(self.payload, torch.uint8, "payload")
+        _need(self.pairs, torch.float16, "pairs")
+        if self.payload.dim() != 2 or tuple(self.pairs.shape) != (self.N, self.K // Q4_GROUP, 2):
+            raise ValueError(f"int4 weight shapes disagree: payload {tuple(self.payload.shape)}, "
+                             f"pairs {tuple(self.pairs.shape)}")
+
+
+@dataclass
+class Q8Weight:
+    payload: torch.Tensor   # int8 [N, K]
+    scale: torch.Tensor     # float32 [N]
+
+    @property
+    def N(self) -> int:
+        return self.payload.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.payload.shape[1]
+
+    fmt = FMT_Q8
+
+    @property
+    def scale_tensor(self) -> torch.Tensor:
+        return self.scale
+
+    def validate(self) -> None:
+        _need(self.payload, torch.int8, "payload")
+        _need(self.scale, torch.float32, "scale")
+        if self.payload.dim() != 2 or tuple(self.scale.shape) != (self.N,):
+            raise ValueError(f"int8 weight shapes disagree: payload {tuple(self.payload.shape)}, "
+                             f"scale {tuple(self.scale.shape)}")
+
+
+def weight_from_tensors(payload: torch.Tensor, scale: torch.Tensor):
+    """Format detection from the payload dtype, as the engine's loader does
+    (int4 card, "Usage": the format is read off the tensor dtypes): uint8 -> int4, int8 -> int8."""
+    if payload.dtype == torch.uint8:
+        return Q4Weight(payload, scale)
+    if payload.dtype == torch.int8:
+        return Q8Weight(payload, scale)
+    raise TypeError(f"payload dtype {payload.dtype} is not a quantized format")
+
+
+def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream) -> torch.Tensor:
+    lib = load_library()
+    w.validate()
+    _need(x, torch.float32, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [M, {w.K}], got {tuple(x.shape)}")
+    M = x.shape[0]
+    if y is None:
+        y = torch.empty((M, w.N), dtype=torch.float32, device=x.device)
+    else:
+        _need(y, torch.float32, "y")
+        if tuple(y.shape) != (M, w.N):
+            raise ValueError(f"y must be [{M}, {w.N}], got {tuple(y.shape)}")
+    fn = lib.rtq_gemm_q4 if w.fmt == FMT_Q4 else lib.rtq_gemm_q8
+    _check(fn(_ptr(x), _ptr(w.payload), _ptr(w.scale_tensor), _ptr(y), M, w.N, w.K, _stream(stream)))
+    return y
+
+
+def gemm_q4(x: torch.Tensor, w: Q4Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x . dequant(w)^T for an int4 weight (rtq_gemm_q4)."""
+    if not isinstance(w, Q4Weight):
+        raise TypeError("gemm_q4 needs a Q4Weight")
+    return _gemm(x, w, y, stream)
+
+
+def gemm_q8(x: torch.Tensor, w: Q8Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x . dequant(w)^T for an int8 weight (rtq_gemm_q8)."""
+    if not isinstance(w, Q8Weight):
+        raise TypeError("gemm_q8 needs a Q8Weight")
+    return _gemm(x, w, y, stream)
+
+
+def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    return _gemm(x, w, y, stream)
+
+
+def dequant(w, stream=None) -> torch.Tensor:
+    """Dense fp32 W [N, K] (rtq_dequant_q4 / rtq_dequant_q8)."""
+    lib = load_library()
+    w.validate()
+    out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.payload.device)
+    fn = lib.rtq_dequant_q4 if w.fmt == FMT_Q4 else lib.rtq_dequant_q8
+    _check(fn(_ptr(w.payload), _ptr(w.scale_tensor), _ptr(out), w.N, w.K, _stream(stream)))
+    return out
+
+
+def quantize_q4(W: torch.Tensor, stream=None) -> Q4Weight:
+    """int4 group-32 quantization with the min-MSE clip search (rtq_quantize_q4)."""
+    lib = load_library()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    payload = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    pairs = torch.empty((N, K // Q4_GROUP, 2), dtype=torch.float16, device=W.device)
+    _check(lib.rtq_quantize_q4(_ptr(W), _ptr(payload), _ptr(pairs), N, K, _stream(stream)))
+    return Q4Weight(payload, pairs)
+
+
+def quantize_q8(W: torch.Tensor, stream=None) -> Q8Weight:
+    """int8 per-row symmetric quantization (rtq_quantize_q8)."""
+    lib = load_library()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    q = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    scale = torch.empty((N,), dtype=torch.float32, device=W.device)
+    _check(lib.rtq_quantize_q8(_ptr(W), _ptr(q), _ptr(scale), N, K, _stream(stream)))
+    return Q8Weight(q, scale)
+
+
+def quantize(W: torch.Tensor, fmt: str, stream=None):
+    if fmt == "q4":
+        return quantize_q4(W, stream)
+    if fmt == "q8":
+        return quantize_q8(W, stream)
+    raise ValueError(f"unknown format {fmt!r}")
+
+
+@dataclass
+class Projection:
+    """One projection of a block: its weight, the input it reads and the output it writes."""
+    weight: object               # Q4Weight | Q8Weight
+    x: torch.Tensor              # float32 [M, K]
+    y: torch.Tensor              # float32 [M, N]
+
+
+def pack_blocks(blocks: list[dict[str, Projection]], M: int):
+    """Builds the host descriptor array of rtq_block_project. Names missing from
+    a block's dict (e.g. a checkpoint without wg) are skipped."""
+    if not 1 <= len(blocks) <= MAX_BLOCKS:
+        raise ValueError(f"1..{MAX_BLOCKS} blocks per call, got {len(blocks)}")
+    arr = (_Block * len(blocks))()
+    keep = []
+    for b, blk in enumerate(blocks):
+        for name in PROJ_NAMES:
+            p = blk.get(name)
+            if p is None:
+                continue
+            w = p.weight
+            w.validate()
+            _need(p.x, torch.float32, f"{name}.x")
+            _need(p.y, torch.float32, f"{name}.y")
+            if tuple(p.x.shape) != (M, w.K) or tuple(p.y.shape) != (M, w.N):
+                raise ValueError(f"block {b} {name}: x {tuple(p.x.shape)} / y {tuple(p.y.shape)} "
+                                 f"do not match M={M}, N={w.N}, K={w.K}")
+            d = getattr(arr[b], name)
+            d.fmt, d.N, d.K, d.reserved = w.fmt, w.N, w.K, 0
+            d.payload, d.scale = _ptr(w.payload), _ptr(w.scale_tensor)
+            d.x, d.y = _ptr(p.x), _ptr(p.y)
+            keep.append(p)
+    return arr, keep
+
+
+def block_project(blocks: list[dict[str, Projection]], M: int, stream=None, packed=None) -> None:
+    """Runs every projection of the given blocks (rtq_block_project).
+    `packed` may hold a pack_blocks() result to reuse across calls."""
+    lib = load_library()
+    arr, _keep = packed if packed is not None else pack_blocks(blocks, M)
+    _check(lib.rtq_block_project(arr, len(arr), M, _stream(stream)))

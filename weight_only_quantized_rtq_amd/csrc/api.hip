@@ -1,0 +1,224 @@
+// C ABI of the rtq library: argument validation (host only, before any HIP
+// call) and dispatch to the gfx950 kernels. Declarations and the contract of
+// each entry point are in rtq.h.
+#include <rtq.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "rtq_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+void clear_error() { g_err[0] = '\0'; }
+
+rtq_status fail(rtq_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+rtq_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return RTQ_OK;
+    return fail(RTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a.hi && b.lo != b.hi; }
+
+// Checks shared by the projection entry points. `name` prefixes messages.
+rtq_status check_proj(const char* name, int fmt, const float* x, const void* payload,
+                      const void* scale, const float* y, int64_t M, int64_t N, int64_t K) {
+    if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: M=%lld out of range [0, 2^31)", name, (long long)M);
+    if (N < 1 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [1, 2^31)", name, (long long)N);
+    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
+        return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
+    if (M == 0) return RTQ_OK;
+    if (!x) return fail(RTQ_ERR_NULL, "%s: x is NULL", name);
+    if (!payload) return fail(RTQ_ERR_NULL, "%s: payload is NULL", name);
+    if (!scale) return fail(RTQ_ERR_NULL, "%s: scale is NULL", name);
+    if (!y) return fail(RTQ_ERR_NULL, "%s: y is NULL", name);
+    if (!aligned(x, 16)) return fail(RTQ_ERR_ALIGN, "%s: x is not 16-byte aligned", name);
+    if (!aligned(y, 16)) return fail(RTQ_ERR_ALIGN, "%s: y is not 16-byte aligned", name);
+    if (!aligned(payload, 16)) return fail(RTQ_ERR_ALIGN, "%s: payload is not 16-byte aligned", name);
+    if (!aligned(scale, 4)) return fail(RTQ_ERR_ALIGN, "%s: scale is not 4-byte aligned", name);
+    const int64_t payload_bytes = fmt == rtq::kFmtQ4 ? N * (K / 2) : N * K;
+    const int64_t scale_bytes = fmt == rtq::kFmtQ4 ? N * (K / RTQ_Q4_GROUP) * 4 : N * 4;
+    const Range ry = range_of(y, M * N * 4);
+    if (overlaps(ry, range_of(x, M * K * 4)) || overlaps(ry, range_of(payload, payload_bytes)) ||
+        overlaps(ry, range_of(scale, scale_bytes)))
+        return fail(RTQ_ERR_OVERLAP, "%s: y overlaps an input", name);
+    return RTQ_OK;
+}
+
+rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, const void* c,
+                    int64_t N, int64_t K) {
+    if (N < 0 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [0, 2^31)", name, (long long)N);
+    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
+        return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!a || !b || !c) return fail(RTQ_ERR_NULL, "%s: a pointer argument is NULL", name);
+    if (!aligned(a, 16) || !aligned(b, 4) || !aligned(c, 16))
+        return fail(RTQ_ERR_ALIGN, "%s: misaligned pointer", name);
+    return RTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rtq_version(void) { return "rtq 0.1.0 gfx950"; }
+
+const char* rtq_last_error(void) { return g_err; }
+
+const char* rtq_status_string(rtq_status s) {
+    switch (s) {
+        case RTQ_OK: return "ok";
+        case RTQ_ERR_NULL: return "null pointer";
+        case RTQ_ERR_SHAPE: return "bad shape";
+        case RTQ_ERR_ALIGN: return "misaligned pointer";
+        case RTQ_ERR_FORMAT: return "unknown format";
+        case RTQ_ERR_HIP: return "HIP runtime error";
+        case RTQ_ERR_OVERLAP: return "output overlaps an input";
+    }
+    return "unknown status";
+}
+
+rtq_status rtq_gemm_q4(const float* x, const uint8_t* payload, const uint16_t* pairs, float* y,
+                       int64_t M, int64_t N, int64_t K, void* stream) {
+    clear_error();
+    rtq_status s = check_proj("rtq_gemm_q4", rtq::kFmtQ4, x, payload, pairs, y, M, N, K);
+    if (s != RTQ_OK || M == 0) return s;
+    const rtq::ProjTask t{rtq::kFmtQ4, static_cast<int>(N), static_cast<int>(K), payload, pairs, x, y};
+    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_q4 launch");
+}
+
+rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale, float* y, int64_t M,
+                       int64_t N, int64_t K, void* stream) {
+    clear_error();
+    rtq_status s = check_proj("rtq_gemm_q8", rtq::kFmtQ8, x, q, scale, y, M, N, K);
+    if (s != RTQ_OK || M == 0) return s;
+    const rtq::ProjTask t{rtq::kFmtQ8, static_cast<int>(N), static_cast<int>(K), q, scale, x, y};
+    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_q8 launch");
+}
+
+rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
+    clear_error();
+    if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
+    if (n_blocks < 1 || n_blocks > RTQ_MAX_BLOCKS)
+        return fail(RTQ_ERR_SHAPE, "rtq_block_project: n_blocks=%d out of range [1, %d]", n_blocks, RTQ_MAX_BLOCKS);
+    if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "rtq_block_project: M=%lld out of range", (long long)M);
+    static const char* names[8] = {"wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2"};
+    rtq::ProjTask grouped[RTQ_MAX_BLOCKS * 8];
+    rtq::ProjTask single[RTQ_MAX_BLOCKS * 8];
+    Range outs[RTQ_MAX_BLOCKS * 8];
+    int n_grouped = 0, n_single = 0, n_outs = 0;
+    for (int b = 0; b < n_blocks; ++b) {
+        const rtq_proj* p = &blocks[b].wq;
+        for (int j = 0; j < 8; ++j) {
+            const rtq_proj& d = p[j];
+            if (!d.payload) continue;
+            char name[64];
+            std::snprintf(name, sizeof(name), "rtq_block_project: block %d %s", b, names[j]);
+            if (d.fmt != RTQ_FMT_Q4 && d.fmt != RTQ_FMT_Q8)
+                return fail(RTQ_ERR_FORMAT, "%s: unknown fmt %d", name, d.fmt);
+            if (d.reserved != 0) return fail(RTQ_ERR_SHAPE, "%s: reserved field must be 0", name);
+            const rtq_status s = check_proj(name, d.fmt, d.x, d.payload, d.scale, d.y, M, d.N, d.K);
+            if (s != RTQ_OK) return s;
+            const Range ry = range_of(d.y, M * int64_t(d.N) * 4);
+            for (int i = 0; i < n_outs; ++i)
+                if (overlaps(ry, outs[i])) return fail(RTQ_ERR_OVERLAP, "%s: y overlaps another output", name);
+            outs[n_outs++] = ry;
+            const rtq::ProjTask t{d.fmt, d.N, d.K, d.payload, d.scale, d.x, d.y};
+            if (rtq::grouped_ok(t)) grouped[n_grouped++] = t;
+            else single[n_single++] = t;
+        }
+    }
+    // Outputs must not overlap any input of any projection either.
+    for (int b = 0; b < n_blocks; ++b) {
+        const rtq_proj* p = &blocks[b].wq;
+        for (int j = 0; j < 8; ++j) {
+            const rtq_proj& d = p[j];
+            if (!d.payload || M == 0) continue;
+            const int64_t pb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 2) : int64_t(d.N) * d.K;
+            const int64_t sb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 32) * 4 : int64_t(d.N) * 4;
+            const Range ins[3] = {range_of(d.x, M * int64_t(d.K) * 4), range_of(d.payload, pb), range_of(d.scale, sb)};
+            for (int i = 0; i < n_outs; ++i)
+                for (const Range& r : ins)
+                    if (overlaps(outs[i], r))
+                        return fail(RTQ_ERR_OVERLAP, "rtq_block_project: an output overlaps block %d %s's inputs", b, names[j]);
+        }
+    }
+    if (M == 0) return RTQ_OK;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    if (n_grouped) {
+        const rtq_status s = hip_status(rtq::launch_grouped(grouped, n_grouped, M, st), "rtq_block_project launch");
+        if (s != RTQ_OK) return s;
+    }
+    for (int i = 0; i < n_single; ++i) {
+        const rtq_status s = hip_status(rtq::launch_gemm(single[i], M, st), "rtq_block_project launch");
+        if (s != RTQ_OK) return s;
+    }
+    return RTQ_OK;
+}
+
+rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N, int64_t K,
+                          void* stream) {
+    clear_error();
+    rtq_status s = check_nk("rtq_dequant_q4", rtq::kFmtQ4, payload, pairs, w, N, K);
+    if (s != RTQ_OK || N == 0) return s;
+    return hip_status(rtq::launch_dequant_q4(payload, pairs, w, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_dequant_q4 launch");
+}
+
+rtq_status rtq_dequant_q8(const int8_t* q, const float* scale, float* w, int64_t N, int64_t K, void* stream) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+        return fail(RTQ_ERR_SHAPE, "rtq_dequant_q8: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!q || !scale || !w) return fail(RTQ_ERR_NULL, "rtq_dequant_q8: a pointer argument is NULL");
+    if (!aligned(scale, 4) || !aligned(w, 4)) return fail(RTQ_ERR_ALIGN, "rtq_dequant_q8: misaligned pointer");
+    return hip_status(rtq::launch_dequant_q8(q, scale, w, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_dequant_q8 launch");
+}
+
+rtq_status rtq_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N, int64_t K,
+                           void* stream) {
+    clear_error();
+    rtq_status s = check_nk("rtq_quantize_q4", rtq::kFmtQ4, payload, pairs, w, N, K);
+    if (s != RTQ_OK || N == 0) return s;
+    return hip_status(rtq::launch_quantize_q4(w, payload, pairs, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_quantize_q4 launch");
+}
+
+rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, int64_t K, void* stream) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+        return fail(RTQ_ERR_SHAPE, "rtq_quantize_q8: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!w || !q || !scale) return fail(RTQ_ERR_NULL, "rtq_quantize_q8: a pointer argument is NULL");
+    if (!aligned(w, 4) || !aligned(scale, 4)) return fail(RTQ_ERR_ALIGN, "rtq_quantize_q8: misaligned pointer");
+    return hip_status(rtq::launch_quantize_q8(w, q, scale, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_quantize_q8 launch");
+}
+
+}  // extern "C"

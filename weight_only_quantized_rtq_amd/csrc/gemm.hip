@@ -1,0 +1,377 @@
+// Dequant-in-GEMM kernels: y[M][N] = x[M][K] . W^T with W kept packed in HBM.
+//
+// The packed weights are streamed once per output tile, unpacked and
+// dequantized in registers while the tile is staged into LDS (int4: code*s+m
+// with the group's fp16 pair; int8: the integer itself, the row scale being
+// applied once in the epilogue since it factors out of the K sum), and the
+// contraction runs on the fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32
+// accumulators. The format is that of the RT-J int4 / int8 model cards,
+// section "Quantization format"; the dequantize-inside-the-GEMM design is the
+// one their opening paragraphs describe.
+#include "rtq_device.h"
+#include "rtq_internal.h"
+
+namespace rtq {
+
+namespace {
+
+constexpr int kBK = 32;        // K step: one int4 group
+constexpr int kLD = kBK + 4;   // LDS row stride in floats (pad keeps b128 reads conflict-free)
+constexpr int kMaxGrouped = 96;
+
+struct TileArgs {
+    const float* x;
+    const void* payload;
+    const void* scale;
+    float* y;
+    int M, N, K;
+};
+
+// Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+// contiguous range of logical tiles so tiles sharing an x row-block share an L2.
+__device__ __forceinline__ int xcd_remap(int w, int G) {
+    const int q = G / 8, r = G % 8;
+    const int xcd = w % 8, local = w / 8;
+    const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
+    return start + local;
+}
+
+template <int WM, int WN, int TM, int TN>
+struct TileShape {
+    static constexpr int NT = WM * WN * 64;
+    static constexpr int BM = WM * TM * 16;
+    static constexpr int BN = WN * TN * 16;
+    static constexpr int XV = BM * (kBK / 4);              // float4 loads per x tile
+    static constexpr int XPT = (XV + NT - 1) / NT;
+    static constexpr int SMEM = 2 * (BM + BN) * kLD;       // floats, double buffered
+    static_assert(BN * kBK == NT * 16, "each thread stages 16 weights of the W tile");
+};
+
+// One BM x BN output tile over the whole K range.
+// SAFE: per-element bounds on K (int8 with K % 32 != 0 or unaligned rows).
+template <int FMT, int WM, int WN, int TM, int TN, bool SAFE>
+__device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, float* smem) {
+    using S = TileShape<WM, WN, TM, TN>;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int wm = wave / WN;
+    const int wn = wave % WN;
+    const int m0 = mt * S::BM;
+    const int n0 = nt * S::BN;
+    const int M = a.M, N = a.N, K = a.K;
+    const int KT = (K + kBK - 1) / kBK;
+
+    float* xs[2] = {smem, smem + S::BM * kLD};
+    float* ws[2] = {smem + 2 * S::BM * kLD, smem + 2 * S::BM * kLD + S::BN * kLD};
+
+    // Staging registers.
+    float4 xr[S::XPT];
+    const int wr = tid >> 1;        // W tile row staged by this thread
+    const int wh = tid & 1;         // which 16 of the 32 k
+    const int wrow = n0 + wr;
+    uint2 q4bits = make_uint2(0, 0);
+    uint32_t q4pair = 0;
+    uint4 q8bits = make_uint4(0, 0, 0, 0);
+    float wsafe[16];
+
+    const float* __restrict__ x = a.x;
+
+    auto load = [&](int kt) {
+        const int k0 = kt * kBK;
+#pragma unroll
+        for (int i = 0; i < S::XPT; ++i) {
+            const int idx = tid + i * S::NT;
+            if (idx < S::XV) {
+                const int r = idx >> 3;
+                const int c = idx & 7;
+                const int row = m0 + r;
+                const int k = k0 + 4 * c;
+                if constexpr (SAFE) {
+                    const float* p = x + static_cast<int64_t>(row) * K;
+                    const bool rv = row < M;
+                    xr[i].x = (rv && k + 0 < K) ? p[k + 0] : 0.0f;
+                    xr[i].y = (rv && k + 1 < K) ? p[k + 1] : 0.0f;
+                    xr[i].z = (rv && k + 2 < K) ? p[k + 2] : 0.0f;
+                    xr[i].w = (rv && k + 3 < K) ? p[k + 3] : 0.0f;
+                } else {
+                    xr[i] = row < M ? *reinterpret_cast<const float4*>(x + static_cast<int64_t>(row) * K + k)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
+        if constexpr (FMT == kFmtQ4) {
+            if (wrow < N) {
+                const uint8_t* p = static_cast<const uint8_t*>(a.payload) +
+                                   static_cast<int64_t>(wrow) * (K / 2) + kt * (kBK / 2) + wh * 8;
+                q4bits = *reinterpret_cast<const uint2*>(p);
+                q4pair = static_cast<const uint32_t*>(a.scale)[static_cast<int64_t>(wrow) * (K / kBK) + kt];
+            } else {
+                q4bits = make_uint2(0, 0);
+                q4pair = 0;
+            }
+        } else {
+            const int8_t* p = static_cast<const int8_t*>(a.payload) + static_cast<int64_t>(wrow) * K;
+            const int kb = k0 + wh * 16;
+            if constexpr (SAFE) {
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    wsafe[j] = (wrow < N && kb + j < K) ? static_cast<float>(p[kb + j]) : 0.0f;
+            } else {
+                q8bits = wrow < N ? *reinterpret_cast<const uint4*>(p + kb) : make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    auto commit = [&](int buf) {
+        float* xd = xs[buf];
+#pragma unroll
+        for (int i = 0; i < S::XPT; ++i) {
+            const int idx = tid + i * S::NT;
+            if (idx < S::XV) {
+                const int r = idx >> 3;
+                const int c = idx & 7;
+                *reinterpret_cast<float4*>(xd + r * kLD + 4 * c) = xr[i];
+            }
+        }
+        float wv[16];
+        if constexpr (FMT == kFmtQ4) {
+            const float s = half_bits_to_float(q4pair & 0xffffu);
+            const float m = half_bits_to_float(q4pair >> 16);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                wv[j] = fmaf(static_cast<float>(nibble(q4bits.x, j)), s, m);
+                wv[8 + j] = fmaf(static_cast<float>(nibble(q4bits.y, j)), s, m);
+            }
+        } else if constexpr (SAFE) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) wv[j] = wsafe[j];
+        } else {
+            const uint32_t words[4] = {q8bits.x, q8bits.y, q8bits.z, q8bits.w};
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                wv[j] = static_cast<float>(static_cast<int8_t>((words[j >> 2] >> (8 * (j & 3))) & 0xffu));
+        }
+        float* wd = ws[buf] + wr * kLD + wh * 16;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<float4*>(wd + 4 * j) = make_float4(wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]);
+    };
+
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // MFMA 16x16x4: lane l supplies A[l%16][l/16] and B[l/16][l%16]. The four
+    // lane groups c = l/16 take the physical k = 8c + kk at step kk, the same
+    // permutation for x and W, so each lane reads 8 consecutive k from LDS.
+    const int li = lane & 15;
+    const int kq = (lane >> 4) * 8;
+    auto compute = [&](int buf) {
+        const float* xsrc = xs[buf];
+        const float* wsrc = ws[buf];
+        float xa[TM][8];
+        float wb[TN][8];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const float* p = xsrc + (wm * TM * 16 + tm * 16 + li) * kLD + kq;
+            const float4 v0 = *reinterpret_cast<const float4*>(p);
+            const float4 v1 = *reinterpret_cast<const float4*>(p + 4);
+            xa[tm][0] = v0.x; xa[tm][1] = v0.y; xa[tm][2] = v0.z; xa[tm][3] = v0.w;
+            xa[tm][4] = v1.x; xa[tm][5] = v1.y; xa[tm][6] = v1.z; xa[tm][7] = v1.w;
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const float* p = wsrc + (wn * TN * 16 + tn * 16 + li) * kLD + kq;
+            const float4 v0 = *reinterpret_cast<const float4*>(p);
+            const float4 v1 = *reinterpret_cast<const float4*>(p + 4);
+            wb[tn][0] = v0.x; wb[tn][1] = v0.y; wb[tn][2] = v0.z; wb[tn][3] = v0.w;
+            wb[tn][4] = v1.x; wb[tn][5] = v1.y; wb[tn][6] = v1.z; wb[tn][7] = v1.w;
+        }
+#pragma unroll
+        for (int kk = 0; kk < 8; ++kk)
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[tm][kk], wb[tn][kk], acc[tm][tn], 0, 0, 0);
+    };
+
+    load(0);
+    commit(0);
+    __syncthreads();
+    for (int kt = 0; kt < KT; ++kt) {
+        const bool more = kt + 1 < KT;
+        if (more) load(kt + 1);
+        compute(kt & 1);
+        if (more) commit((kt + 1) & 1);
+        __syncthreads();
+    }
+
+    // Epilogue. Lane l holds D[4*(l/16) + r][l%16] of each 16x16 tile.
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int col = n0 + wn * TN * 16 + tn * 16 + li;
+        if (col >= N) continue;
+        float sc = 1.0f;
+        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = m0 + wm * TM * 16 + tm * 16 + 4 * (lane >> 4) + r;
+                if (row < M) {
+                    float v = acc[tm][tn][r];
+                    if constexpr (FMT == kFmtQ8) v *= sc;
+                    a.y[static_cast<int64_t>(row) * N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+template <int FMT, int WM, int WN, int TM, int TN, bool SAFE>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(TileArgs a, int tiles_n, int remap) {
+    __shared__ __attribute__((aligned(16))) float smem[TileShape<WM, WN, TM, TN>::SMEM];
+    int w = blockIdx.x;
+    if (remap) w = xcd_remap(w, gridDim.x);
+    gemm_tile<FMT, WM, WN, TM, TN, SAFE>(a, w / tiles_n, w % tiles_n, smem);
+}
+
+// Kernel arguments of a grouped launch, laid out as arrays so that the 96
+// projections of a 12-block RT-J pass fit in one launch under the 4 KiB
+// kernel-argument budget. Inputs are deduplicated into a small table (the
+// projections of a block share four of them).
+constexpr int kMaxInputs = 48;
+
+struct GroupArgs {
+    int count;                        // projections in this launch
+    int M;
+    int n_inputs;
+    int total_tiles;
+    const float* xs[kMaxInputs];
+    int xk[kMaxInputs];               // K of each input
+    const void* payload[kMaxGrouped];
+    const void* scale[kMaxGrouped];
+    float* y[kMaxGrouped];
+    int n[kMaxGrouped];
+    int tile_begin[kMaxGrouped];
+    uint8_t x_idx[kMaxGrouped];
+    uint8_t fmt[kMaxGrouped];
+};
+static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
+
+template <int WM, int WN, int TM, int TN>
+__global__ __launch_bounds__(WM * WN * 64) void grouped_kernel(GroupArgs g) {
+    using S = TileShape<WM, WN, TM, TN>;
+    __shared__ __attribute__((aligned(16))) float smem[S::SMEM];
+    const int w = blockIdx.x;
+    int i = 0;
+    while (i + 1 < g.count && g.tile_begin[i + 1] <= w) ++i;
+    const int xi = g.x_idx[i];
+    const int N = g.n[i];
+    const int tiles_n = (N + S::BN - 1) / S::BN;
+    const int local = w - g.tile_begin[i];
+    const TileArgs a{g.xs[xi], g.payload[i], g.scale[i], g.y[i], g.M, N, g.xk[xi]};
+    if (g.fmt[i] == kFmtQ4)
+        gemm_tile<kFmtQ4, WM, WN, TM, TN, false>(a, local / tiles_n, local % tiles_n, smem);
+    else
+        gemm_tile<kFmtQ8, WM, WN, TM, TN, false>(a, local / tiles_n, local % tiles_n, smem);
+}
+
+// Tile configurations: small M keeps all rows in one tile and splits N over
+// four waves; large M uses 128x128 tiles on a 2x2 wave grid.
+using Small = TileShape<1, 4, 5, 2>;
+using Large = TileShape<2, 2, 4, 4>;
+constexpr int kSmallMaxM = Small::BM;
+
+template <int FMT, bool SAFE>
+hipError_t launch_one(const TileArgs& a, hipStream_t stream) {
+    if (a.M <= kSmallMaxM) {
+        const int tn = (a.N + Small::BN - 1) / Small::BN;
+        const int tm = (a.M + Small::BM - 1) / Small::BM;
+        gemm_kernel<FMT, 1, 4, 5, 2, SAFE><<<tm * tn, Small::NT, 0, stream>>>(a, tn, 0);
+    } else {
+        const int tn = (a.N + Large::BN - 1) / Large::BN;
+        const int tm = (a.M + Large::BM - 1) / Large::BM;
+        gemm_kernel<FMT, 2, 2, 4, 4, SAFE><<<tm * tn, Large::NT, 0, stream>>>(a, tn, 1);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool grouped_ok(const ProjTask& t) {
+    // Vector loads need whole 32-wide K steps and 16-byte aligned rows.
+    return t.K % kBK == 0 && (reinterpret_cast<uintptr_t>(t.x) & 15) == 0 &&
+           (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0;
+}
+
+hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
+    const TileArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
+    const bool safe = !grouped_ok(t);
+    if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
+    return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
+}
+
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
+    if (M > kSmallMaxM) {
+        // Many row tiles: every projection alone already fills the GPU; one
+        // launch each keeps the XCD-contiguous tile order.
+        for (int i = 0; i < count; ++i) {
+            const hipError_t e = launch_gemm(tasks[i], M, stream);
+            if (e != hipSuccess) return e;
+        }
+        return hipSuccess;
+    }
+    // Small M: all projections in one launch (or as few as the argument
+    // budget allows), longest K first so the long tiles start early.
+    int order[8 * 64];
+    for (int i = 0; i < count; ++i) order[i] = i;
+    for (int i = 1; i < count; ++i) {                 // stable insertion sort, K descending
+        const int v = order[i];
+        int j = i - 1;
+        while (j >= 0 && tasks[order[j]].K < tasks[v].K) {
+            order[j + 1] = order[j];
+            --j;
+        }
+        order[j + 1] = v;
+    }
+    int done = 0;
+    while (done < count) {
+        GroupArgs g{};
+        g.M = static_cast<int>(M);
+        int tiles = 0;
+        while (done < count && g.count < kMaxGrouped) {
+            const ProjTask& t = tasks[order[done]];
+            int xi = -1;
+            for (int k = 0; k < g.n_inputs; ++k)
+                if (g.xs[k] == t.x && g.xk[k] == t.K) xi = k;
+            if (xi < 0) {
+                if (g.n_inputs == kMaxInputs) break;
+                xi = g.n_inputs++;
+                g.xs[xi] = t.x;
+                g.xk[xi] = t.K;
+            }
+            const int c = g.count++;
+            g.payload[c] = t.payload;
+            g.scale[c] = t.scale;
+            g.y[c] = t.y;
+            g.n[c] = t.N;
+            g.tile_begin[c] = tiles;
+            g.x_idx[c] = static_cast<uint8_t>(xi);
+            g.fmt[c] = static_cast<uint8_t>(t.fmt);
+            tiles += (t.N + Small::BN - 1) / Small::BN;   // one row tile: M <= BM
+            ++done;
+        }
+        g.total_tiles = tiles;
+        grouped_kernel<1, 4, 5, 2><<<tiles, Small::NT, 0, stream>>>(g);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+}  // namespace rtq

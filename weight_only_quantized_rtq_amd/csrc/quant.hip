@@ -1,0 +1,195 @@
+// Quantizers and element-wise dequantizers for the two weight formats.
+//
+// int4 (RT-J int4 model card, "Quantization format"): groups of 32 along K,
+// two codes per byte with the low nibble at the even index, one fp16
+// (scale, min) pair per group, W = code * scale + min; group ranges from a
+// min-MSE clip search over the shrink factors 1.00 .. 0.80.
+// int8 (RT-J int8 model card, "Quantization format"): one symmetric fp32
+// scale per output row, scale = max|row| / 127, W = q * scale.
+#include "rtq_device.h"
+#include "rtq_internal.h"
+
+namespace rtq {
+
+namespace {
+
+constexpr int kGroup = 32;
+
+// ---------------------------------------------------------------------------
+// int4 quantizer: one thread per 32-group. All decisions in fp64 with every
+// operation rounded on its own (no contraction), so the codes and pairs are a
+// deterministic function of the fp32 input.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const float* __restrict__ w,
+                                                          uint8_t* __restrict__ payload,
+                                                          uint32_t* __restrict__ pairs,
+                                                          int64_t n_groups, int64_t groups_per_row,
+                                                          int64_t K) {
+#pragma clang fp contract(off)
+    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= n_groups) return;
+    const int64_t row = gid / groups_per_row;
+    const int64_t grp = gid - row * groups_per_row;
+    const float4* src = reinterpret_cast<const float4*>(w + row * K + grp * kGroup);
+
+    double v[kGroup];
+#pragma unroll
+    for (int i = 0; i < kGroup / 4; ++i) {
+        const float4 f = src[i];
+        v[4 * i + 0] = f.x;
+        v[4 * i + 1] = f.y;
+        v[4 * i + 2] = f.z;
+        v[4 * i + 3] = f.w;
+    }
+    double wmin = v[0], wmax = v[0];
+#pragma unroll
+    for (int k = 1; k < kGroup; ++k) {
+        wmin = fmin(wmin, v[k]);
+        wmax = fmax(wmax, v[k]);
+    }
+
+    const double alphas[5] = {1.00, 0.95, 0.90, 0.85, 0.80};
+    double best_err = 0.0;
+    uint32_t best_pair = 0;
+    uint32_t best_codes[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int a = 0; a < 5; ++a) {
+        const double lo = alphas[a] * wmin;
+        const double hi = alphas[a] * wmax;
+        const uint32_t s16 = double_to_half_bits((hi - lo) / 15.0);
+        const uint32_t m16 = double_to_half_bits(lo);
+        const double s = half_bits_to_double(s16);
+        const double m = half_bits_to_double(m16);
+        double err = 0.0;
+        uint32_t codes[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+            double q = 0.0;
+            if (s > 0.0) {
+                q = __builtin_rint((v[k] - m) / s);
+                q = fmin(fmax(q, 0.0), 15.0);
+            }
+            const double recon = q * s + m;
+            const double d = recon - v[k];
+            const double sq = d * d;
+            err = err + sq;
+            codes[k / 8] |= static_cast<uint32_t>(q) << (4 * (k % 8));
+        }
+        if (a == 0 || err < best_err) {
+            best_err = err;
+            best_pair = s16 | (m16 << 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) best_codes[i] = codes[i];
+        }
+    }
+    uint4 out;
+    out.x = best_codes[0];
+    out.y = best_codes[1];
+    out.z = best_codes[2];
+    out.w = best_codes[3];
+    *reinterpret_cast<uint4*>(payload + row * (K / 2) + grp * (kGroup / 2)) = out;
+    pairs[gid] = best_pair;
+}
+
+// ---------------------------------------------------------------------------
+// int8 quantizer: one 256-thread workgroup per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void quantize_q8_kernel(const float* __restrict__ w,
+                                                          int8_t* __restrict__ q,
+                                                          float* __restrict__ scale, int64_t K) {
+    const int64_t row = blockIdx.x;
+    const float* src = w + row * K;
+    float amax = 0.0f;
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) amax = fmaxf(amax, fabsf(src[k]));
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
+    __syncthreads();
+    amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    const float sc = static_cast<float>(static_cast<double>(amax) / 127.0);
+    if (threadIdx.x == 0) scale[row] = sc;
+    const double scd = sc;
+    int8_t* dst = q + row * K;
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
+        double r = 0.0;
+        if (scd > 0.0) {
+            r = __builtin_rint(static_cast<double>(src[k]) / scd);
+            r = fmin(fmax(r, -127.0), 127.0);
+        }
+        dst[k] = static_cast<int8_t>(r);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Element-wise dequantizers (same arithmetic as the GEMM's staging step).
+// ---------------------------------------------------------------------------
+// One thread per 8 codes (one 32-bit word of payload).
+__global__ __launch_bounds__(256) void dequant_q4_kernel(const uint32_t* __restrict__ payload,
+                                                         const uint32_t* __restrict__ pairs,
+                                                         float* __restrict__ w, int64_t n_words,
+                                                         int64_t words_per_row, int64_t K) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= n_words) return;
+    const int64_t row = t / words_per_row;
+    const int64_t word = t - row * words_per_row;       // covers k = 8*word .. 8*word+7
+    const uint32_t bits = payload[t];
+    const uint32_t pr = pairs[row * (K / kGroup) + (word * 8) / kGroup];
+    const float s = half_bits_to_float(pr & 0xffffu);
+    const float m = half_bits_to_float(pr >> 16);
+    float o[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = fmaf(static_cast<float>(nibble(bits, i)), s, m);
+    float4* dst = reinterpret_cast<float4*>(w + row * K + word * 8);
+    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+}
+
+__global__ __launch_bounds__(256) void dequant_q8_kernel(const int8_t* __restrict__ q,
+                                                         const float* __restrict__ scale,
+                                                         float* __restrict__ w, int64_t total, int64_t K) {
+    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (t >= total) return;
+    const int64_t row = t / K;
+    w[t] = static_cast<float>(q[t]) * scale[row];
+}
+
+inline unsigned blocks_for(int64_t n, int per) {
+    return static_cast<unsigned>((n + per - 1) / per);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N,
+                              int64_t K, hipStream_t stream) {
+    const int64_t G = K / kGroup;
+    const int64_t n_groups = N * G;
+    quantize_q4_kernel<<<blocks_for(n_groups, 256), 256, 0, stream>>>(
+        w, payload, reinterpret_cast<uint32_t*>(pairs), n_groups, G, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, int64_t K,
+                              hipStream_t stream) {
+    quantize_q8_kernel<<<static_cast<unsigned>(N), 256, 0, stream>>>(w, q, scale, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N,
+                             int64_t K, hipStream_t stream) {
+    const int64_t words_per_row = K / 8;
+    const int64_t n_words = N * words_per_row;
+    dequant_q4_kernel<<<blocks_for(n_words, 256), 256, 0, stream>>>(
+        reinterpret_cast<const uint32_t*>(payload), reinterpret_cast<const uint32_t*>(pairs), w,
+        n_words, words_per_row, K);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8(const int8_t* q, const float* scale, float* w, int64_t N, int64_t K,
+                             hipStream_t stream) {
+    const int64_t total = N * K;
+    dequant_q8_kernel<<<blocks_for(total, 256), 256, 0, stream>>>(q, scale, w, total, K);
+    return hipGetLastError();
+}
+
+}  // namespace rtq

@@ -1,0 +1,39 @@
+// Internal launchers of the rtq library (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rtq {
+
+enum Fmt : int { kFmtQ4 = 1, kFmtQ8 = 2 };
+
+hipError_t launch_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N,
+                              int64_t K, hipStream_t stream);
+hipError_t launch_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, int64_t K,
+                              hipStream_t stream);
+hipError_t launch_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N,
+                             int64_t K, hipStream_t stream);
+hipError_t launch_dequant_q8(const int8_t* q, const float* scale, float* w, int64_t N, int64_t K,
+                             hipStream_t stream);
+
+// One projection of a grouped launch.
+struct ProjTask {
+    int fmt;
+    int N;
+    int K;
+    const void* payload;
+    const void* scale;
+    const float* x;
+    float* y;
+};
+
+// Single projection y[M][N] = x[M][K] . dequant(W)^T.
+hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
+
+// Several projections sharing M, in grouped launches. Every task must satisfy
+// grouped_ok().
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
+bool grouped_ok(const ProjTask& task);
+
+}  // namespace rtq
