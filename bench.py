@@ -222,7 +222,7 @@ def main():
             "bound": "mfma", "achieved": round(prim["kernel_tflops"], 3), "peak": PEAK_FP32_MFMA_TFLOPS,
             "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
             "traffic": None,
-            "kernel": "grouped_kernel (one launch per step)",
+            "kernel": "grouped_stream_kernel (one launch per step)",
             "launch_ms": round(prim["launch_ms"], 5),
             "weight_gbs_in_kernel": round(prim["kernel_weight_gbs"], 2),
         }

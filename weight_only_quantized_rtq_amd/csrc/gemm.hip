@@ -240,6 +240,213 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_kernel(TileArgs a, int tile
     gemm_tile<FMT, WM, WN, TM, TN, SAFE>(a, w / tiles_n, w % tiles_n, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Small-M streaming kernel (M <= 80). Every wave owns all TM*16 rows and TN*16
+// output columns over one K chunk and loads both operands straight from global
+// memory into registers, in MFMA operand layout: no LDS staging and no barrier
+// in the main loop. The packed weights are read exactly once.
+//
+// K is walked in blocks of 128 (four int4 groups). In a block, lane group
+// c = l/16 owns group 4b+c: at MFMA step t (0..31) it supplies k = 32(4b+c)+t,
+// for x (A operand) and W (B operand) alike. So each lane fetches one 16-byte
+// run of packed codes and one (scale, min) pair per column tile per block and
+// dequantizes with its own group's pair, and each x row is read as 32
+// consecutive floats per lane.
+//
+// A workgroup is 4 waves: 4/KS column slices x KS K-chunks. With KS > 1 the
+// chunk partials are summed through LDS in a fixed order (deterministic).
+// ---------------------------------------------------------------------------
+constexpr int kStreamTN = 4;
+
+template <int FMT, int TM, int TN>
+__device__ __forceinline__ void stream_tile(const TileArgs& a, int slice, int n_slices, int ks, int chunk,
+                                            float* red) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int li = lane & 15;
+    const int lc = lane >> 4;
+    const int M = a.M, N = a.N, K = a.K;
+    const int G = K / 32;                          // 32-wide groups along K
+    const int g_lo = chunk * G / ks;
+    const int g_hi = (chunk + 1) * G / ks;
+    const bool valid = slice < n_slices;
+    const int n0 = slice * TN * 16;
+
+    floatx4 acc[TM][TN];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    if (valid) {
+        // Out-of-range rows/columns read a clamped in-bounds row (their results
+        // are never stored); groups past the chunk read a clamped group of the
+        // same row and contribute zero through a zeroed weight. No load is
+        // predicated, so the loop body has no branches.
+        const float* xp[TM];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const int row = min(tm * 16 + li, M - 1);
+            xp[tm] = a.x + static_cast<int64_t>(row) * K;
+        }
+        const uint8_t* wp[TN];
+        const uint32_t* pp[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int col = min(n0 + tn * 16 + li, N - 1);
+            if constexpr (FMT == kFmtQ4) {
+                wp[tn] = static_cast<const uint8_t*>(a.payload) + static_cast<int64_t>(col) * (K / 2);
+                pp[tn] = static_cast<const uint32_t*>(a.scale) + static_cast<int64_t>(col) * G;
+            } else {
+                wp[tn] = reinterpret_cast<const uint8_t*>(static_cast<const int8_t*>(a.payload) + static_cast<int64_t>(col) * K);
+                pp[tn] = nullptr;
+            }
+        }
+
+        // Weight registers for one 128-k block: int4 -> 4 dwords + pair; int8 -> 8 dwords.
+        constexpr int WD = FMT == kFmtQ4 ? 4 : 8;
+        uint32_t wcur[TN][WD], wnxt[TN][WD];
+        uint32_t pcur[TN], pnxt[TN];
+
+        auto load_w = [&](int gblk, uint32_t (&wd)[TN][WD], uint32_t (&pr)[TN]) {
+            const int g = gblk + lc;
+            const bool live = g < g_hi;
+            const int gc = live ? g : g_hi - 1;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                if constexpr (FMT == kFmtQ4) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(wp[tn] + gc * 16);
+                    const uint32_t p = pp[tn][gc];
+                    wd[tn][0] = v.x; wd[tn][1] = v.y; wd[tn][2] = v.z; wd[tn][3] = v.w;
+                    pr[tn] = live ? p : 0u;           // (scale, min) = (0, 0): contributes 0
+                } else {
+                    const uint4* q = reinterpret_cast<const uint4*>(wp[tn] + gc * 32);
+                    const uint4 v0 = q[0];
+                    const uint4 v1 = q[1];
+                    wd[tn][0] = live ? v0.x : 0u; wd[tn][1] = live ? v0.y : 0u;
+                    wd[tn][2] = live ? v0.z : 0u; wd[tn][3] = live ? v0.w : 0u;
+                    wd[tn][4] = live ? v1.x : 0u; wd[tn][5] = live ? v1.y : 0u;
+                    wd[tn][6] = live ? v1.z : 0u; wd[tn][7] = live ? v1.w : 0u;
+                    pr[tn] = 0;
+                }
+            }
+        };
+        // x for steps 8u..8u+7 of the block starting at group gblk.
+        auto load_x = [&](int gblk, int u, float (&xa)[TM][8]) {
+            const int g = min(gblk + lc, g_hi - 1);
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const float4* p = reinterpret_cast<const float4*>(xp[tm] + g * 32 + 8 * u);
+                const float4 v0 = p[0];
+                const float4 v1 = p[1];
+                xa[tm][0] = v0.x; xa[tm][1] = v0.y; xa[tm][2] = v0.z; xa[tm][3] = v0.w;
+                xa[tm][4] = v1.x; xa[tm][5] = v1.y; xa[tm][6] = v1.z; xa[tm][7] = v1.w;
+            }
+        };
+        auto compute = [&](int u, const float (&xa)[TM][8], const uint32_t (&wd)[TN][WD], const uint32_t (&pr)[TN]) {
+            float s[TN], m[TN];
+            if constexpr (FMT == kFmtQ4) {
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    s[tn] = half_bits_to_float(pr[tn] & 0xffffu);
+                    m[tn] = half_bits_to_float(pr[tn] >> 16);
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int step = 8 * u + t;      // 0..31 within the group
+                float b[TN];
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    if constexpr (FMT == kFmtQ4) {
+                        b[tn] = fmaf(static_cast<float>(nibble(wd[tn][step >> 3], step & 7)), s[tn], m[tn]);
+                    } else {
+                        b[tn] = static_cast<float>(static_cast<int8_t>((wd[tn][step >> 2] >> (8 * (step & 3))) & 0xffu));
+                    }
+                }
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xa[tm][t], b[tn], acc[tm][tn], 0, 0, 0);
+            }
+        };
+
+        float xa0[TM][8], xa1[TM][8];
+        load_w(g_lo, wcur, pcur);
+        load_x(g_lo, 0, xa0);
+        for (int gb = g_lo; gb < g_hi; gb += 4) {
+            // Prefetch the next block unconditionally (clamped past the end).
+            load_w(gb + 4, wnxt, pnxt);
+            load_x(gb, 1, xa1);
+            compute(0, xa0, wcur, pcur);
+            load_x(gb, 2, xa0);
+            compute(1, xa1, wcur, pcur);
+            load_x(gb, 3, xa1);
+            compute(2, xa0, wcur, pcur);
+            load_x(gb + 4, 0, xa0);
+            compute(3, xa1, wcur, pcur);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+#pragma unroll
+                for (int i = 0; i < WD; ++i) wcur[tn][i] = wnxt[tn][i];
+                pcur[tn] = pnxt[tn];
+            }
+        }
+    }
+
+    if (ks > 1) {
+        // Chunk partials -> LDS, then chunk 0 adds chunks 1..ks-1 in order.
+        constexpr int R = TM * TN * 4;
+        if (chunk != 0) {
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) red[(wave * R + (tm * TN + tn) * 4 + r) * 64 + lane] = acc[tm][tn][r];
+        }
+        __syncthreads();
+        if (chunk != 0) return;
+        for (int c = 1; c < ks; ++c) {
+            const int src = wave + c;         // waves of one slice are consecutive
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[tm][tn][r] += red[(src * R + (tm * TN + tn) * 4 + r) * 64 + lane];
+        }
+    }
+    if (!valid) return;
+
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int col = n0 + tn * 16 + li;
+        if (col >= N) continue;
+        float sc = 1.0f;
+        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = tm * 16 + 4 * lc + r;
+                if (row < M) {
+                    float v = acc[tm][tn][r];
+                    if constexpr (FMT == kFmtQ8) v *= sc;
+                    a.y[static_cast<int64_t>(row) * N + col] = v;
+                }
+            }
+        }
+    }
+}
+
+// Number of K chunks for a projection: about 512 of K per wave, at most 4.
+__host__ __device__ inline int stream_ks(int K) {
+    const int G = K / 32;
+    return G >= 64 ? 4 : (G >= 32 ? 2 : 1);
+}
+
 // Kernel arguments of a grouped launch, laid out as arrays so that the 96
 // projections of a 12-block RT-J pass fit in one launch under the 4 KiB
 // kernel-argument budget. Inputs are deduplicated into a small table (the
@@ -263,22 +470,26 @@ struct GroupArgs {
 };
 static_assert(sizeof(GroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
-template <int WM, int WN, int TM, int TN>
-__global__ __launch_bounds__(WM * WN * 64) void grouped_kernel(GroupArgs g) {
-    using S = TileShape<WM, WN, TM, TN>;
-    __shared__ __attribute__((aligned(16))) float smem[S::SMEM];
+template <int TM>
+__global__ __launch_bounds__(256) void grouped_stream_kernel(GroupArgs g) {
+    __shared__ __attribute__((aligned(16))) float red[4 * TM * kStreamTN * 4 * 64];
     const int w = blockIdx.x;
     int i = 0;
     while (i + 1 < g.count && g.tile_begin[i + 1] <= w) ++i;
     const int xi = g.x_idx[i];
     const int N = g.n[i];
-    const int tiles_n = (N + S::BN - 1) / S::BN;
-    const int local = w - g.tile_begin[i];
-    const TileArgs a{g.xs[xi], g.payload[i], g.scale[i], g.y[i], g.M, N, g.xk[xi]};
+    const int K = g.xk[xi];
+    const int ks = stream_ks(K);
+    const int per_wg = 4 / ks;                                  // column slices per workgroup
+    const int n_slices = (N + kStreamTN * 16 - 1) / (kStreamTN * 16);
+    const int wave = threadIdx.x >> 6;
+    const int slice = (w - g.tile_begin[i]) * per_wg + wave / ks;
+    const int chunk = wave % ks;
+    const TileArgs a{g.xs[xi], g.payload[i], g.scale[i], g.y[i], g.M, N, K};
     if (g.fmt[i] == kFmtQ4)
-        gemm_tile<kFmtQ4, WM, WN, TM, TN, false>(a, local / tiles_n, local % tiles_n, smem);
+        stream_tile<kFmtQ4, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
     else
-        gemm_tile<kFmtQ8, WM, WN, TM, TN, false>(a, local / tiles_n, local % tiles_n, smem);
+        stream_tile<kFmtQ8, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
 }
 
 // Tile configurations: small M keeps all rows in one tile and splits N over
@@ -312,6 +523,7 @@ bool grouped_ok(const ProjTask& t) {
 hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
     const TileArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
     const bool safe = !grouped_ok(t);
+    if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
     if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
     return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
 }
@@ -363,11 +575,20 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
             g.tile_begin[c] = tiles;
             g.x_idx[c] = static_cast<uint8_t>(xi);
             g.fmt[c] = static_cast<uint8_t>(t.fmt);
-            tiles += (t.N + Small::BN - 1) / Small::BN;   // one row tile: M <= BM
+            const int ks = stream_ks(t.K);
+            const int n_slices = (t.N + kStreamTN * 16 - 1) / (kStreamTN * 16);
+            tiles += (n_slices + 4 / ks - 1) / (4 / ks);
             ++done;
         }
         g.total_tiles = tiles;
-        grouped_kernel<1, 4, 5, 2><<<tiles, Small::NT, 0, stream>>>(g);
+        const int tm = static_cast<int>((M + 15) / 16);
+        switch (tm) {
+            case 1: grouped_stream_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
+            case 2: grouped_stream_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
+            case 3: grouped_stream_kernel<3><<<tiles, 256, 0, stream>>>(g); break;
+            case 4: grouped_stream_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
+            default: grouped_stream_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
+        }
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
