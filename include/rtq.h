@@ -125,6 +125,22 @@ rtq_status rtq_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs,
 rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale,
                            int64_t N, int64_t K, void* stream);
 
+/* Arithmetic of the GEMM entry points, process-wide (default RTQ_MATH_SPLIT_BF16).
+ *
+ * RTQ_MATH_SPLIT_BF16: each fp32 activation is split exactly into three bf16
+ *   limbs (x = x1 + x2 + x3, no rounding); the int4/int8 codes are exact in
+ *   bf16, so every code*limb product is exact in fp32 and the bf16 matrix
+ *   cores (v_mfma_f32_16x16x32_bf16) accumulate them in fp32. Per 32-group:
+ *   y += scale*sum(code*x) + min*sum(x) (int4), y = scale[o]*sum(q*x) (int8).
+ *   Same accuracy class as an fp32 GEMM (fp32 accumulation of exact products).
+ * RTQ_MATH_FP32_MFMA: the weights are dequantized to fp32 while staging and the
+ *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction.
+ * Both satisfy the same parity bar against the fp64 reference. Calls already
+ * enqueued are not affected. Returns RTQ_ERR_FORMAT for an unknown mode. */
+enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1 };
+rtq_status rtq_set_math(int32_t mode);
+int32_t rtq_get_math(void);
+
 const char* rtq_status_string(rtq_status status);
 const char* rtq_last_error(void);   /* thread-local; valid until the next call on this thread */
 const char* rtq_version(void);

@@ -145,6 +145,14 @@ def test_quantize_dequant_validation(lib):
     assert lib.rtq_dequant_q8(B, C, A, 0, 64, None) == OK
 
 
+def test_math_mode_switch(lib):
+    assert lib.rtq_get_math() == rtq.MATH_SPLIT_BF16
+    assert lib.rtq_set_math(7) == ERR_FORMAT
+    assert lib.rtq_set_math(rtq.MATH_FP32_MFMA) == OK
+    assert lib.rtq_get_math() == rtq.MATH_FP32_MFMA
+    assert lib.rtq_set_math(rtq.MATH_SPLIT_BF16) == OK
+
+
 def test_struct_layout_matches_header():
     # rtq_proj: 4 x int32 then 4 pointers; rtq_block: 8 of them in name order.
     assert ctypes.sizeof(rtq._Proj) == 48

@@ -35,6 +35,14 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
+@pytest.fixture(params=[rtq.MATH_SPLIT_BF16, rtq.MATH_FP32_MFMA], ids=["split_bf16", "fp32_mfma"])
+def math(request):
+    """Runs a test under both arithmetic modes of the GEMM entry points."""
+    rtq.set_math(request.param)
+    yield request.param
+    rtq.set_math(rtq.MATH_SPLIT_BF16)
+
+
 def gpu_quantize(W: np.ndarray, fmt: str):
     return rtq.quantize(dev(W), fmt)
 
@@ -139,8 +147,8 @@ Q8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (100, 50, 100), (5, 
 
 
 @pytest.mark.parametrize("M,N,K", Q4_SHAPES)
-def test_gemm_q4_parity(M, N, K):
-    say(f"gemm_q4 M={M} N={N} K={K}")
+def test_gemm_q4_parity(M, N, K, math):
+    say(f"gemm_q4 M={M} N={N} K={K} math={math}")
     W = synth.weight(11, 0, 0, "wq", N, K)
     x = synth.activation(11, 0, "x_attn", M, K)
     ref = oracle.quantize_q4(W)
@@ -152,8 +160,8 @@ def test_gemm_q4_parity(M, N, K):
 
 
 @pytest.mark.parametrize("M,N,K", Q8_SHAPES)
-def test_gemm_q8_parity(M, N, K):
-    say(f"gemm_q8 M={M} N={N} K={K}")
+def test_gemm_q8_parity(M, N, K, math):
+    say(f"gemm_q8 M={M} N={N} K={K} math={math}")
     W = synth.weight(12, 0, 0, "w2", N, K, heavy="rows")
     x = synth.activation(12, 0, "h", M, K)
     ref = oracle.quantize_q8(W)
@@ -165,9 +173,9 @@ def test_gemm_q8_parity(M, N, K):
 
 
 @pytest.mark.parametrize("fmt,K", [("q4", 64), ("q4", 96), ("q4", 512), ("q8", 64), ("q8", 160), ("q8", 40)])
-def test_gemm_identity_is_bit_exact(fmt, K):
+def test_gemm_identity_is_bit_exact(fmt, K, math):
     """x = I_K gives y = W^T exactly: checks the in-GEMM unpack/dequant bit for bit."""
-    say(f"identity {fmt} K={K}")
+    say(f"identity {fmt} K={K} math={math}")
     N = 72
     W = synth.weight(13, 0, 0, "wv", N, K, heavy="rows")
     ref = oracle.quantize(W, fmt)
@@ -179,7 +187,7 @@ def test_gemm_identity_is_bit_exact(fmt, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(80, 512, 512), (200, 96, 2048)])
-def test_gemm_exact_integer_arithmetic(M, N, K):
+def test_gemm_exact_integer_arithmetic(M, N, K, math):
     """Integer x and dyadic (scale, min): every partial sum is exact in fp32, so
     any summation order must reproduce the oracle bit for bit."""
     x = synth.uniform_ints(M, (M, K), -4, 4).astype(np.float32)
@@ -196,7 +204,7 @@ def test_gemm_exact_integer_arithmetic(M, N, K):
     assert np.array_equal(y8.astype(np.float64), oracle.project_q8(x, q, scale))
 
 
-def test_gemm_guard_bands_and_determinism():
+def test_gemm_guard_bands_and_determinism(math):
     """Outputs land only inside y (canaries around it survive) and a rerun is
     bitwise identical (no atomics, fixed reduction order)."""
     M, N, K = 77, 130, 512
@@ -249,7 +257,7 @@ def make_block(cfg, set_, b, M, recipe, xs=None, heavy=None, skip=()):
 
 
 @pytest.mark.parametrize("recipe_name", ["mixed", "all_q8"])
-def test_block_project_one_block(recipe_name):
+def test_block_project_one_block(recipe_name, math):
     say(f"block_project one block recipe={recipe_name}")
     recipe = rtq.RECIPE_MIXED if recipe_name == "mixed" else rtq.RECIPE_ALL_Q8
     assert recipe == (oracle.RECIPE_MIXED if recipe_name == "mixed" else oracle.RECIPE_ALL_Q8)
@@ -262,7 +270,7 @@ def test_block_project_one_block(recipe_name):
         assert err <= TOL, (name, err)
 
 
-def test_block_project_skips_missing_gate_and_runs_multi_tile():
+def test_block_project_skips_missing_gate_and_runs_multi_tile(math):
     """A block without wg (ungated attention) leaves nothing behind for it, and
     M above one row tile goes through the per-projection launches."""
     for M in (80, 333):
@@ -305,8 +313,8 @@ def _sampled_check(blocks, refs_w, xs_all, M, rng, n_rows=24, n_cols=24):
 
 
 @pytest.mark.parametrize("M,heavy", [(synth.M_GOLDEN, None), (synth.M_LARGE, "rows")])
-def test_full_size_twelve_blocks_sampled(M, heavy):
-    say(f"full-size 12 blocks M={M} heavy={heavy}")
+def test_full_size_twelve_blocks_sampled(M, heavy, math):
+    say(f"full-size 12 blocks M={M} heavy={heavy} math={math}")
     cfg = 4 if M == synth.M_GOLDEN else 5
     per_block = M == synth.M_GOLDEN          # as in the benchmark: own inputs per block at M=80
     shared = None if per_block else {n: synth.activation(cfg, synth.SHARED_BLOCK, n, M) for n in synth.INPUT_WIDTH}

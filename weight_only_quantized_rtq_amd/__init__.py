@@ -37,7 +37,10 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 
 # Every symbol include/rtq.h declares.
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_block_project", "rtq_dequant_q4", "rtq_dequant_q8",
-           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_status_string", "rtq_last_error", "rtq_version")
+           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_set_math", "rtq_get_math", "rtq_status_string",
+           "rtq_last_error", "rtq_version")
+
+MATH_SPLIT_BF16, MATH_FP32_MFMA = 0, 1
 
 
 class RtqError(RuntimeError):
@@ -78,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, i64, i64, vp]
         f.restype = ctypes.c_int
+    lib.rtq_set_math.argtypes = [i32]
+    lib.rtq_set_math.restype = ctypes.c_int
+    lib.rtq_get_math.argtypes = []
+    lib.rtq_get_math.restype = i32
     lib.rtq_status_string.argtypes = [ctypes.c_int]
     lib.rtq_status_string.restype = ctypes.c_char_p
     lib.rtq_last_error.argtypes = []
@@ -90,6 +97,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def version() -> str:
     return load_library().rtq_version().decode()
+
+
+def set_math(mode: int) -> None:
+    """MATH_SPLIT_BF16 (default) or MATH_FP32_MFMA for the GEMM entry points (rtq_set_math)."""
+    _check(load_library().rtq_set_math(mode))
+
+
+def get_math() -> int:
+    return int(load_library().rtq_get_math())
 
 
 def _check(status: int) -> None:

@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librtq.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_split.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}",

@@ -3,6 +3,7 @@
 // each entry point are in rtq.h.
 #include <rtq.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -29,6 +30,8 @@ rtq_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+std::atomic<int> g_math{rtq::kMathSplitBf16};
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -84,7 +87,21 @@ rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, con
 
 }  // namespace
 
+namespace rtq {
+int math_mode() { return g_math.load(std::memory_order_relaxed); }
+}  // namespace rtq
+
 extern "C" {
+
+rtq_status rtq_set_math(int32_t mode) {
+    clear_error();
+    if (mode != RTQ_MATH_SPLIT_BF16 && mode != RTQ_MATH_FP32_MFMA)
+        return fail(RTQ_ERR_FORMAT, "rtq_set_math: unknown mode %d", mode);
+    g_math.store(mode, std::memory_order_relaxed);
+    return RTQ_OK;
+}
+
+int32_t rtq_get_math(void) { return g_math.load(std::memory_order_relaxed); }
 
 const char* rtq_version(void) { return "rtq 0.1.0 gfx950"; }
 

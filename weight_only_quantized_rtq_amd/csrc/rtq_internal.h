@@ -28,6 +28,10 @@ struct ProjTask {
     float* y;
 };
 
+// Arithmetic of the GEMM kernels (process-wide, see rtq_set_math).
+enum Math : int { kMathSplitBf16 = 0, kMathFp32Mfma = 1 };
+int math_mode();
+
 // Single projection y[M][N] = x[M][K] . dequant(W)^T.
 hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
 
@@ -35,5 +39,10 @@ hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
 // grouped_ok().
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 bool grouped_ok(const ProjTask& task);
+
+// bf16 split-limb kernels (gemm_split.hip). Tasks must satisfy split_ok().
+bool split_ok(const ProjTask& task);
+hipError_t launch_split_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
+hipError_t launch_split_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 
 }  // namespace rtq
