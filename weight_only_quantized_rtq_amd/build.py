@@ -30,6 +30,8 @@ FLAGS = [
     "-Wno-unused-function",
     # Keep the compiler from forming packed fp32 ops (v_pk_*_f32).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the per-group epilogue updates them on the VALU.
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

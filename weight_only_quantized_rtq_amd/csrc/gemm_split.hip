@@ -50,17 +50,26 @@ __device__ __forceinline__ void split2(float a, float b, uint32_t& h, uint32_t& 
     lo = (fbits(sa) >> 16) | (fbits(sb) & 0xffff0000u);
 }
 
+// Byte k of a word -> fp32 (v_cvt_f32_ubyte{k}: exact).
+__device__ __forceinline__ float ubyte0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
+__device__ __forceinline__ float ubyte3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
+
+// High halves of two fp32 (bf16 truncation of exact small integers) -> one bf16x2 word.
+__device__ __forceinline__ uint32_t pack_hi(float even, float odd) {
+    return __builtin_amdgcn_perm(fbits(odd), fbits(even), 0x07060302u);
+}
+
 // 8 int4 codes (one payload word, low nibble first) -> 8 bf16 (exact integers).
 __device__ __forceinline__ u32x4 codes4_to_bf16(uint32_t w) {
     const uint32_t lo = w & 0x0f0f0f0fu;           // codes 0,2,4,6 in bytes 0..3
     const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;    // codes 1,3,5,7
     u32x4 r;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const float e = static_cast<float>((lo >> (8 * d)) & 0xffu);
-        const float o = static_cast<float>((hi >> (8 * d)) & 0xffu);
-        r[d] = (fbits(e) >> 16) | (fbits(o) & 0xffff0000u);
-    }
+    r[0] = pack_hi(ubyte0(lo), ubyte0(hi));
+    r[1] = pack_hi(ubyte1(lo), ubyte1(hi));
+    r[2] = pack_hi(ubyte2(lo), ubyte2(hi));
+    r[3] = pack_hi(ubyte3(lo), ubyte3(hi));
     return r;
 }
 
@@ -73,7 +82,7 @@ __device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t w0, uint32_t w1) {
         const int sh = 16 * (d & 1);
         const float e = static_cast<float>(static_cast<int8_t>((w >> sh) & 0xffu));
         const float o = static_cast<float>(static_cast<int8_t>((w >> (sh + 8)) & 0xffu));
-        r[d] = (fbits(e) >> 16) | (fbits(o) & 0xffff0000u);
+        r[d] = pack_hi(e, o);
     }
     return r;
 }
@@ -91,11 +100,15 @@ struct SplitArgs {
     int M, N, K;
 };
 
-// LDS of one stage: 3 limb planes [BM][kXS] bf16 + group sums [BM] fp32.
+// LDS: two stages of 3 limb planes [BM][kXS] bf16, then a ring of the last 8
+// groups' sums X_g [8][BM] fp32 (read by the deferred min term).
+constexpr int kRing = 8;
 template <int BM>
 struct StageLayout {
     static constexpr int PLANE = BM * kXS * 2;                     // bytes
-    static constexpr int BYTES = 3 * PLANE + BM * 4;
+    static constexpr int BYTES = 3 * PLANE;
+    static constexpr int RING = 2 * BYTES;                         // offset of the X ring
+    static constexpr int TOTAL = 2 * BYTES + kRing * BM * 4;
 };
 
 // One BM x (WN*TN*16) tile (this workgroup's rows m0.., columns n0..) over the
@@ -120,15 +133,14 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
     const int shalf = tid & 1;
     const bool stager = srow < BM;
     const float* xsrc = a.x + static_cast<int64_t>(min(m0 + min(srow, BM - 1), M - 1)) * K + 16 * shalf;
-    float4 xr[4];
-    auto stage_load = [&](int g) {
+    auto stage_load = [&](int g, float4 (&xr)[4]) {
         if (stager) {
             const float4* p = reinterpret_cast<const float4*>(xsrc + g * 32);
 #pragma unroll
             for (int i = 0; i < 4; ++i) xr[i] = p[i];
         }
     };
-    auto stage_store = [&](int buf) {
+    auto stage_store = [&](int buf, int g, const float4 (&xr)[4]) {
         if (stager) {
             unsigned char* base = smem + buf * L::BYTES;
             const float v[16] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w, xr[1].x, xr[1].y, xr[1].z, xr[1].w,
@@ -154,7 +166,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             // group sum: first 16 + last 16, the same order in both threads
             const float other = __shfl_xor(sum, 1, 64);
             const float gsum = shalf ? other + sum : sum + other;
-            if (shalf == 0) reinterpret_cast<float*>(base + 3 * L::PLANE)[srow] = gsum;
+            if (shalf == 0) reinterpret_cast<float*>(smem + L::RING)[(g & (kRing - 1)) * BM + srow] = gsum;
         }
     };
 
@@ -173,9 +185,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             prow[tn] = nullptr;
         }
     }
-    uint32_t wq[TN][2];      // packed codes of the group being fetched
-    uint32_t wp[TN];         // its (scale, min) pair (int4)
-    auto w_load = [&](int g) {
+    auto w_load = [&](int g, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
@@ -197,16 +207,23 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
 #pragma unroll
         for (int j = 0; j < TN; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-    auto compute = [&](int buf, const uint32_t (&cq)[TN][2], const uint32_t (&cp)[TN]) {
+    // int4 min term, deferred: lane group c keeps min_g of group 4b+c for its
+    // columns; every 4 groups one fp32 MFMA 16x16x4 adds sum_g X_g[row] * min_g[col].
+    float mreg[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) mreg[tn] = 0.0f;
+
+    auto compute = [&](int buf, int g, const uint32_t (&cq)[TN][2], const uint32_t (&cp)[TN]) {
         const unsigned char* base = smem + buf * L::BYTES;
         u32x4 b[TN];
-        float s[TN], mn[TN];
+        float s[TN];
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
                 b[tn] = codes4_to_bf16(cq[tn][0]);
                 s[tn] = half_bits_to_float(cp[tn] & 0xffffu);
-                mn[tn] = half_bits_to_float(cp[tn] >> 16);
+                const float mn = half_bits_to_float(cp[tn] >> 16);
+                mreg[tn] = lc == (g & 3) ? mn : mreg[tn];
             } else {
                 b[tn] = codes8_to_bf16(cq[tn][0], cq[tn][1]);
             }
@@ -219,17 +236,13 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             const u32x4 xm = *reinterpret_cast<const u32x4*>(base + 1 * L::PLANE + off);
             const u32x4 xl = *reinterpret_cast<const u32x4*>(base + 2 * L::PLANE + off);
             if constexpr (FMT == kFmtQ4) {
-                const floatx4 X = *reinterpret_cast<const floatx4*>(base + 3 * L::PLANE + (r + 4 * lc) * 4);
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     floatx4 p = mfma_bf16(xl, b[tn], floatx4{0.f, 0.f, 0.f, 0.f});
                     p = mfma_bf16(xm, b[tn], p);
                     p = mfma_bf16(xh, b[tn], p);
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        float t = fmaf(s[tn], p[e], acc[tm][tn][e]);
-                        acc[tm][tn][e] = fmaf(mn[tn], X[e], t);
-                    }
+                    for (int e = 0; e < 4; ++e) acc[tm][tn][e] = fmaf(s[tn], p[e], acc[tm][tn][e]);
                 }
             } else {
 #pragma unroll
@@ -241,36 +254,68 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             }
         }
     };
-
-    // ---- main loop: one 32-wide group per stage, double-buffered LDS ----
-    uint32_t cq[TN][2], cp[TN];
-    stage_load(0);
-    w_load(0);
-    stage_store(0);
+    // After group g: if it closes a block of 4 (or is the last), add the block's min term.
+    auto min_flush = [&](int g) {
+        if constexpr (FMT == kFmtQ4) {
+            if ((g & 3) != 3 && g != G - 1) return;
+            const int gc = (g & ~3) + lc;                 // this lane group's group
+            const bool live = gc <= g;
+            const float* ring = reinterpret_cast<const float*>(smem + L::RING) + (gc & (kRing - 1)) * BM;
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        cq[tn][0] = wq[tn][0];
-        cq[tn][1] = wq[tn][1];
-        cp[tn] = wp[tn];
-    }
-    __syncthreads();
-    for (int g = 0; g < G; ++g) {
-        const bool more = g + 1 < G;
-        if (more) {
-            stage_load(g + 1);
-            w_load(g + 1);
-        }
-        compute(g & 1, cq, cp);
-        if (more) {
-            stage_store((g + 1) & 1);
+            for (int tm = 0; tm < TM; ++tm) {
+                const float xv = live ? ring[wm * TM * 16 + tm * 16 + li] : 0.0f;
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                cq[tn][0] = wq[tn][0];
-                cq[tn][1] = wq[tn][1];
-                cp[tn] = wp[tn];
+                for (int tn = 0; tn < TN; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, mreg[tn], acc[tm][tn], 0, 0, 0);
             }
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) mreg[tn] = 0.0f;
         }
-        __syncthreads();
+    };
+
+    // ---- main loop: one 32-wide group per stage, double-buffered LDS; global
+    //      loads run two groups ahead through two register slots (the loop is
+    //      unrolled by two so the slots are fixed registers) ----
+    float4 xr0[4], xr1[4];
+    uint32_t wq0[TN][2], wq1[TN][2], wp0[TN], wp1[TN];
+    stage_load(0, xr0);
+    w_load(0, wq0, wp0);
+    if (G > 1) {
+        stage_load(1, xr1);
+        w_load(1, wq1, wp1);
+    }
+    stage_store(0, 0, xr0);
+    __syncthreads();
+    for (int g = 0; g < G; g += 2) {
+        {
+            uint32_t cq[TN][2], cp[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) { cq[tn][0] = wq0[tn][0]; cq[tn][1] = wq0[tn][1]; cp[tn] = wp0[tn]; }
+            if (g + 2 < G) {
+                stage_load(g + 2, xr0);
+                w_load(g + 2, wq0, wp0);
+            }
+            compute(0, g, cq, cp);
+            min_flush(g);
+            if (g + 1 < G) stage_store(1, g + 1, xr1);
+            __syncthreads();
+        }
+        if (g + 1 >= G) break;
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            uint32_t cq[TN][2], cp[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) { cq[tn][0] = wq1[tn][0]; cq[tn][1] = wq1[tn][1]; cp[tn] = wp1[tn]; }
+            if (g + 3 < G) {
+                stage_load(g + 3, xr1);
+                w_load(g + 3, wq1, wp1);
+            }
+            compute(1, g + 1, cq, cp);
+            min_flush(g + 1);
+            if (g + 2 < G) stage_store(0, g + 2, xr0);
+            __syncthreads();
+        }
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile ----
@@ -309,7 +354,7 @@ constexpr int kLBN = kLWN * kLTN * 16;
 
 template <int FMT>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * StageLayout<kLBM>::BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[StageLayout<kLBM>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     split_tile<FMT, kLWM, kLWN, kLTM, kLTN>(a, (w / tiles_n) * kLBM, (w % tiles_n) * kLBN, smem);
 }
@@ -351,7 +396,7 @@ __device__ __forceinline__ void grouped_dispatch(const SplitArgs& a, int fmt, in
 
 template <int TM>
 __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * StageLayout<TM * 16>::BYTES];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[StageLayout<TM * 16>::TOTAL];
     const int w = blockIdx.x;
     int i = 0;
     while (i + 1 < g.count && g.tile_begin[i + 1] <= w) ++i;
