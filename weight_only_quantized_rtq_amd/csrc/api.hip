@@ -3,6 +3,7 @@
 // each entry point are in rtq.h.
 #include <rtq.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <cstdio>
@@ -148,7 +149,8 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
     rtq::ProjTask grouped[RTQ_MAX_BLOCKS * 8];
     rtq::ProjTask single[RTQ_MAX_BLOCKS * 8];
     Range outs[RTQ_MAX_BLOCKS * 8];
-    int n_grouped = 0, n_single = 0, n_outs = 0;
+    Range ins[RTQ_MAX_BLOCKS * 8 * 3];
+    int n_grouped = 0, n_single = 0, n_outs = 0, n_ins = 0;
     for (int b = 0; b < n_blocks; ++b) {
         const rtq_proj* p = &blocks[b].wq;
         for (int j = 0; j < 8; ++j) {
@@ -161,29 +163,31 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
             if (d.reserved != 0) return fail(RTQ_ERR_SHAPE, "%s: reserved field must be 0", name);
             const rtq_status s = check_proj(name, d.fmt, d.x, d.payload, d.scale, d.y, M, d.N, d.K);
             if (s != RTQ_OK) return s;
-            const Range ry = range_of(d.y, M * int64_t(d.N) * 4);
-            for (int i = 0; i < n_outs; ++i)
-                if (overlaps(ry, outs[i])) return fail(RTQ_ERR_OVERLAP, "%s: y overlaps another output", name);
-            outs[n_outs++] = ry;
+            if (M == 0) continue;
+            outs[n_outs++] = range_of(d.y, M * int64_t(d.N) * 4);
+            const int64_t pb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 2) : int64_t(d.N) * d.K;
+            const int64_t sb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 32) * 4 : int64_t(d.N) * 4;
+            ins[n_ins++] = range_of(d.x, M * int64_t(d.K) * 4);
+            ins[n_ins++] = range_of(d.payload, pb);
+            ins[n_ins++] = range_of(d.scale, sb);
             const rtq::ProjTask t{d.fmt, d.N, d.K, d.payload, d.scale, d.x, d.y};
             if (rtq::grouped_ok(t)) grouped[n_grouped++] = t;
             else single[n_single++] = t;
         }
     }
-    // Outputs must not overlap any input of any projection either.
-    for (int b = 0; b < n_blocks; ++b) {
-        const rtq_proj* p = &blocks[b].wq;
-        for (int j = 0; j < 8; ++j) {
-            const rtq_proj& d = p[j];
-            if (!d.payload || M == 0) continue;
-            const int64_t pb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 2) : int64_t(d.N) * d.K;
-            const int64_t sb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 32) * 4 : int64_t(d.N) * 4;
-            const Range ins[3] = {range_of(d.x, M * int64_t(d.K) * 4), range_of(d.payload, pb), range_of(d.scale, sb)};
-            for (int i = 0; i < n_outs; ++i)
-                for (const Range& r : ins)
-                    if (overlaps(outs[i], r))
-                        return fail(RTQ_ERR_OVERLAP, "rtq_block_project: an output overlaps block %d %s's inputs", b, names[j]);
-        }
+    // Outputs must be pairwise disjoint and must not overlap any input of any
+    // projection: sort the outputs, then check neighbours and binary-search each input.
+    std::sort(outs, outs + n_outs, [](const Range& a, const Range& b) { return a.lo < b.lo; });
+    for (int i = 1; i < n_outs; ++i)
+        if (overlaps(outs[i - 1], outs[i]))
+            return fail(RTQ_ERR_OVERLAP, "rtq_block_project: two projections write overlapping outputs");
+    for (int i = 0; i < n_ins; ++i) {
+        const Range r = ins[i];
+        // first output whose end lies past the input's start (outputs are disjoint and sorted)
+        const Range* it = std::upper_bound(outs, outs + n_outs, r.lo,
+                                           [](uintptr_t v, const Range& o) { return v < o.hi; });
+        if (it != outs + n_outs && overlaps(*it, r))
+            return fail(RTQ_ERR_OVERLAP, "rtq_block_project: an output overlaps a projection's input");
     }
     if (M == 0) return RTQ_OK;
     const hipStream_t st = static_cast<hipStream_t>(stream);

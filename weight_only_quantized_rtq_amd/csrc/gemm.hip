@@ -523,16 +523,14 @@ bool grouped_ok(const ProjTask& t) {
 hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
     const TileArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
     const bool safe = !grouped_ok(t);
-    if (!safe && math_mode() == kMathSplitBf16 && split_ok(t)) {
-        if (M <= kSmallMaxM) return launch_split_grouped(&t, 1, M, stream);
-        return launch_split_gemm(t, M, stream);
-    }
+    if (!safe && math_mode() == kMathSplitBf16 && split_ok(t)) return launch_split(&t, 1, M, stream);
     if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
     if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
     return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
 }
 
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
+    if (math_mode() == kMathSplitBf16) return launch_split(tasks, count, M, stream);
     if (M > kSmallMaxM) {
         // Many row tiles: every projection alone already fills the GPU; one
         // launch each keeps the XCD-contiguous tile order.
@@ -542,7 +540,6 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
         }
         return hipSuccess;
     }
-    if (math_mode() == kMathSplitBf16) return launch_split_grouped(tasks, count, M, stream);
     // Small M: all projections in one launch (or as few as the argument
     // budget allows), longest K first so the long tiles start early.
     int order[8 * 64];

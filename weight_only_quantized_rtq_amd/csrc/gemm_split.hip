@@ -13,16 +13,23 @@
 // v_mfma_f32_16x16x32_bf16 accumulates them in fp32: the per-group code sum
 // P_g[m][o] = sum_{k in g} code[o][k] * x[m][k] is an fp32 dot product of the
 // exact values. One MFMA covers exactly one 32-wide int4 group, so
-//   int4: y = sum_g ( scale_g[o] * P_g + min_g[o] * X_g[m] ),  X_g[m] = sum_{k in g} x[m][k]
+//   int4: y = sum_g scale_g[o] * P_g  +  sum_g min_g[o] * X_g[m],   X_g[m] = sum_{k in g} x[m][k]
 //   int8: y = scale[o] * sum_k q[o][k] * x[m][k]
 // which is W = code*scale + min (int4) and W = q*scale (int8) by
-// distributivity. The two fp32 multiply-adds per group run on the VALU.
+// distributivity. The scale term is one fp32 FMA per output per group on the
+// VALU; the min term is a K/32-long contraction run on the fp32 matrix cores
+// (v_mfma_f32_16x16x4_f32, four groups per instruction).
 //
-// Data movement. A workgroup stages its x rows once per group into LDS as the
-// three bf16 planes plus the group sums X_g (shared by all its waves); each wave
-// streams its own packed weight columns from global memory straight into
-// registers in MFMA operand layout (4 bytes of int4 codes or 8 bytes of int8
-// codes per lane per group), so the packed payload is read once per row tile.
+// Data movement.
+//  1. A pre-pass splits every distinct activation once into a limb image in a
+//     device workspace (three bf16 planes in MFMA operand order with an XOR
+//     swizzle that makes the LDS reads conflict-free, plus the group sums X_g).
+//  2. The GEMM streams each 32-wide group of its row block from that image into
+//     a three-stage LDS ring with global_load_lds_dwordx4 (direct to LDS: no
+//     registers, no VALU), one group ahead of the compute, one barrier per group.
+//  3. Each wave streams its own packed weight columns from global memory into
+//     registers in MFMA operand layout (4 bytes of int4 codes or 8 bytes of int8
+//     codes per lane per group): the packed payload is read once per row block.
 #include "rtq_device.h"
 #include "rtq_internal.h"
 
@@ -32,8 +39,6 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kXS = 40;   // limb-plane row stride in bf16 (80 bytes: conflict-free b128 reads)
 
 __device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
@@ -92,32 +97,149 @@ __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
                                                    0, 0, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Limb image of one activation x [M][K] (G = K/32 groups, RB row blocks of 16,
+// RB*16 >= M; rows >= M are zero):
+//   block (g, rb) of 3 KB at byte ((g*RB + rb)*3 + limb) * 1024, limb 0 = x1
+//   (high), 1 = x2, 2 = x3; inside a limb, row r (0..15) and 16-byte chunk c
+//   (k = 8c..8c+7 of the group) sit at (r*4 + (c ^ ((r>>2)&3))) * 16;
+//   then the group sums X[g][row] (fp32, RB*16 rows per group).
+// For a fixed group the RB blocks are contiguous, so a row block of BM rows is
+// one contiguous run of BM/16 * 3 KB.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int64_t image_plane_bytes(int G, int RB) { return int64_t(G) * RB * 3072; }
+__host__ __device__ inline int64_t image_bytes(int G, int RB) {
+    return image_plane_bytes(G, RB) + int64_t(G) * RB * 16 * 4;
+}
+__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
+
+constexpr int kMaxImages = 48;
+struct PrepArgs {
+    int count;
+    int pad;
+    const float* x[kMaxImages];
+    unsigned char* img[kMaxImages];
+    int M[kMaxImages];
+    int K[kMaxImages];
+    int RB[kMaxImages];
+    int block_begin[kMaxImages + 1];    // 256-thread blocks per image, prefix
+};
+static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB");
+
+// One thread per (row, 8-wide chunk). A wave covers one 16-row block of one
+// group (4 threads per row), so each limb it writes is one contiguous 1 KB run,
+// and the group sum of a row is two shuffles in a fixed order.
+__global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
+    const int b = blockIdx.x;
+    int i = 0;
+    while (i + 1 < p.count && p.block_begin[i + 1] <= b) ++i;
+    const int M = p.M[i], K = p.K[i], RB = p.RB[i];
+    const int G = K / 32;
+    const int64_t t = static_cast<int64_t>(b - p.block_begin[i]) * 256 + threadIdx.x;
+    const int64_t total = int64_t(RB) * 16 * G * 4;
+    const bool live = t < total;
+    const int c = static_cast<int>(t & 3);
+    const int r = static_cast<int>((t >> 2) & 15);
+    const int64_t blk_id = t >> 6;                      // g * RB + rb
+    const int rb = static_cast<int>(blk_id % RB);
+    const int g = static_cast<int>(blk_id / RB);
+    const int row = rb * 16 + r;
+    float v[8];
+    if (live && row < M) {
+        const float4* src = reinterpret_cast<const float4*>(p.x[i] + static_cast<int64_t>(row) * K + g * 32 + c * 8);
+        const float4 a = src[0], bb = src[1];
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
+    }
+    uint32_t h[4], m[4], l[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], h[j], m[j], l[j]);
+    float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+    const float s1 = __shfl_xor(s, 1, 64);
+    s = (c & 1) ? s1 + s : s + s1;                  // chunks (0+1), (2+3)
+    const float s2 = __shfl_xor(s, 2, 64);
+    s = (c & 2) ? s2 + s : s + s2;                  // (0+1) + (2+3)
+    if (!live) return;
+    unsigned char* img = p.img[i];
+    unsigned char* blk = img + blk_id * 3072 + swz(r, c) * 16;
+    *reinterpret_cast<uint4*>(blk + 0) = make_uint4(h[0], h[1], h[2], h[3]);
+    *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(m[0], m[1], m[2], m[3]);
+    *reinterpret_cast<uint4*>(blk + 2048) = make_uint4(l[0], l[1], l[2], l[3]);
+    if (c == 0) {
+        float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB));
+        X[static_cast<int64_t>(g) * RB * 16 + row] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// GEMM on the limb image.
+// ---------------------------------------------------------------------------
 struct SplitArgs {
-    const float* x;
+    const unsigned char* img;     // limb image of x
     const void* payload;
     const void* scale;
-    float* y;
-    int M, N, K;
+    float* y;                     // output (or this K chunk's partial), [M][N]
+    int M, N, K, RB;
+    int g_lo, g_cnt;              // groups [g_lo, g_lo + g_cnt) of K
 };
 
-// LDS: two stages of 3 limb planes [BM][kXS] bf16, then a ring of the last 8
-// groups' sums X_g [8][BM] fp32 (read by the deferred min term).
-constexpr int kRing = 8;
-template <int BM>
-struct StageLayout {
-    static constexpr int PLANE = BM * kXS * 2;                     // bytes
-    static constexpr int BYTES = 3 * PLANE;
-    static constexpr int RING = 2 * BYTES;                         // offset of the X ring
-    static constexpr int TOTAL = 2 * BYTES + kRing * BM * 4;
+constexpr int kStages = 2;        // LDS ring depth (loads run one group ahead)
+constexpr int kRing = 8;          // group sums kept for the deferred min term
+constexpr int kXSlot = 128;       // floats per group-sum slot (>= BM; waves 0 and 1 copy 64 rows each)
+
+// LDS map of a workgroup: x stages, group-sum ring, dummy DMA target and, when
+// the weights stream through LDS (PDW > 0), a per-wave weight ring of PDW + 1
+// slots of TN x (256 B codes + 256 B pairs / second code word).
+template <int BM, int TN = 1, int PDW = 0>
+struct Lds {
+    static constexpr int NSTAGE = PDW > 0 ? PDW + 1 : kStages;    // x stages
+    static constexpr int STAGE = (BM / 16) * 3072;
+    static constexpr int XRING = NSTAGE * STAGE;
+    static constexpr int DUMMY = XRING + kRing * kXSlot * 4;
+    static constexpr int WSLOT = 4 * TN * 512;                    // one step, all four waves
+    static constexpr int WRING = DUMMY + 1024;
+    static constexpr int TOTAL = WRING + (PDW > 0 ? (PDW + 1) * WSLOT : 0);
+    static constexpr int COPIES = (BM / 16) * 3;                   // 1 KB copies per stage
+    static constexpr int PER_WAVE = (COPIES + 3) / 4;
 };
 
-// One BM x (WN*TN*16) tile (this workgroup's rows m0.., columns n0..) over the
-// whole K. Waves are laid out WM x WN; each owns TM x TN 16x16 output tiles.
-template <int FMT, int WM, int WN, int TM, int TN>
-__device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, unsigned char* smem) {
+// Wait until at most N vector-memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+__device__ __forceinline__ void dma16(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const void* src, void* lds_base) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
+}
+
+// One BM x (WN*TN*16) tile (rows m0.., columns n0..) over the whole K. The 4
+// waves are laid out WM x WN; each owns TM x TN 16x16 output tiles.
+//
+// K order: the tile walks the groups starting at group `rot` (cyclically), so
+// the column tiles that share a row block (rot = their column-tile index) read
+// different groups at any moment and, after the first group, find the limb
+// image already in L2 instead of all missing on the same lines together.
+// Iteration i is called step i below; the group it processes is (rot + i) % G.
+//
+// Weights: with PDW == 0 each wave loads its codes and pairs into registers one
+// step ahead (enough when they come from L2); with PDW > 0 they are copied by
+// DMA into a per-wave LDS ring PDW steps ahead (for weights streamed from HBM).
+template <int FMT, int WM, int WN, int TM, int TN, int PDW = 0>
+__device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
-    constexpr int NT = WM * WN * 64;
-    using L = StageLayout<BM>;
+    using L = Lds<BM, TN, PDW>;
+    static_assert(WM * WN == 4, "four waves");
+    static_assert(PDW <= 3, "prefetch depth");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
@@ -125,49 +247,30 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
     const int wn = wave % WN;
     const int li = lane & 15;
     const int lc = lane >> 4;
-    const int M = a.M, N = a.N, K = a.K;
-    const int G = K / 32;
+    const int M = a.M, N = a.N, K = a.K, RB = a.RB;
+    const int G = K / 32;                                 // groups of the whole row (image, pairs)
+    const int GS = a.g_cnt;                               // steps: groups of this K chunk
+    const int rb0 = m0 / 16;
 
-    // ---- x staging: thread -> (row, 16 consecutive k of the group) ----
-    const int srow = tid >> 1;
-    const int shalf = tid & 1;
-    const bool stager = srow < BM;
-    const float* xsrc = a.x + static_cast<int64_t>(min(m0 + min(srow, BM - 1), M - 1)) * K + 16 * shalf;
-    auto stage_load = [&](int g, float4 (&xr)[4]) {
-        if (stager) {
-            const float4* p = reinterpret_cast<const float4*>(xsrc + g * 32);
+    // ---- async stage copies: 1 KB per wave instruction, all waves issue the same count ----
+    const unsigned char* xsum = a.img + image_plane_bytes(G, RB);
+    const int xrow = min(m0 + (wave & 1) * 64 + lane, RB * 16 - 1);   // clamped: rows past BM are never read
+    auto group_of = [&](int i) { const int g = rot + i; return a.g_lo + (g >= GS ? g - GS : g); };
+    auto stage_copy = [&](int i) {
+        const int g = group_of(i);
+        const unsigned char* src = a.img + (static_cast<int64_t>(g) * RB + rb0) * 3072;
+        unsigned char* dst = smem + (i % L::NSTAGE) * L::STAGE;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xr[i] = p[i];
+        for (int j = 0; j < L::PER_WAVE; ++j) {
+            const int cpy = wave * L::PER_WAVE + j;
+            if (cpy < L::COPIES)
+                dma16(src + cpy * 1024 + lane * 16, dst + cpy * 1024);
+            else
+                dma16(src + lane * 16, smem + L::DUMMY);               // keeps the per-wave count uniform
         }
-    };
-    auto stage_store = [&](int buf, int g, const float4 (&xr)[4]) {
-        if (stager) {
-            unsigned char* base = smem + buf * L::BYTES;
-            const float v[16] = {xr[0].x, xr[0].y, xr[0].z, xr[0].w, xr[1].x, xr[1].y, xr[1].z, xr[1].w,
-                                 xr[2].x, xr[2].y, xr[2].z, xr[2].w, xr[3].x, xr[3].y, xr[3].z, xr[3].w};
-            uint32_t hw[8], mw[8], lw[8];
-            float sum = 0.0f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                split2(v[2 * j], v[2 * j + 1], hw[j], mw[j], lw[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 16; ++j) sum += v[j];
-            const int off = (srow * kXS + 16 * shalf) * 2;
-            uint4* ph = reinterpret_cast<uint4*>(base + 0 * L::PLANE + off);
-            uint4* pm = reinterpret_cast<uint4*>(base + 1 * L::PLANE + off);
-            uint4* pl = reinterpret_cast<uint4*>(base + 2 * L::PLANE + off);
-            ph[0] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-            ph[1] = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-            pm[0] = make_uint4(mw[0], mw[1], mw[2], mw[3]);
-            pm[1] = make_uint4(mw[4], mw[5], mw[6], mw[7]);
-            pl[0] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-            pl[1] = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-            // group sum: first 16 + last 16, the same order in both threads
-            const float other = __shfl_xor(sum, 1, 64);
-            const float gsum = shalf ? other + sum : sum + other;
-            if (shalf == 0) reinterpret_cast<float*>(smem + L::RING)[(g & (kRing - 1)) * BM + srow] = gsum;
-        }
+        // group sums: waves 0 and 1 copy 64 rows each, waves 2 and 3 a dummy
+        unsigned char* xdst = wave < 2 ? smem + L::XRING + ((i % kRing) * kXSlot + wave * 64) * 4 : smem + L::DUMMY;
+        dma4(xsum + (static_cast<int64_t>(g) * RB * 16 + xrow) * 4, xdst);
     };
 
     // ---- weights: lane (li, lc) of column tile tn holds row n0 + wn*TN*16 + tn*16 + li,
@@ -185,7 +288,10 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             prow[tn] = nullptr;
         }
     }
-    auto w_load = [&](int g, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
+    constexpr int NW = FMT == kFmtQ4 ? 2 * TN : TN;                  // weight loads per group
+    constexpr int NVM = L::PER_WAVE + 1 + NW;                         // vector-memory ops per group
+    auto w_load = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
+        const int g = group_of(i);
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
@@ -196,6 +302,44 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
                 const uint2 v = *reinterpret_cast<const uint2*>(wrow[tn] + g * 32);
                 wq[tn][0] = v.x;
                 wq[tn][1] = v.y;
+                wp[tn] = 0;
+            }
+        }
+    };
+
+    // Weight ring (PDW > 0): slot s of this wave holds, per column tile, 64 lanes
+    // x 4 bytes of codes (int4: the lane's 8 codes; int8: its first 4 codes) and
+    // 64 x 4 bytes of the pair (int4) or the lane's last 4 codes (int8).
+    unsigned char* wbase = smem + L::WRING + wave * TN * 512;
+    auto w_issue = [&](int i) {
+        if constexpr (PDW > 0) {
+            const int g = group_of(i);
+            unsigned char* slot = wbase + (i % (PDW + 1)) * L::WSLOT;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                if constexpr (FMT == kFmtQ4) {
+                    dma4(wrow[tn] + g * 16, slot + tn * 512);
+                    dma4(prow[tn] + g, slot + tn * 512 + 256);
+                } else {
+                    dma4(wrow[tn] + g * 32, slot + tn * 512);
+                    dma4(wrow[tn] + g * 32 + 4, slot + tn * 512 + 256);
+                }
+            }
+        }
+    };
+    auto w_read = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
+        const unsigned char* slot = wbase + (i % (PDW + 1)) * L::WSLOT;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const uint32_t w0 = reinterpret_cast<const uint32_t*>(slot + tn * 512)[lane];
+            const uint32_t w1 = reinterpret_cast<const uint32_t*>(slot + tn * 512 + 256)[lane];
+            if constexpr (FMT == kFmtQ4) {
+                wq[tn][0] = w0;
+                wq[tn][1] = 0;
+                wp[tn] = w1;
+            } else {
+                wq[tn][0] = w0;
+                wq[tn][1] = w1;
                 wp[tn] = 0;
             }
         }
@@ -213,8 +357,9 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) mreg[tn] = 0.0f;
 
-    auto compute = [&](int buf, int g, const uint32_t (&cq)[TN][2], const uint32_t (&cp)[TN]) {
-        const unsigned char* base = smem + buf * L::BYTES;
+    const int aoff = swz(li, lc) * 16;                                  // this lane's A chunk in a limb
+    auto compute = [&](int i, const uint32_t (&cq)[TN][2], const uint32_t (&cp)[TN]) {
+        const unsigned char* base = smem + (i % L::NSTAGE) * L::STAGE;
         u32x4 b[TN];
         float s[TN];
 #pragma unroll
@@ -223,18 +368,17 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
                 b[tn] = codes4_to_bf16(cq[tn][0]);
                 s[tn] = half_bits_to_float(cp[tn] & 0xffffu);
                 const float mn = half_bits_to_float(cp[tn] >> 16);
-                mreg[tn] = lc == (g & 3) ? mn : mreg[tn];
+                mreg[tn] = lc == (i & 3) ? mn : mreg[tn];
             } else {
                 b[tn] = codes8_to_bf16(cq[tn][0], cq[tn][1]);
             }
         }
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const int r = wm * TM * 16 + tm * 16;
-            const int off = ((r + li) * kXS + 8 * lc) * 2;
-            const u32x4 xh = *reinterpret_cast<const u32x4*>(base + 0 * L::PLANE + off);
-            const u32x4 xm = *reinterpret_cast<const u32x4*>(base + 1 * L::PLANE + off);
-            const u32x4 xl = *reinterpret_cast<const u32x4*>(base + 2 * L::PLANE + off);
+            const unsigned char* blk = base + (wm * TM + tm) * 3072 + aoff;
+            const u32x4 xh = *reinterpret_cast<const u32x4*>(blk);
+            const u32x4 xm = *reinterpret_cast<const u32x4*>(blk + 1024);
+            const u32x4 xl = *reinterpret_cast<const u32x4*>(blk + 2048);
             if constexpr (FMT == kFmtQ4) {
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
@@ -254,13 +398,13 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
             }
         }
     };
-    // After group g: if it closes a block of 4 (or is the last), add the block's min term.
-    auto min_flush = [&](int g) {
+    // After step i: if it closes a block of 4 steps (or is the last), add the block's min term.
+    auto min_flush = [&](int i) {
         if constexpr (FMT == kFmtQ4) {
-            if ((g & 3) != 3 && g != G - 1) return;
-            const int gc = (g & ~3) + lc;                 // this lane group's group
-            const bool live = gc <= g;
-            const float* ring = reinterpret_cast<const float*>(smem + L::RING) + (gc & (kRing - 1)) * BM;
+            if ((i & 3) != 3 && i != GS - 1) return;
+            const int ic = (i & ~3) + lc;                 // this lane group's step
+            const bool live = ic <= i;
+            const float* ring = reinterpret_cast<const float*>(smem + L::XRING) + (ic % kRing) * kXSlot;
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
                 const float xv = live ? ring[wm * TM * 16 + tm * 16 + li] : 0.0f;
@@ -273,49 +417,62 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, u
         }
     };
 
-    // ---- main loop: one 32-wide group per stage, double-buffered LDS; global
-    //      loads run two groups ahead through two register slots (the loop is
-    //      unrolled by two so the slots are fixed registers) ----
-    float4 xr0[4], xr1[4];
-    uint32_t wq0[TN][2], wq1[TN][2], wp0[TN], wp1[TN];
-    stage_load(0, xr0);
-    w_load(0, wq0, wp0);
-    if (G > 1) {
-        stage_load(1, xr1);
-        w_load(1, wq1, wp1);
+    // ---- main loop: while step i computes, step i+1 streams into the other
+    //      LDS stage (and the weights of step i+1, or of step i+PDW through the
+    //      weight ring). A stage or ring slot is refilled only after the barrier
+    //      that follows every wave's last read of it. ----
+    uint32_t wq[TN][2], wp[TN], cq[TN][2], cp[TN];
+    // With PDW > 0, step j's x stage and weights go out as one batch of NB
+    // vector-memory ops, PDW steps ahead: batches 0..PDW-1 in the prologue, batch
+    // i+PDW in iteration i.
+    constexpr int NB = L::PER_WAVE + 1 + 2 * TN;
+    if constexpr (PDW == 0) {
+        stage_copy(0);
+        w_load(0, wq, wp);
+    } else {
+#pragma unroll
+        for (int j = 0; j < PDW; ++j)
+            if (j < GS) {
+                stage_copy(j);
+                w_issue(j);
+            }
     }
-    stage_store(0, 0, xr0);
-    __syncthreads();
-    for (int g = 0; g < G; g += 2) {
-        {
-            uint32_t cq[TN][2], cp[TN];
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) { cq[tn][0] = wq0[tn][0]; cq[tn][1] = wq0[tn][1]; cp[tn] = wp0[tn]; }
-            if (g + 2 < G) {
-                stage_load(g + 2, xr0);
-                w_load(g + 2, wq0, wp0);
-            }
-            compute(0, g, cq, cp);
-            min_flush(g);
-            if (g + 1 < G) stage_store(1, g + 1, xr1);
-            __syncthreads();
+    for (int i = 0; i < GS; ++i) {
+        if constexpr (PDW == 0) {
+            wait_vm<0>();                                 // this wave's part of step i has landed
+        } else {
+            // Batches issued after step i's: steps i+1 .. min(i+PDW-1, GS-1).
+            const int later = min(PDW - 1, GS - 1 - i);
+            if (later >= 2 && PDW >= 3) wait_vm<(PDW >= 3 ? 2 : 0) * NB>();
+            else if (later >= 1) wait_vm<NB>();
+            else wait_vm<0>();
         }
-        if (g + 1 >= G) break;
+        // Barrier without a memory fence: the LDS data of step i came in by DMA
+        // and is complete after the wait above (in every wave, after the barrier);
+        // nothing else writes LDS, and a fence would also wait for later steps.
+        __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        {
-            uint32_t cq[TN][2], cp[TN];
+        if constexpr (PDW == 0) {
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) { cq[tn][0] = wq1[tn][0]; cq[tn][1] = wq1[tn][1]; cp[tn] = wp1[tn]; }
-            if (g + 3 < G) {
-                stage_load(g + 3, xr1);
-                w_load(g + 3, wq1, wp1);
+            for (int tn = 0; tn < TN; ++tn) {
+                cq[tn][0] = wq[tn][0];
+                cq[tn][1] = wq[tn][1];
+                cp[tn] = wp[tn];
             }
-            compute(1, g + 1, cq, cp);
-            min_flush(g + 1);
-            if (g + 2 < G) stage_store(0, g + 2, xr0);
-            __syncthreads();
+            if (i + 1 < GS) {
+                stage_copy(i + 1);
+                w_load(i + 1, wq, wp);
+            }
+        } else {
+            w_read(i, cq, cp);
+            if (i + PDW < GS) {
+                stage_copy(i + PDW);
+                w_issue(i + PDW);
+            }
         }
         __builtin_amdgcn_sched_barrier(0);
+        compute(i, cq, cp);
+        min_flush(i);
     }
 
     // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile ----
@@ -347,70 +504,143 @@ __device__ __forceinline__ int xcd_remap_split(int w, int G) {
     return start + local;
 }
 
-// Large M: 128 x 128 tiles, 2 x 2 waves of 64 x 64.
-constexpr int kLWM = 2, kLWN = 2, kLTM = 4, kLTN = 4;
+// Large M: 128 x 128 tiles, 4 waves side by side along N, each 128 rows x 32 columns.
+constexpr int kLWM = 1, kLWN = 4, kLTM = 8, kLTN = 2;
 constexpr int kLBM = kLWM * kLTM * 16;
 constexpr int kLBN = kLWN * kLTN * 16;
 
 template <int FMT>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[StageLayout<kLBM>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
-    split_tile<FMT, kLWM, kLWN, kLTM, kLTN>(a, (w / tiles_n) * kLBM, (w % tiles_n) * kLBN, smem);
+    const int nt = w % tiles_n;
+    split_tile<FMT, kLWM, kLWN, kLTM, kLTN>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
-// Small M (<= 80): one row tile of TM*16 rows; 4 waves side by side along N,
+// Small M (<= 80): one row block of TM*16 rows; 4 waves side by side along N,
 // each with TN column tiles, TN chosen per projection so that TN*K is about
 // constant (long-K projections get narrower tiles and more workgroups).
 constexpr int kMaxSplitGrouped = 96;
-constexpr int kMaxSplitInputs = 48;
 
 struct SplitGroupArgs {
     int count;
     int M;
-    int n_inputs;
-    int total;
-    const float* xs[kMaxSplitInputs];
-    int xk[kMaxSplitInputs];
+    int RB;
+    int pad;
+    const unsigned char* img[kMaxSplitGrouped];
     const void* payload[kMaxSplitGrouped];
     const void* scale[kMaxSplitGrouped];
     float* y[kMaxSplitGrouped];
     int n[kMaxSplitGrouped];
-    int tile_begin[kMaxSplitGrouped];
-    uint8_t x_idx[kMaxSplitGrouped];
+    int k[kMaxSplitGrouped];
     uint8_t fmt[kMaxSplitGrouped];
+    uint8_t ks[kMaxSplitGrouped];       // K chunks (> 1: y[] is the partial buffer [ks][M][N])
 };
 static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
-__host__ __device__ inline int split_tn(int K) {
-    return K >= 2048 ? 1 : (K >= 1024 ? 2 : 4);
-}
-
-template <int TM, int TN>
-__device__ __forceinline__ void grouped_dispatch(const SplitArgs& a, int fmt, int n0, unsigned char* smem) {
-    if (fmt == kFmtQ4)
-        split_tile<kFmtQ4, 1, 4, TM, TN>(a, 0, n0, smem);
-    else
-        split_tile<kFmtQ8, 1, 4, TM, TN>(a, 0, n0, smem);
+// Small M: column tiles of 4 waves x 4 x 16 = 256 and K chunks of at most 16
+// groups (512 of K), so every workgroup does about the same work.
+constexpr int kSmallBN = 256;
+constexpr int kSmallPDW = 2;        // x stages and weights (streamed from HBM) two steps ahead
+constexpr int kChunkGroups = 16;
+__host__ __device__ inline int split_chunks(int K) {
+    const int G = K / 32;
+    return (G + kChunkGroups - 1) / kChunkGroups;
 }
 
 template <int TM>
 __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[StageLayout<TM * 16>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, kSmallPDW>::TOTAL];
+    // Find this workgroup's projection: tiles are numbered projection by
+    // projection, (column block, K chunk) within one.
     const int w = blockIdx.x;
-    int i = 0;
-    while (i + 1 < g.count && g.tile_begin[i + 1] <= w) ++i;
-    const int xi = g.x_idx[i];
-    const int K = g.xk[xi];
-    const SplitArgs a{g.xs[xi], g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], K};
-    const int tn = split_tn(K);
-    const int n0 = (w - g.tile_begin[i]) * 4 * tn * 16;
-    if (tn == 1)
-        grouped_dispatch<TM, 1>(a, g.fmt[i], n0, smem);
-    else if (tn == 2)
-        grouped_dispatch<TM, 2>(a, g.fmt[i], n0, smem);
+    int i = 0, begin = 0;
+    for (;;) {
+        const int tiles = (g.n[i] + kSmallBN - 1) / kSmallBN * g.ks[i];
+        if (w < begin + tiles || i + 1 == g.count) break;
+        begin += tiles;
+        ++i;
+    }
+    const int K = g.k[i];
+    const int G = K / 32;
+    const int ks = g.ks[i];
+    const int local = w - begin;
+    const int cb = local / ks, kc = local % ks;
+    const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
+    float* y = g.y[i] + static_cast<int64_t>(ks > 1 ? kc : 0) * g.M * g.n[i];
+    const SplitArgs a{g.img[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo};
+    const int rot = cb % (g_hi - g_lo);
+    if (g.fmt[i] == kFmtQ4)
+        split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
     else
-        grouped_dispatch<TM, 4>(a, g.fmt[i], n0, smem);
+        split_tile<kFmtQ8, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
+}
+
+// Sums the K-chunk partials of split projections in chunk order.
+constexpr int kMaxReduce = 96;
+struct ReduceArgs {
+    int count;
+    int pad;
+    const float* part[kMaxReduce];
+    float* y[kMaxReduce];
+    int64_t elems[kMaxReduce];
+    int ks[kMaxReduce];
+};
+static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments must stay within 4 KiB");
+
+__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs r) {
+    const int i = blockIdx.y;
+    const int64_t n = r.elems[i];
+    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
+        float s = r.part[i][e];
+        for (int c = 1; c < r.ks[i]; ++c) s += r.part[i][c * n + e];
+        r.y[i][e] = s;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host side.
+// ---------------------------------------------------------------------------
+struct Input {
+    const float* x;
+    int K;
+    int64_t offset;     // of its image in the workspace
+};
+
+hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB, hipStream_t stream) {
+    int done = 0;
+    while (done < n_in) {
+        PrepArgs p{};
+        int blocks = 0;
+        while (done < n_in && p.count < kMaxImages) {
+            const Input& u = in[done++];
+            const int c = p.count++;
+            p.x[c] = u.x;
+            p.img[c] = ws + u.offset;
+            p.M[c] = M;
+            p.K[c] = u.K;
+            p.RB[c] = RB;
+            p.block_begin[c] = blocks;
+            const int64_t threads = int64_t(RB) * 16 * (u.K / 32) * 4;
+            blocks += static_cast<int>((threads + 255) / 256);
+        }
+        p.block_begin[p.count] = blocks;
+        prep_kernel<<<blocks, 256, 0, stream>>>(p);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+void release_threshold_once(int device) {
+    static bool done[64] = {};
+    if (device < 0 || device >= 64 || done[device]) return;
+    hipMemPool_t pool;
+    if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
+        uint64_t keep = ~0ull;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+    }
+    done[device] = true;
 }
 
 }  // namespace
@@ -420,69 +650,123 @@ bool split_ok(const ProjTask& t) {
            (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0;
 }
 
-hipError_t launch_split_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
-    const SplitArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
-    const int tn = (t.N + kLBN - 1) / kLBN;
-    const int tm = static_cast<int>((M + kLBM - 1) / kLBM);
-    if (t.fmt == kFmtQ4)
-        split_gemm_kernel<kFmtQ4><<<tm * tn, 256, 0, stream>>>(a, tn);
-    else
-        split_gemm_kernel<kFmtQ8><<<tm * tn, 256, 0, stream>>>(a, tn);
-    return hipGetLastError();
-}
+// All projections (sharing M) of this call: split every distinct input once into
+// a stream-ordered workspace, run the GEMMs, release the workspace.
+hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream_t stream) {
+    const int M = static_cast<int>(M64);
+    const bool small = M <= 80;
+    const int tm_small = (M + 15) / 16;
+    const int RB = small ? tm_small : ((M + kLBM - 1) / kLBM) * (kLBM / 16);
 
-hipError_t launch_split_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
-    int order[8 * 64];
-    for (int i = 0; i < count; ++i) order[i] = i;
-    for (int i = 1; i < count; ++i) {                 // stable insertion sort, K descending
-        const int v = order[i];
-        int j = i - 1;
-        while (j >= 0 && tasks[order[j]].K < tasks[v].K) {
-            order[j + 1] = order[j];
-            --j;
+    // Distinct inputs (pointer, K).
+    Input inputs[8 * 64];
+    int img_of[8 * 64];
+    int n_in = 0;
+    int64_t ws_bytes = 0;
+    for (int i = 0; i < count; ++i) {
+        int found = -1;
+        for (int j = 0; j < n_in; ++j)
+            if (inputs[j].x == tasks[i].x && inputs[j].K == tasks[i].K) found = j;
+        if (found < 0) {
+            found = n_in++;
+            inputs[found] = Input{tasks[i].x, tasks[i].K, ws_bytes};
+            ws_bytes += (image_bytes(tasks[i].K / 32, RB) + 255) / 256 * 256;
         }
-        order[j + 1] = v;
+        img_of[i] = found;
     }
-    int done = 0;
-    while (done < count) {
-        SplitGroupArgs g{};
-        g.M = static_cast<int>(M);
-        int tiles = 0;
-        while (done < count && g.count < kMaxSplitGrouped) {
-            const ProjTask& t = tasks[order[done]];
-            int xi = -1;
-            for (int k = 0; k < g.n_inputs; ++k)
-                if (g.xs[k] == t.x && g.xk[k] == t.K) xi = k;
-            if (xi < 0) {
-                if (g.n_inputs == kMaxSplitInputs) break;
-                xi = g.n_inputs++;
-                g.xs[xi] = t.x;
-                g.xk[xi] = t.K;
+    int64_t part_off[8 * 64];
+    for (int i = 0; i < count; ++i) {
+        part_off[i] = -1;
+        const int ks = split_chunks(tasks[i].K);
+        if (small && ks > 1) {
+            part_off[i] = ws_bytes;
+            ws_bytes += (int64_t(ks) * M * tasks[i].N * 4 + 255) / 256 * 256;
+        }
+    }
+    int device = 0;
+    (void)hipGetDevice(&device);
+    release_threshold_once(device);
+    void* ws = nullptr;
+    hipError_t e = hipMallocAsync(&ws, static_cast<size_t>(ws_bytes), stream);
+    if (e != hipSuccess) return e;
+    unsigned char* wsb = static_cast<unsigned char*>(ws);
+    e = run_prep(inputs, n_in, wsb, M, RB, stream);
+
+    if (e == hipSuccess && small) {
+        int order[8 * 64];
+        for (int i = 0; i < count; ++i) order[i] = i;
+        for (int i = 1; i < count; ++i) {                 // stable insertion sort, K descending
+            const int v = order[i];
+            int j = i - 1;
+            while (j >= 0 && tasks[order[j]].K < tasks[v].K) {
+                order[j + 1] = order[j];
+                --j;
             }
-            const int c = g.count++;
-            g.payload[c] = t.payload;
-            g.scale[c] = t.scale;
-            g.y[c] = t.y;
-            g.n[c] = t.N;
-            g.tile_begin[c] = tiles;
-            g.x_idx[c] = static_cast<uint8_t>(xi);
-            g.fmt[c] = static_cast<uint8_t>(t.fmt);
-            const int bn = 4 * split_tn(t.K) * 16;
-            tiles += (t.N + bn - 1) / bn;
-            ++done;
+            order[j + 1] = v;
         }
-        g.total = tiles;
-        switch (static_cast<int>((M + 15) / 16)) {
-            case 1: split_grouped_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
-            case 2: split_grouped_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
-            case 3: split_grouped_kernel<3><<<tiles, 256, 0, stream>>>(g); break;
-            case 4: split_grouped_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
-            default: split_grouped_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
+        int done = 0;
+        ReduceArgs red{};
+        int red_blocks = 0;
+        while (e == hipSuccess && done < count) {
+            SplitGroupArgs g{};
+            g.M = M;
+            g.RB = RB;
+            int tiles = 0;
+            while (done < count && g.count < kMaxSplitGrouped) {
+                const int ti = order[done++];
+                const ProjTask& t = tasks[ti];
+                const int c = g.count++;
+                const int ks = split_chunks(t.K);
+                g.img[c] = wsb + inputs[img_of[ti]].offset;
+                g.payload[c] = t.payload;
+                g.scale[c] = t.scale;
+                g.y[c] = ks > 1 ? reinterpret_cast<float*>(wsb + part_off[ti]) : t.y;
+                g.n[c] = t.N;
+                g.k[c] = t.K;
+                g.fmt[c] = static_cast<uint8_t>(t.fmt);
+                g.ks[c] = static_cast<uint8_t>(ks);
+                tiles += (t.N + kSmallBN - 1) / kSmallBN * ks;
+                if (ks > 1) {
+                    const int r = red.count++;
+                    red.part[r] = reinterpret_cast<const float*>(wsb + part_off[ti]);
+                    red.y[r] = t.y;
+                    red.elems[r] = int64_t(M) * t.N;
+                    red.ks[r] = ks;
+                    const int64_t need = (red.elems[r] + 255) / 256;
+                    const int nb = need < 1024 ? static_cast<int>(need) : 1024;
+                    red_blocks = red_blocks > nb ? red_blocks : nb;
+                }
+            }
+            switch (tm_small) {
+                case 1: split_grouped_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
+                case 2: split_grouped_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
+                case 3: split_grouped_kernel<3><<<tiles, 256, 0, stream>>>(g); break;
+                case 4: split_grouped_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
+                default: split_grouped_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
+            }
+            e = hipGetLastError();
+            if (e == hipSuccess && red.count) {
+                reduce_kernel<<<dim3(red_blocks, red.count), 256, 0, stream>>>(red);
+                e = hipGetLastError();
+                red = ReduceArgs{};
+                red_blocks = 0;
+            }
         }
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+    } else if (e == hipSuccess) {
+        for (int i = 0; i < count && e == hipSuccess; ++i) {
+            const ProjTask& t = tasks[i];
+            const SplitArgs a{wsb + inputs[img_of[i]].offset, t.payload, t.scale, t.y, M, t.N, t.K, RB, 0, t.K / 32};
+            const int tn = (t.N + kLBN - 1) / kLBN;
+            const int tmb = (M + kLBM - 1) / kLBM;
+            if (t.fmt == kFmtQ4)
+                split_gemm_kernel<kFmtQ4><<<tmb * tn, 256, 0, stream>>>(a, tn);
+            else
+                split_gemm_kernel<kFmtQ8><<<tmb * tn, 256, 0, stream>>>(a, tn);
+            e = hipGetLastError();
+        }
     }
-    return hipSuccess;
+    const hipError_t f = hipFreeAsync(ws, stream);
+    return e != hipSuccess ? e : f;
 }
 
 }  // namespace rtq

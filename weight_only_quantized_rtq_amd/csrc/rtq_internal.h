@@ -40,9 +40,9 @@ hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 bool grouped_ok(const ProjTask& task);
 
-// bf16 split-limb kernels (gemm_split.hip). Tasks must satisfy split_ok().
+// bf16 split-limb path (gemm_split.hip): every projection of the call, sharing M.
+// Tasks must satisfy split_ok(). Uses a stream-ordered workspace (hipMallocAsync).
 bool split_ok(const ProjTask& task);
-hipError_t launch_split_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
-hipError_t launch_split_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
+hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 
 }  // namespace rtq
