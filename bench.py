@@ -31,8 +31,15 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
-PEAK_FP32_MFMA_TFLOPS = 157.3
+PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix
+PEAK_BF16_MFMA_TFLOPS = 2516.6     # MI355X dense bf16 matrix
 WEIGHT_SETS = 16
+KERNELS = {  # main GEMM kernel of each (math, workload), as rocprofv3 names it
+    ("split", "m80"): "split_grouped_kernel<5>",
+    ("split", "m65536"): "split_gemm_kernel<1|2>",
+    ("fp32", "m80"): "grouped_stream_kernel<5>",
+    ("fp32", "m65536"): "gemm_kernel<1|2,2,2,4,4>",
+}
 
 
 def parse():
@@ -44,6 +51,10 @@ def parse():
     ap.add_argument("--warmup-large", type=int, default=2)
     ap.add_argument("--workload", choices=["m80", "m65536", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--math", choices=["split", "fp32"], default="split",
+                    help="GEMM arithmetic: exact bf16x3 split on the bf16 MFMA (default) or fp32 MFMA")
+    ap.add_argument("--compare-fp32", action="store_true",
+                    help="also time the fp32-MFMA path (few steps) and report it alongside")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -94,24 +105,77 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None):
 
 
 def time_workload(torch, rtq, sets, M, steps, warmup):
-    """Times exactly `steps` steps; also brackets every launch with events on
-    the launch stream to get the per-launch kernel duration."""
-    stream = torch.cuda.current_stream()
+    """Times exactly `steps` steps (wall clock between synchronizations) and,
+    through the library's event timing, the main GEMM kernel launches inside
+    them (HIP events recorded on the launch stream)."""
     for i in range(warmup):
         blocks, packed = sets[i % len(sets)]
         rtq.block_project(blocks, M, packed=packed)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
+    rtq.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
         blocks, packed = sets[i % len(sets)]
-        ev[i][0].record(stream)
         rtq.block_project(blocks, M, packed=packed)
-        ev[i][1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = np.array([a.elapsed_time(b) for a, b in ev])      # ms
-    return wall, per
+    kernel_ms, launches = rtq.timing_read()
+    rtq.timing_enable(False)
+    return wall, kernel_ms, launches
+
+
+def measure(torch, rtq, synth, workload, steps, warmup):
+    nb = synth.NUM_BLOCKS
+    if workload == "m80":
+        M = synth.M_GOLDEN
+        sets = build_sets(torch, rtq, synth, 4, M, WEIGHT_SETS, xs_per_block=True)
+    else:
+        M = synth.M_LARGE
+        sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False)
+    wb, fl = block_bytes_flops(M)
+    wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup)
+    del sets
+    torch.cuda.empty_cache()
+    flops_step, bytes_step = fl * nb, wb * nb
+    ms_step = wall / steps * 1e3
+    per_step = launches / steps
+    launch_ms = kernel_ms / launches
+    return {
+        "M": M, "ms_per_step": ms_step, "tflops": flops_step / (ms_step * 1e-3) / 1e12,
+        "weight_gbs": bytes_step / (ms_step * 1e-3) / 1e9,
+        "kernel_launches_per_step": per_step, "kernel_ms_per_launch": launch_ms,
+        "kernel_tflops": flops_step / per_step / (launch_ms * 1e-3) / 1e12,
+        "kernel_weight_gbs": bytes_step / per_step / (launch_ms * 1e-3) / 1e9,
+        "flops_per_step": flops_step, "weight_bytes_per_step": bytes_step, "steps": steps,
+    }
+
+
+def load_traffic(workload, math):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE /
+    WRITE_SIZE, copy-kernel calibrated), if recorded for the current sources."""
+    import weight_only_quantized_rtq_amd.traffic as tr
+    return tr.lookup(workload, math)
+
+
+def roofline(res, math, workload):
+    """Roofline of the main GEMM kernel: algorithmic flops per launch over the
+    kernel's average launch duration, against the peak of the matrix unit it
+    runs on (split: bf16 MFMA, three limb products per algorithmic multiply-add)."""
+    ach = res["kernel_tflops"]
+    if math == "split":
+        peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
+    else:
+        peak, issued = PEAK_FP32_MFMA_TFLOPS, 1
+    out = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+           "frac": round(ach / peak, 5), "traffic": load_traffic(workload, math),
+           "kernel": KERNELS[(math, workload)],
+           "kernel_ms_per_launch": round(res["kernel_ms_per_launch"], 6),
+           "launches_per_step": res["kernel_launches_per_step"],
+           "mfma_flops_per_algorithmic_flop": issued,
+           "matrix_unit_frac": round(ach * issued / peak, 5),
+           "weight_gbs_in_kernel": round(res["kernel_weight_gbs"], 2),
+           "weight_hbm_frac_in_kernel": round(res["kernel_weight_gbs"] / PEAK_HBM_GBS, 5)}
+    return out
 
 
 def cpu_baseline(cfg, M, seconds, rows=None):
@@ -163,73 +227,57 @@ def main():
     import weight_only_quantized_rtq_amd as rtq
     rtq.load_library()
     torch.cuda.init()
+    rtq.set_math(rtq.MATH_SPLIT_BF16 if args.math == "split" else rtq.MATH_FP32_MFMA)
     out = {}
-
-    wb, fl80 = block_bytes_flops(synth.M_GOLDEN)
-    nb = synth.NUM_BLOCKS
     if args.workload in ("m80", "both"):
-        sets = build_sets(torch, rtq, synth, 4, synth.M_GOLDEN, WEIGHT_SETS, xs_per_block=True)
-        wall, per = time_workload(torch, rtq, sets, synth.M_GOLDEN, args.steps, args.warmup)
-        ms_step = wall / args.steps * 1e3
-        flops_step = fl80 * nb
-        bytes_step = wb * nb
-        launch_ms = float(per.mean())
-        achieved_tf = flops_step / (launch_ms * 1e-3) / 1e12
-        out["m80"] = {
-            "ms_per_step": ms_step, "tflops": flops_step / (ms_step * 1e-3) / 1e12,
-            "weight_gbs": bytes_step / (ms_step * 1e-3) / 1e9,
-            "launch_ms": launch_ms, "launch_ms_min": float(per.min()),
-            "kernel_tflops": achieved_tf, "kernel_weight_gbs": bytes_step / (launch_ms * 1e-3) / 1e9,
-            "flops_per_step": flops_step, "weight_bytes_per_step": bytes_step,
-        }
-        del sets
-        torch.cuda.empty_cache()
-
+        out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup)
     if args.workload in ("m65536", "both"):
-        M = synth.M_LARGE
-        _, flL = block_bytes_flops(M)
-        sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False)
-        wall, per = time_workload(torch, rtq, sets, M, args.steps_large, args.warmup_large)
-        ms_step = wall / args.steps_large * 1e3
-        flops_step = flL * nb
-        out["m65536"] = {
-            "ms_per_step": ms_step, "tflops": flops_step / (ms_step * 1e-3) / 1e12,
-            "weight_gbs": wb * nb / (ms_step * 1e-3) / 1e9,
-            "step_event_ms": float(per.mean()), "flops_per_step": flops_step,
-            "fp32_mfma_frac": flops_step / (ms_step * 1e-3) / 1e12 / PEAK_FP32_MFMA_TFLOPS,
-        }
-        del sets
-        torch.cuda.empty_cache()
+        out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large)
+    fp32 = {}
+    if args.compare_fp32 and args.math == "split":
+        rtq.set_math(rtq.MATH_FP32_MFMA)
+        for wl in out:
+            r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1)
+            fp32[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
+                        "roofline": roofline(r, "fp32", wl)}
+        rtq.set_math(rtq.MATH_SPLIT_BF16)
 
-    prim = out.get("m80")
+    prim_name = "m80" if "m80" in out else "m65536"
+    prim = out[prim_name]
+    cfg = {"m80": "m80: 12 RT-J blocks (wq/wk/wv/wg/w1/w3 int4 g32, wo/w2 int8), M=80, 16 weight sets "
+                  "cycled (630 MB packed), per-block fp32 activations",
+           "m65536": "m65536: 12 RT-J blocks (mixed int4/int8), M=65536, one weight set, fp32 "
+                     "activations shared by the blocks"}[prim_name]
     line = {
         "metric": "dequant-GEMM TFLOP/s + weight-payload HBM GB/s (frac. of peak), M=80 and M=65536",
-        "value": round(prim["tflops"], 3) if prim else None,
+        "value": round(prim["tflops"], 3),
         "unit": "TFLOP/s",
-        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": round(prim["ms_per_step"], 5) if prim else None,
+        "n_gpus": 1,
+        "steps": prim["steps"],
+        "warmup": args.warmup if prim_name == "m80" else args.warmup_large,
+        "ms_per_step": round(prim["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f32", "data": "synthetic",
-        "config": {"workload": "m80: 12 RT-J blocks (wq/wk/wv/wg/w1/w3 int4 g32, wo/w2 int8), "
-                               "M=80, 16 weight sets cycled (630 MB packed)",
-                   "M": synth.M_GOLDEN, "n_blocks": nb, "weight_sets": WEIGHT_SETS, "recipe": "mixed int4/int8",
-                   "d_model": synth.D_MODEL, "d_ff": synth.D_FF},
+        "dtype": "bf16x3/f32" if args.math == "split" else "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg, "M": prim["M"], "n_blocks": synth.NUM_BLOCKS,
+                   "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": "mixed int4/int8",
+                   "d_model": synth.D_MODEL, "d_ff": synth.D_FF,
+                   "math": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation"
+                           if args.math == "split" else "fp32 MFMA on dequantized weights"},
+        "weight_gbs": round(prim["weight_gbs"], 2),
+        "weight_hbm_frac": round(prim["weight_gbs"] / PEAK_HBM_GBS, 5),
+        "roofline": roofline(prim, args.math, prim_name),
     }
-    if prim:
-        line["weight_gbs"] = round(prim["weight_gbs"], 2)
-        line["weight_hbm_frac"] = round(prim["weight_gbs"] / PEAK_HBM_GBS, 5)
-        line["roofline"] = {
-            "bound": "mfma", "achieved": round(prim["kernel_tflops"], 3), "peak": PEAK_FP32_MFMA_TFLOPS,
-            "unit": "TFLOP/s", "frac": round(prim["kernel_tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "grouped_stream_kernel (one launch per step)",
-            "launch_ms": round(prim["launch_ms"], 5),
-            "weight_gbs_in_kernel": round(prim["kernel_weight_gbs"], 2),
-        }
-    if "m65536" in out:
-        line["m65536"] = {k: (round(v, 5) if isinstance(v, float) else v) for k, v in out["m65536"].items()}
-        line["m65536"]["steps"] = args.steps_large
-    if not args.no_cpu_baseline and prim:
+    for wl, r in out.items():
+        if wl == prim_name:
+            continue
+        line[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
+                    "weight_gbs": round(r["weight_gbs"], 3), "steps": r["steps"],
+                    "frac_of_fp32_mfma_peak": round(r["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
+                    "roofline": roofline(r, args.math, wl)}
+    if fp32:
+        line["fp32_mfma_path"] = fp32
+    if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

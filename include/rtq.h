@@ -141,6 +141,16 @@ enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1 };
 rtq_status rtq_set_math(int32_t mode);
 int32_t rtq_get_math(void);
 
+/* Kernel timing (profiling aid). While enabled, every main GEMM kernel launch
+ * of the entry points above is bracketed by a pair of HIP events recorded on
+ * its stream (events are created on first use and kept for reuse). Enabling
+ * (or disabling) clears the record. rtq_timing_read waits for the recorded
+ * events, returns the summed elapsed time in ms and the number of timed
+ * launches, and clears the record. At most 16384 launches are recorded per
+ * window; later ones are not timed. */
+rtq_status rtq_timing_enable(int32_t on);
+rtq_status rtq_timing_read(double* total_ms, int64_t* launches);
+
 const char* rtq_status_string(rtq_status status);
 const char* rtq_last_error(void);   /* thread-local; valid until the next call on this thread */
 const char* rtq_version(void);

@@ -37,8 +37,8 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 
 # Every symbol include/rtq.h declares.
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_block_project", "rtq_dequant_q4", "rtq_dequant_q8",
-           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_set_math", "rtq_get_math", "rtq_status_string",
-           "rtq_last_error", "rtq_version")
+           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
+           "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 MATH_SPLIT_BF16, MATH_FP32_MFMA = 0, 1
 
@@ -85,6 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtq_set_math.restype = ctypes.c_int
     lib.rtq_get_math.argtypes = []
     lib.rtq_get_math.restype = i32
+    lib.rtq_timing_enable.argtypes = [i32]
+    lib.rtq_timing_enable.restype = ctypes.c_int
+    lib.rtq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.rtq_timing_read.restype = ctypes.c_int
     lib.rtq_status_string.argtypes = [ctypes.c_int]
     lib.rtq_status_string.restype = ctypes.c_char_p
     lib.rtq_last_error.argtypes = []
@@ -106,6 +110,18 @@ def set_math(mode: int) -> None:
 
 def get_math() -> int:
     return int(load_library().rtq_get_math())
+
+
+def timing_enable(on: bool = True) -> None:
+    """Bracket every main GEMM kernel launch with HIP events (rtq_timing_enable)."""
+    _check(load_library().rtq_timing_enable(1 if on else 0))
+
+
+def timing_read() -> tuple[float, int]:
+    """(summed kernel ms, number of timed launches) since the last enable/read."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(load_library().rtq_timing_read(ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def _check(status: int) -> None:

@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "rtq_internal.h"
 
@@ -88,8 +89,44 @@ rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, con
 
 }  // namespace
 
+// Kernel timing: when enabled, every main GEMM launch is bracketed by a pair of
+// HIP events recorded on its stream; rtq_timing_read sums their elapsed times.
+constexpr int kMaxTimed = 16384;
+struct Timing {
+    std::mutex mu;
+    bool on = false;
+    int n = 0;
+    int created = 0;
+    hipEvent_t begin[kMaxTimed];
+    hipEvent_t end[kMaxTimed];
+};
+Timing g_timing;
+
 namespace rtq {
 int math_mode() { return g_math.load(std::memory_order_relaxed); }
+
+int timing_begin(hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    if (!g_timing.on || g_timing.n >= kMaxTimed) return -1;
+    const int i = g_timing.n;
+    if (i >= g_timing.created) {
+        if (hipEventCreate(&g_timing.begin[i]) != hipSuccess) return -1;
+        if (hipEventCreate(&g_timing.end[i]) != hipSuccess) {
+            (void)hipEventDestroy(g_timing.begin[i]);
+            return -1;
+        }
+        g_timing.created = i + 1;
+    }
+    if (hipEventRecord(g_timing.begin[i], stream) != hipSuccess) return -1;
+    g_timing.n = i + 1;
+    return i;
+}
+
+void timing_end(int slot, hipStream_t stream) {
+    if (slot < 0) return;
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    (void)hipEventRecord(g_timing.end[slot], stream);
+}
 }  // namespace rtq
 
 extern "C" {
@@ -105,6 +142,32 @@ rtq_status rtq_set_math(int32_t mode) {
 int32_t rtq_get_math(void) { return g_math.load(std::memory_order_relaxed); }
 
 const char* rtq_version(void) { return "rtq 0.1.0 gfx950"; }
+
+rtq_status rtq_timing_enable(int32_t on) {
+    clear_error();
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    g_timing.on = on != 0;
+    g_timing.n = 0;
+    return RTQ_OK;
+}
+
+rtq_status rtq_timing_read(double* total_ms, int64_t* launches) {
+    clear_error();
+    if (!total_ms || !launches) return fail(RTQ_ERR_NULL, "rtq_timing_read: NULL output");
+    std::lock_guard<std::mutex> lock(g_timing.mu);
+    double sum = 0.0;
+    for (int i = 0; i < g_timing.n; ++i) {
+        hipError_t e = hipEventSynchronize(g_timing.end[i]);
+        float ms = 0.0f;
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_timing.begin[i], g_timing.end[i]);
+        if (e != hipSuccess) return fail(RTQ_ERR_HIP, "rtq_timing_read: %s", hipGetErrorString(e));
+        sum += ms;
+    }
+    *total_ms = sum;
+    *launches = g_timing.n;
+    g_timing.n = 0;
+    return RTQ_OK;
+}
 
 const char* rtq_last_error(void) { return g_err; }
 

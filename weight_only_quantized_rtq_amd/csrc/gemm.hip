@@ -492,6 +492,9 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupArgs g) {
         stream_tile<kFmtQ8, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
 }
 
+template <int FMT, bool SAFE>
+hipError_t launch_one_untimed(const TileArgs& a, hipStream_t stream);
+
 // Tile configurations: small M keeps all rows in one tile and splits N over
 // four waves; large M uses 128x128 tiles on a 2x2 wave grid.
 using Small = TileShape<1, 4, 5, 2>;
@@ -500,6 +503,14 @@ constexpr int kSmallMaxM = Small::BM;
 
 template <int FMT, bool SAFE>
 hipError_t launch_one(const TileArgs& a, hipStream_t stream) {
+    const int mark = timing_begin(stream);
+    const hipError_t e = launch_one_untimed<FMT, SAFE>(a, stream);
+    timing_end(mark, stream);
+    return e;
+}
+
+template <int FMT, bool SAFE>
+hipError_t launch_one_untimed(const TileArgs& a, hipStream_t stream) {
     if (a.M <= kSmallMaxM) {
         const int tn = (a.N + Small::BN - 1) / Small::BN;
         const int tm = (a.M + Small::BM - 1) / Small::BM;
@@ -584,6 +595,7 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
         }
         g.total_tiles = tiles;
         const int tm = static_cast<int>((M + 15) / 16);
+        const int mark = timing_begin(stream);
         switch (tm) {
             case 1: grouped_stream_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
             case 2: grouped_stream_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
@@ -591,6 +603,7 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
             case 4: grouped_stream_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
             default: grouped_stream_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
         }
+        timing_end(mark, stream);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -737,6 +737,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
                     red_blocks = red_blocks > nb ? red_blocks : nb;
                 }
             }
+            const int mark = timing_begin(stream);
             switch (tm_small) {
                 case 1: split_grouped_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
                 case 2: split_grouped_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
@@ -744,6 +745,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
                 case 4: split_grouped_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
                 default: split_grouped_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
             }
+            timing_end(mark, stream);
             e = hipGetLastError();
             if (e == hipSuccess && red.count) {
                 reduce_kernel<<<dim3(red_blocks, red.count), 256, 0, stream>>>(red);
@@ -758,10 +760,12 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             const SplitArgs a{wsb + inputs[img_of[i]].offset, t.payload, t.scale, t.y, M, t.N, t.K, RB, 0, t.K / 32};
             const int tn = (t.N + kLBN - 1) / kLBN;
             const int tmb = (M + kLBM - 1) / kLBM;
+            const int mark = timing_begin(stream);
             if (t.fmt == kFmtQ4)
                 split_gemm_kernel<kFmtQ4><<<tmb * tn, 256, 0, stream>>>(a, tn);
             else
                 split_gemm_kernel<kFmtQ8><<<tmb * tn, 256, 0, stream>>>(a, tn);
+            timing_end(mark, stream);
             e = hipGetLastError();
         }
     }

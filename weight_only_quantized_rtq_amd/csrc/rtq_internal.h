@@ -28,6 +28,10 @@ struct ProjTask {
     float* y;
 };
 
+// Kernel timing marks (rtq_timing_enable): returns a slot or -1 when off.
+int timing_begin(hipStream_t stream);
+void timing_end(int slot, hipStream_t stream);
+
 // Arithmetic of the GEMM kernels (process-wide, see rtq_set_math).
 enum Math : int { kMathSplitBf16 = 0, kMathFp32Mfma = 1 };
 int math_mode();
