@@ -166,8 +166,10 @@ def roofline(res, math, workload):
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
     else:
         peak, issued = PEAK_FP32_MFMA_TFLOPS, 1
+    tr = load_traffic(workload, math)
     out = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-           "frac": round(ach / peak, 5), "traffic": load_traffic(workload, math),
+           "frac": round(ach / peak, 5), "traffic": tr["bytes_per_launch"] if tr else None,
+           "traffic_detail": tr,
            "kernel": KERNELS[(math, workload)],
            "kernel_ms_per_launch": round(res["kernel_ms_per_launch"], 6),
            "launches_per_step": res["kernel_launches_per_step"],

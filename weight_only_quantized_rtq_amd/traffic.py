@@ -16,7 +16,13 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h"
 
 # (workload, math) -> record; filled from the counter runs described in the
 # profiles folder.
-RECORDS: dict = {}
+RECORDS: dict = {
+    # split_grouped_kernel<5>, 12 blocks at M = 80: 33 dispatches per counter run
+    ("m80", "split"): {"fetch_kib": 61503.697, "write_kib": 34660.256,
+                       "fetch_factor": 1.99987, "write_factor": 1.0,
+                       "algorithmic_bytes": 80658432,
+                       "sources_sha256": "2ec556d260c2a787dac9ddf17372f2599f19f2d457a6729f3c8146311c7d030e"},
+}
 
 
 def sources_sha256() -> str:
@@ -36,3 +42,63 @@ def lookup(workload: str, math: str):
     return {"bytes_per_launch": round(fetch + write), "fetch_bytes": round(fetch),
             "write_bytes": round(write), "algorithmic_bytes": rec["algorithmic_bytes"],
             "ratio": round((fetch + write) / rec["algorithmic_bytes"], 4)}
+
+
+# ---------------------------------------------------------------------------
+# Command line: the calibration copy and the summary of counter runs.
+#   python -m weight_only_quantized_rtq_amd.traffic copy [--mib 256] [--reps 4]
+#       runs a plain device-to-device copy-like kernel (torch.neg) of known size;
+#   python -m weight_only_quantized_rtq_amd.traffic summarize FETCH_CSV WRITE_CSV
+#       COPY_FETCH_CSV COPY_WRITE_CSV KERNEL_REGEX ALGORITHMIC_BYTES [MIB]
+#       prints the per-launch averages and the calibrated record.
+# ---------------------------------------------------------------------------
+def _copy(mib: int, reps: int) -> None:
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    print(f"copy: {reps} x {mib} MiB read + {mib} MiB written", flush=True)
+
+
+def _per_dispatch(csv_path: str, regex: str, counter: str):
+    import csv
+    import re
+    pat = re.compile(regex)
+    vals = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"]):
+                vals[r["Dispatch_Id"]] = vals.get(r["Dispatch_Id"], 0.0) + float(r["Counter_Value"])
+    if not vals:
+        raise SystemExit(f"no {counter} rows for /{regex}/ in {csv_path}")
+    return sum(vals.values()) / len(vals), len(vals)
+
+
+def _summarize(fetch_csv, write_csv, cfetch_csv, cwrite_csv, regex, algo_bytes, mib=256):
+    fetch, nf = _per_dispatch(fetch_csv, regex, "FETCH_SIZE")
+    write, nw = _per_dispatch(write_csv, regex, "WRITE_SIZE")
+    cf, _ = _per_dispatch(cfetch_csv, r"neg|elementwise", "FETCH_SIZE")
+    cw, _ = _per_dispatch(cwrite_csv, r"neg|elementwise", "WRITE_SIZE")
+    known = mib * 1024 * 1024
+    rec = {"fetch_kib": round(fetch, 3), "write_kib": round(write, 3),
+           "fetch_factor": round(known / (cf * 1024), 5), "write_factor": round(known / (cw * 1024), 5),
+           "algorithmic_bytes": int(algo_bytes), "dispatches": [nf, nw],
+           "copy_fetch_kib": round(cf, 1), "copy_write_kib": round(cw, 1),
+           "sources_sha256": sources_sha256()}
+    print(rec)
+
+
+if __name__ == "__main__":
+    import sys
+    if len(sys.argv) >= 2 and sys.argv[1] == "copy":
+        mib = int(sys.argv[sys.argv.index("--mib") + 1]) if "--mib" in sys.argv else 256
+        reps = int(sys.argv[sys.argv.index("--reps") + 1]) if "--reps" in sys.argv else 4
+        _copy(mib, reps)
+    elif len(sys.argv) >= 8 and sys.argv[1] == "summarize":
+        _summarize(*sys.argv[2:7], int(sys.argv[7]), *(int(v) for v in sys.argv[8:9]))
+    else:
+        raise SystemExit(__doc__)
