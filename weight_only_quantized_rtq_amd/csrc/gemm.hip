@@ -474,8 +474,7 @@ template <int TM>
 __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupArgs g) {
     __shared__ __attribute__((aligned(16))) float red[4 * TM * kStreamTN * 4 * 64];
     const int w = blockIdx.x;
-    int i = 0;
-    while (i + 1 < g.count && g.tile_begin[i + 1] <= w) ++i;
+    const int i = segment_of(g.tile_begin, g.count, w);
     const int xi = g.x_idx[i];
     const int N = g.n[i];
     const int K = g.xk[xi];

@@ -131,8 +131,7 @@ static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB
 // and the group sum of a row is two shuffles in a fixed order.
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     const int b = blockIdx.x;
-    int i = 0;
-    while (i + 1 < p.count && p.block_begin[i + 1] <= b) ++i;
+    const int i = segment_of(p.block_begin, p.count, b);
     const int M = p.M[i], K = p.K[i], RB = p.RB[i];
     const int G = K / 32;
     const int64_t t = static_cast<int64_t>(b - p.block_begin[i]) * 256 + threadIdx.x;
@@ -527,7 +526,9 @@ struct SplitGroupArgs {
     int M;
     int RB;
     int pad;
-    const unsigned char* img[kMaxSplitGrouped];
+    const unsigned char* ws;                // workspace holding the limb images
+    int tile_begin[kMaxSplitGrouped];       // first workgroup of each projection
+    uint32_t img_off[kMaxSplitGrouped];     // byte offset of the projection's limb image in ws
     const void* payload[kMaxSplitGrouped];
     const void* scale[kMaxSplitGrouped];
     float* y[kMaxSplitGrouped];
@@ -541,6 +542,7 @@ static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within
 // Small M: column tiles of 4 waves x 4 x 16 = 256 and K chunks of at most 16
 // groups (512 of K), so every workgroup does about the same work.
 constexpr int kSmallBN = 256;
+constexpr int kMaxGroupedTiles = 1 << 30;   // workgroups of one grouped launch
 constexpr int kSmallPDW = 2;        // x stages and weights (streamed from HBM) two steps ahead
 constexpr int kChunkGroups = 16;
 __host__ __device__ inline int split_chunks(int K) {
@@ -554,13 +556,8 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     // Find this workgroup's projection: tiles are numbered projection by
     // projection, (column block, K chunk) within one.
     const int w = blockIdx.x;
-    int i = 0, begin = 0;
-    for (;;) {
-        const int tiles = (g.n[i] + kSmallBN - 1) / kSmallBN * g.ks[i];
-        if (w < begin + tiles || i + 1 == g.count) break;
-        begin += tiles;
-        ++i;
-    }
+    const int i = segment_of(g.tile_begin, g.count, w);
+    const int begin = g.tile_begin[i];
     const int K = g.k[i];
     const int G = K / 32;
     const int ks = g.ks[i];
@@ -568,7 +565,7 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     const int cb = local / ks, kc = local % ks;
     const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
     float* y = g.y[i] + static_cast<int64_t>(ks > 1 ? kc : 0) * g.M * g.n[i];
-    const SplitArgs a{g.img[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo};
+    const SplitArgs a{g.ws + g.img_off[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo};
     const int rot = cb % (g_hi - g_lo);
     if (g.fmt[i] == kFmtQ4)
         split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
@@ -654,25 +651,33 @@ bool split_ok(const ProjTask& t) {
 // a stream-ordered workspace, run the GEMMs, release the workspace.
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream_t stream) {
     const int M = static_cast<int>(M64);
-    const bool small = M <= 80;
     const int tm_small = (M + 15) / 16;
-    const int RB = small ? tm_small : ((M + kLBM - 1) / kLBM) * (kLBM / 16);
-
-    // Distinct inputs (pointer, K).
+    // The grouped small-M launch addresses the limb images by 32-bit offsets;
+    // a call whose images would not fit (enormous K) takes the tiled path.
+    bool small = M <= 80;
+    int RB = 0;
     Input inputs[8 * 64];
     int img_of[8 * 64];
     int n_in = 0;
     int64_t ws_bytes = 0;
-    for (int i = 0; i < count; ++i) {
-        int found = -1;
-        for (int j = 0; j < n_in; ++j)
-            if (inputs[j].x == tasks[i].x && inputs[j].K == tasks[i].K) found = j;
-        if (found < 0) {
-            found = n_in++;
-            inputs[found] = Input{tasks[i].x, tasks[i].K, ws_bytes};
-            ws_bytes += (image_bytes(tasks[i].K / 32, RB) + 255) / 256 * 256;
+    for (;;) {
+        RB = small ? tm_small : ((M + kLBM - 1) / kLBM) * (kLBM / 16);
+        // Distinct inputs (pointer, K).
+        n_in = 0;
+        ws_bytes = 0;
+        for (int i = 0; i < count; ++i) {
+            int found = -1;
+            for (int j = 0; j < n_in; ++j)
+                if (inputs[j].x == tasks[i].x && inputs[j].K == tasks[i].K) found = j;
+            if (found < 0) {
+                found = n_in++;
+                inputs[found] = Input{tasks[i].x, tasks[i].K, ws_bytes};
+                ws_bytes += (image_bytes(tasks[i].K / 32, RB) + 255) / 256 * 256;
+            }
+            img_of[i] = found;
         }
-        img_of[i] = found;
+        if (!small || ws_bytes <= int64_t(UINT32_MAX)) break;
+        small = false;
     }
     int64_t part_off[8 * 64];
     for (int i = 0; i < count; ++i) {
@@ -711,18 +716,22 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             SplitGroupArgs g{};
             g.M = M;
             g.RB = RB;
+            g.ws = wsb;
             int tiles = 0;
-            while (done < count && g.count < kMaxSplitGrouped) {
+            while (done < count && g.count < kMaxSplitGrouped &&
+                   tiles + (tasks[order[done]].N + kSmallBN - 1) / kSmallBN * split_chunks(tasks[order[done]].K) <=
+                       kMaxGroupedTiles) {
                 const int ti = order[done++];
                 const ProjTask& t = tasks[ti];
                 const int c = g.count++;
                 const int ks = split_chunks(t.K);
-                g.img[c] = wsb + inputs[img_of[ti]].offset;
+                g.img_off[c] = static_cast<uint32_t>(inputs[img_of[ti]].offset);
                 g.payload[c] = t.payload;
                 g.scale[c] = t.scale;
                 g.y[c] = ks > 1 ? reinterpret_cast<float*>(wsb + part_off[ti]) : t.y;
                 g.n[c] = t.N;
                 g.k[c] = t.K;
+                g.tile_begin[c] = tiles;
                 g.fmt[c] = static_cast<uint8_t>(t.fmt);
                 g.ks[c] = static_cast<uint8_t>(ks);
                 tiles += (t.N + kSmallBN - 1) / kSmallBN * ks;

@@ -50,6 +50,25 @@ __device__ __forceinline__ uint32_t double_to_half_bits(double d) {
     return sign | h;
 }
 
+// Segment lookup for kernels whose workgroups are numbered segment by segment
+// (projection by projection, input by input): segment j starts at item
+// begin[j] (begin[0] = 0, nondecreasing) and the launch has `count` segments.
+// Returns the segment that holds item w: the number of segments j >= 1 that
+// start at or before w. The sum is unrolled over the slots and branch-free, so
+// the argument loads have fixed offsets and none waits for another. The result
+// is then passed through an empty asm statement, which makes it an opaque
+// value: descriptor loads indexed by it are addressed as base plus the
+// sign-extended index.
+template <int SLOTS, class T>
+__device__ __forceinline__ int segment_of(const T (&begin)[SLOTS], int count, int w) {
+    int i = 0;
+#pragma unroll
+    for (int j = 1; j < SLOTS; ++j) i += static_cast<int>(j < count) & static_cast<int>(static_cast<int>(begin[j]) <= w);
+    i = __builtin_amdgcn_readfirstlane(i);
+    asm volatile("" : "+s"(i));
+    return i;
+}
+
 // Low nibble = even index.
 __device__ __forceinline__ uint32_t nibble(uint32_t word, int idx) {
     return (word >> (4 * idx)) & 0xFu;
