@@ -187,22 +187,27 @@ struct SplitArgs {
 
 constexpr int kStages = 2;        // LDS ring depth (loads run one group ahead)
 constexpr int kRing = 8;          // group sums kept for the deferred min term
-constexpr int kXSlot = 128;       // floats per group-sum slot (>= BM; waves 0 and 1 copy 64 rows each)
+constexpr int kChunk = 2;         // steps per weight chunk when the weights stream through LDS
 
-// LDS map of a workgroup: x stages, group-sum ring, dummy DMA target and, when
-// the weights stream through LDS (PDW > 0), a per-wave weight ring of PDW + 1
-// slots of TN x (256 B codes + 256 B pairs / second code word).
+// LDS map of a workgroup: x stages, group-sum ring and, when the weights
+// stream through LDS (PDW > 0), two weight-chunk slots per wave. A chunk holds
+// the wave's TN*16 rows for kChunk steps: int4 as 16-byte code records (one
+// per row and group) plus 4-byte (scale, min) records, int8 as two 16-byte
+// halves per row and group (TN * 1024 bytes either way).
 template <int BM, int TN = 1, int PDW = 0>
 struct Lds {
     static constexpr int NSTAGE = PDW > 0 ? PDW + 1 : kStages;    // x stages
     static constexpr int STAGE = (BM / 16) * 3072;
     static constexpr int XRING = NSTAGE * STAGE;
-    static constexpr int DUMMY = XRING + kRing * kXSlot * 4;
-    static constexpr int WSLOT = 4 * TN * 512;                    // one step, all four waves
-    static constexpr int WRING = DUMMY + 1024;
-    static constexpr int TOTAL = WRING + (PDW > 0 ? (PDW + 1) * WSLOT : 0);
+    // Group-sum slot: waves 0 and 2 copy rows 0..63, waves 1 and 3 rows
+    // XSLOT-64 .. XSLOT-1 (the same rows twice, identical bytes).
+    static constexpr int XSLOT = BM <= 96 ? 96 : 128;
+    static constexpr int WRING = XRING + kRing * XSLOT * 4;
+    static constexpr int WCHUNK = TN * 1024;
+    static constexpr int TOTAL = WRING + (PDW > 0 ? 2 * 4 * WCHUNK : 0);
     static constexpr int COPIES = (BM / 16) * 3;                   // 1 KB copies per stage
     static constexpr int PER_WAVE = (COPIES + 3) / 4;
+    static_assert(BM <= XSLOT, "group-sum slot holds every row of the tile");
 };
 
 // Wait until at most N vector-memory operations of this wave are in flight.
@@ -253,7 +258,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 
     // ---- async stage copies: 1 KB per wave instruction, all waves issue the same count ----
     const unsigned char* xsum = a.img + image_plane_bytes(G, RB);
-    const int xrow = min(m0 + (wave & 1) * 64 + lane, RB * 16 - 1);   // clamped: rows past BM are never read
+    const int xrow = min(m0 + (wave & 1) * (L::XSLOT - 64) + lane, RB * 16 - 1);   // clamped: rows past BM are never read
     auto group_of = [&](int i) { const int g = rot + i; return a.g_lo + (g >= GS ? g - GS : g); };
     auto stage_copy = [&](int i) {
         const int g = group_of(i);
@@ -261,14 +266,13 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         unsigned char* dst = smem + (i % L::NSTAGE) * L::STAGE;
 #pragma unroll
         for (int j = 0; j < L::PER_WAVE; ++j) {
-            const int cpy = wave * L::PER_WAVE + j;
-            if (cpy < L::COPIES)
-                dma16(src + cpy * 1024 + lane * 16, dst + cpy * 1024);
-            else
-                dma16(src + lane * 16, smem + L::DUMMY);               // keeps the per-wave count uniform
+            // Every wave issues the same count; padding copies repeat the last
+            // copy exactly (same source, same destination, same bytes).
+            const int c = wave * L::PER_WAVE + j;
+            const int cpy = c < L::COPIES ? c : L::COPIES - 1;
+            dma16(src + cpy * 1024 + lane * 16, dst + cpy * 1024);
         }
-        // group sums: waves 0 and 1 copy 64 rows each, waves 2 and 3 a dummy
-        unsigned char* xdst = wave < 2 ? smem + L::XRING + ((i % kRing) * kXSlot + wave * 64) * 4 : smem + L::DUMMY;
+        unsigned char* xdst = smem + L::XRING + ((i % kRing) * L::XSLOT + (wave & 1) * (L::XSLOT - 64)) * 4;
         dma4(xsum + (static_cast<int64_t>(g) * RB * 16 + xrow) * 4, xdst);
     };
 
@@ -287,8 +291,6 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             prow[tn] = nullptr;
         }
     }
-    constexpr int NW = FMT == kFmtQ4 ? 2 * TN : TN;                  // weight loads per group
-    constexpr int NVM = L::PER_WAVE + 1 + NW;                         // vector-memory ops per group
     auto w_load = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
         const int g = group_of(i);
 #pragma unroll
@@ -306,39 +308,71 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     };
 
-    // Weight ring (PDW > 0): slot s of this wave holds, per column tile, 64 lanes
-    // x 4 bytes of codes (int4: the lane's 8 codes; int8: its first 4 codes) and
-    // 64 x 4 bytes of the pair (int4) or the lane's last 4 codes (int8).
-    unsigned char* wbase = smem + L::WRING + wave * TN * 512;
-    auto w_issue = [&](int i) {
+    // Weight chunks (PDW > 0): chunk c holds the weights of steps kChunk*c and
+    // kChunk*c + 1 for this wave's TN*16 rows, in slot c & 1. Each lane copies
+    // whole 16-byte records (int4: the 32 codes of one row and group; int8:
+    // half of them), so one instruction covers 64 (row, group) records.
+    // Record order is swizzled so that the per-step reads are bank-spread:
+    //   int4 codes: record row*2 + (h ^ (row>>3 & 1)), pairs: row*2 + h (4 B);
+    //   int8: record row*4 + ((2h + half) ^ (row>>2 & 3)),
+    // with h the step within the chunk and row = tn*16 + li.
+    unsigned char* wring = smem + L::WRING + wave * L::WCHUNK;
+    const int wrow0 = n0 + wn * TN * 16;
+    auto w_chunk_issue = [&](int c) {
         if constexpr (PDW > 0) {
-            const int g = group_of(i);
-            unsigned char* slot = wbase + (i % (PDW + 1)) * L::WSLOT;
+            unsigned char* slot = wring + (c & 1) * 4 * L::WCHUNK;
+            const int s0 = kChunk * c;
+            if constexpr (FMT == kFmtQ4) {
+                const unsigned char* payload = static_cast<const unsigned char*>(a.payload);
+                const uint32_t* pairs = static_cast<const uint32_t*>(a.scale);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                if constexpr (FMT == kFmtQ4) {
-                    dma4(wrow[tn] + g * 16, slot + tn * 512);
-                    dma4(prow[tn] + g, slot + tn * 512 + 256);
-                } else {
-                    dma4(wrow[tn] + g * 32, slot + tn * 512);
-                    dma4(wrow[tn] + g * 32 + 4, slot + tn * 512 + 256);
+                for (int j = 0; j < TN / 2; ++j) {
+                    const int rec = j * 64 + lane;
+                    const int row = rec >> 1;
+                    const int h = (rec & 1) ^ ((row >> 3) & 1);
+                    const int col = min(wrow0 + row, N - 1);
+                    const int g = group_of(min(s0 + h, GS - 1));
+                    dma16(payload + static_cast<int64_t>(col) * (K / 2) + g * 16, slot + j * 1024);
+                }
+#pragma unroll
+                for (int j = 0; j < TN / 2; ++j) {
+                    const int rec = j * 64 + lane;
+                    const int row = rec >> 1;
+                    const int h = rec & 1;
+                    const int col = min(wrow0 + row, N - 1);
+                    const int g = group_of(min(s0 + h, GS - 1));
+                    dma4(pairs + static_cast<int64_t>(col) * G + g, slot + TN * 512 + j * 256);
+                }
+            } else {
+                const unsigned char* payload = static_cast<const unsigned char*>(a.payload);
+#pragma unroll
+                for (int j = 0; j < TN; ++j) {
+                    const int rec = j * 64 + lane;
+                    const int row = rec >> 2;
+                    const int sub = (rec & 3) ^ ((row >> 2) & 3);
+                    const int col = min(wrow0 + row, N - 1);
+                    const int g = group_of(min(s0 + (sub >> 1), GS - 1));
+                    dma16(payload + static_cast<int64_t>(col) * K + g * 32 + (sub & 1) * 16, slot + j * 1024);
                 }
             }
         }
     };
     auto w_read = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
-        const unsigned char* slot = wbase + (i % (PDW + 1)) * L::WSLOT;
+        const unsigned char* slot = wring + ((i / kChunk) & 1) * 4 * L::WCHUNK;
+        const int h = i % kChunk;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
-            const uint32_t w0 = reinterpret_cast<const uint32_t*>(slot + tn * 512)[lane];
-            const uint32_t w1 = reinterpret_cast<const uint32_t*>(slot + tn * 512 + 256)[lane];
+            const int row = tn * 16 + li;
             if constexpr (FMT == kFmtQ4) {
-                wq[tn][0] = w0;
+                const int rec = row * 2 + (h ^ ((row >> 3) & 1));
+                wq[tn][0] = *reinterpret_cast<const uint32_t*>(slot + rec * 16 + 4 * lc);
                 wq[tn][1] = 0;
-                wp[tn] = w1;
+                wp[tn] = *reinterpret_cast<const uint32_t*>(slot + TN * 512 + (row * 2 + h) * 4);
             } else {
-                wq[tn][0] = w0;
-                wq[tn][1] = w1;
+                const int rec = row * 4 + ((2 * h + (lc >> 1)) ^ ((row >> 2) & 3));
+                const uint2 v = *reinterpret_cast<const uint2*>(slot + rec * 16 + 8 * (lc & 1));
+                wq[tn][0] = v.x;
+                wq[tn][1] = v.y;
                 wp[tn] = 0;
             }
         }
@@ -403,7 +437,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             if ((i & 3) != 3 && i != GS - 1) return;
             const int ic = (i & ~3) + lc;                 // this lane group's step
             const bool live = ic <= i;
-            const float* ring = reinterpret_cast<const float*>(smem + L::XRING) + (ic % kRing) * kXSlot;
+            const float* ring = reinterpret_cast<const float*>(smem + L::XRING) + (ic % kRing) * L::XSLOT;
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
                 const float xv = live ? ring[wm * TM * 16 + tm * 16 + li] : 0.0f;
@@ -421,30 +455,31 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     //      weight ring). A stage or ring slot is refilled only after the barrier
     //      that follows every wave's last read of it. ----
     uint32_t wq[TN][2], wp[TN], cq[TN][2], cp[TN];
-    // With PDW > 0, step j's x stage and weights go out as one batch of NB
-    // vector-memory ops, PDW steps ahead: batches 0..PDW-1 in the prologue, batch
-    // i+PDW in iteration i.
-    constexpr int NB = L::PER_WAVE + 1 + 2 * TN;
+    // With PDW > 0 (PDW == 2): the x stage of step j goes out in iteration
+    // j - 2 (steps 0 and 1 in the prologue) as NX vector-memory ops, and weight
+    // chunk c in iteration kChunk*(c - 1) (chunk 0 in the prologue), just
+    // before that iteration's x stage, as NWC ops. So what step i needs was
+    // issued no later than its x stage, and the only ops issued after that
+    // stage are those of iteration i - 1: the x stage of step i + 1 and, for
+    // odd i, weight chunk (i + 1) / 2, both only when i + 1 < GS.
+    constexpr int NX = L::PER_WAVE + 1;
+    constexpr int NWC = TN;
+    static_assert(PDW == 0 || (PDW == 2 && kChunk == 2 && TN % 2 == 0), "weight-chunk schedule");
     if constexpr (PDW == 0) {
         stage_copy(0);
         w_load(0, wq, wp);
     } else {
-#pragma unroll
-        for (int j = 0; j < PDW; ++j)
-            if (j < GS) {
-                stage_copy(j);
-                w_issue(j);
-            }
+        w_chunk_issue(0);
+        stage_copy(0);
+        if (1 < GS) stage_copy(1);
     }
     for (int i = 0; i < GS; ++i) {
         if constexpr (PDW == 0) {
             wait_vm<0>();                                 // this wave's part of step i has landed
         } else {
-            // Batches issued after step i's: steps i+1 .. min(i+PDW-1, GS-1).
-            const int later = min(PDW - 1, GS - 1 - i);
-            if (later >= 2 && PDW >= 3) wait_vm<(PDW >= 3 ? 2 : 0) * NB>();
-            else if (later >= 1) wait_vm<NB>();
-            else wait_vm<0>();
+            if (i + 1 >= GS) wait_vm<0>();
+            else if (i & 1) wait_vm<NX + NWC>();
+            else wait_vm<NX>();
         }
         // Barrier without a memory fence: the LDS data of step i came in by DMA
         // and is complete after the wait above (in every wave, after the barrier);
@@ -464,10 +499,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             }
         } else {
             w_read(i, cq, cp);
-            if (i + PDW < GS) {
-                stage_copy(i + PDW);
-                w_issue(i + PDW);
-            }
+            if (i % kChunk == 0 && i + kChunk < GS) w_chunk_issue(i / kChunk + 1);
+            if (i + PDW < GS) stage_copy(i + PDW);
         }
         __builtin_amdgcn_sched_barrier(0);
         compute(i, cq, cp);
