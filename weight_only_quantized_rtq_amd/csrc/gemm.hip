@@ -464,7 +464,8 @@ struct GroupArgs {
     const void* scale[kMaxGrouped];
     float* y[kMaxGrouped];
     int n[kMaxGrouped];
-    int tile_begin[kMaxGrouped];
+    int tile_begin[seg_begin_slots(kMaxGrouped)];
+    int tile_coarse[seg_coarse_slots(kMaxGrouped)];
     uint8_t x_idx[kMaxGrouped];
     uint8_t fmt[kMaxGrouped];
 };
@@ -474,7 +475,7 @@ template <int TM>
 __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupArgs g) {
     __shared__ __attribute__((aligned(16))) float red[4 * TM * kStreamTN * 4 * 64];
     const int w = blockIdx.x;
-    const int i = segment_of(g.tile_begin, g.count, w);
+    const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
     const int xi = g.x_idx[i];
     const int N = g.n[i];
     const int K = g.xk[xi];
@@ -593,6 +594,7 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
             ++done;
         }
         g.total_tiles = tiles;
+        seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
         const int tm = static_cast<int>((M + 15) / 16);
         const int mark = timing_begin(stream);
         switch (tm) {

@@ -122,7 +122,8 @@ struct PrepArgs {
     int M[kMaxImages];
     int K[kMaxImages];
     int RB[kMaxImages];
-    int block_begin[kMaxImages + 1];    // 256-thread blocks per image, prefix
+    int block_begin[seg_begin_slots(kMaxImages + 1)];    // 256-thread blocks per image, prefix
+    int block_coarse[seg_coarse_slots(kMaxImages + 1)];
 };
 static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
@@ -131,7 +132,7 @@ static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB
 // and the group sum of a row is two shuffles in a fixed order.
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     const int b = blockIdx.x;
-    const int i = segment_of(p.block_begin, p.count, b);
+    const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
     const int M = p.M[i], K = p.K[i], RB = p.RB[i];
     const int G = K / 32;
     const int64_t t = static_cast<int64_t>(b - p.block_begin[i]) * 256 + threadIdx.x;
@@ -560,15 +561,15 @@ struct SplitGroupArgs {
     int RB;
     int pad;
     const unsigned char* ws;                // workspace holding the limb images
-    int tile_begin[kMaxSplitGrouped];       // first workgroup of each projection
+    int tile_begin[seg_begin_slots(kMaxSplitGrouped)];   // first workgroup of each projection
+    int tile_coarse[seg_coarse_slots(kMaxSplitGrouped)];
     uint32_t img_off[kMaxSplitGrouped];     // byte offset of the projection's limb image in ws
     const void* payload[kMaxSplitGrouped];
     const void* scale[kMaxSplitGrouped];
     float* y[kMaxSplitGrouped];
     int n[kMaxSplitGrouped];
     int k[kMaxSplitGrouped];
-    uint8_t fmt[kMaxSplitGrouped];
-    uint8_t ks[kMaxSplitGrouped];       // K chunks (> 1: y[] is the partial buffer [ks][M][N])
+    uint8_t fmt[kMaxSplitGrouped];      // y[] is the partial buffer [ks][M][N] when K spans ks > 1 chunks
 };
 static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
@@ -589,11 +590,11 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     // Find this workgroup's projection: tiles are numbered projection by
     // projection, (column block, K chunk) within one.
     const int w = blockIdx.x;
-    const int i = segment_of(g.tile_begin, g.count, w);
+    const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
     const int begin = g.tile_begin[i];
     const int K = g.k[i];
     const int G = K / 32;
-    const int ks = g.ks[i];
+    const int ks = split_chunks(K);
     const int local = w - begin;
     const int cb = local / ks, kc = local % ks;
     const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
@@ -655,6 +656,7 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
             blocks += static_cast<int>((threads + 255) / 256);
         }
         p.block_begin[p.count] = blocks;
+        seg_fill_coarse(p.block_begin, p.block_coarse, p.count);
         prep_kernel<<<blocks, 256, 0, stream>>>(p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -766,7 +768,6 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
                 g.k[c] = t.K;
                 g.tile_begin[c] = tiles;
                 g.fmt[c] = static_cast<uint8_t>(t.fmt);
-                g.ks[c] = static_cast<uint8_t>(ks);
                 tiles += (t.N + kSmallBN - 1) / kSmallBN * ks;
                 if (ks > 1) {
                     const int r = red.count++;
@@ -779,6 +780,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
                     red_blocks = red_blocks > nb ? red_blocks : nb;
                 }
             }
+            seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
             const int mark = timing_begin(stream);
             switch (tm_small) {
                 case 1: split_grouped_kernel<1><<<tiles, 256, 0, stream>>>(g); break;

@@ -52,21 +52,44 @@ __device__ __forceinline__ uint32_t double_to_half_bits(double d) {
 
 // Segment lookup for kernels whose workgroups are numbered segment by segment
 // (projection by projection, input by input): segment j starts at item
-// begin[j] (begin[0] = 0, nondecreasing) and the launch has `count` segments.
-// Returns the segment that holds item w: the number of segments j >= 1 that
-// start at or before w. The sum is unrolled over the slots and branch-free, so
-// the argument loads have fixed offsets and none waits for another. The result
-// is then passed through an empty asm statement, which makes it an opaque
-// value: descriptor loads indexed by it are addressed as base plus the
+// begin[j] (begin[0] = 0, nondecreasing) and the launch has `count` segments;
+// coarse[c] = begin[c * kSegStride] for the slots below count. Returns the
+// segment that holds item w: the coarse table picks the run of kSegStride
+// slots, then that run picks the segment. Both sums are unrolled and
+// branch-free, so each level is one round of independent argument loads; the
+// level results pass through an empty asm statement, which makes them opaque
+// values, so the loads that depend on them are addressed as base plus a
 // sign-extended index.
-template <int SLOTS, class T>
-__device__ __forceinline__ int segment_of(const T (&begin)[SLOTS], int count, int w) {
-    int i = 0;
+constexpr int kSegStride = 8;
+__host__ __device__ constexpr int seg_coarse_slots(int slots) { return (slots + kSegStride - 1) / kSegStride; }
+__host__ __device__ constexpr int seg_begin_slots(int slots) { return slots + kSegStride - 1; }
+
+// begin[] carries kSegStride - 1 slots of padding past the last segment slot,
+// so the second level reads one whole run without clamping.
+template <int SLOTS, int NC, class T>
+__device__ __forceinline__ int segment_of(const T (&begin)[SLOTS], const T (&coarse)[NC], int count, int w) {
+    static_assert(NC == seg_coarse_slots(SLOTS - (kSegStride - 1)), "coarse table size");
+    int c = 0;
 #pragma unroll
-    for (int j = 1; j < SLOTS; ++j) i += static_cast<int>(j < count) & static_cast<int>(static_cast<int>(begin[j]) <= w);
+    for (int j = 1; j < NC; ++j)
+        c += static_cast<int>(j * kSegStride < count) & static_cast<int>(static_cast<int>(coarse[j]) <= w);
+    c = __builtin_amdgcn_readfirstlane(c);
+    asm volatile("" : "+s"(c));
+    const int base = c * kSegStride;
+    int i = base;
+    const T* run = begin + base;
+#pragma unroll
+    for (int j = 1; j < kSegStride; ++j)
+        i += static_cast<int>(base + j < count) & static_cast<int>(static_cast<int>(run[j]) <= w);
     i = __builtin_amdgcn_readfirstlane(i);
     asm volatile("" : "+s"(i));
     return i;
+}
+
+// Host side: fills the coarse table of segment_of from begin[0 .. count).
+template <int SLOTS, int NC, class T>
+inline void seg_fill_coarse(const T (&begin)[SLOTS], T (&coarse)[NC], int count) {
+    for (int c = 0; c < NC; ++c) coarse[c] = c * kSegStride < count ? begin[c * kSegStride] : begin[0];
 }
 
 // Low nibble = even index.
