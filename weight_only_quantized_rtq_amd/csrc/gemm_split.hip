@@ -247,7 +247,9 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     static_assert(PDW <= 3, "prefetch depth");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    // The wave index is uniform: made explicit so that everything derived
+    // from it (LDS destinations, copy indices) stays in scalar registers.
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave / WN;
     const int wn = wave % WN;
     const int li = lane & 15;
@@ -257,9 +259,11 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     const int GS = a.g_cnt;                               // steps: groups of this K chunk
     const int rb0 = m0 / 16;
 
-    // ---- async stage copies: 1 KB per wave instruction, all waves issue the same count ----
+    // ---- async stage copies: 1 KB per wave instruction, all waves issue the same count.
+    //      Every copy is a uniform base plus a fixed per-lane byte offset. ----
     const unsigned char* xsum = a.img + image_plane_bytes(G, RB);
-    const int xrow = min(m0 + (wave & 1) * (L::XSLOT - 64) + lane, RB * 16 - 1);   // clamped: rows past BM are never read
+    const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
+    const uint32_t xrow4 = static_cast<uint32_t>(min(m0 + (wave & 1) * (L::XSLOT - 64) + lane, RB * 16 - 1)) * 4u;
     auto group_of = [&](int i) { const int g = rot + i; return a.g_lo + (g >= GS ? g - GS : g); };
     auto stage_copy = [&](int i) {
         const int g = group_of(i);
@@ -271,25 +275,28 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             // copy exactly (same source, same destination, same bytes).
             const int c = wave * L::PER_WAVE + j;
             const int cpy = c < L::COPIES ? c : L::COPIES - 1;
-            dma16(src + cpy * 1024 + lane * 16, dst + cpy * 1024);
+            dma16(src + cpy * 1024 + lane16, dst + cpy * 1024);
         }
         unsigned char* xdst = smem + L::XRING + ((i % kRing) * L::XSLOT + (wave & 1) * (L::XSLOT - 64)) * 4;
-        dma4(xsum + (static_cast<int64_t>(g) * RB * 16 + xrow) * 4, xdst);
+        dma4(xsum + static_cast<int64_t>(g) * RB * 16 * 4 + xrow4, xdst);
     };
 
     // ---- weights: lane (li, lc) of column tile tn holds row n0 + wn*TN*16 + tn*16 + li,
     //      k = 8*lc .. 8*lc+7 of the group ----
-    const unsigned char* wrow[TN];
-    const uint32_t* prow[TN];
+    // Weight addresses are the uniform payload / pair base plus 32-bit per-lane
+    // byte offsets (the payload of a split projection is below 4 GiB).
+    const unsigned char* payload = static_cast<const unsigned char*>(a.payload);
+    const unsigned char* pairs = static_cast<const unsigned char*>(a.scale);
+    uint32_t wvoff[TN], pvoff[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
-        const int col = min(n0 + wn * TN * 16 + tn * 16 + li, N - 1);
+        const uint32_t col = static_cast<uint32_t>(min(n0 + wn * TN * 16 + tn * 16 + li, N - 1));
         if constexpr (FMT == kFmtQ4) {
-            wrow[tn] = static_cast<const unsigned char*>(a.payload) + static_cast<int64_t>(col) * (K / 2) + 4 * lc;
-            prow[tn] = static_cast<const uint32_t*>(a.scale) + static_cast<int64_t>(col) * G;
+            wvoff[tn] = col * static_cast<uint32_t>(K / 2) + 4u * lc;
+            pvoff[tn] = col * static_cast<uint32_t>(G) * 4u;
         } else {
-            wrow[tn] = static_cast<const unsigned char*>(a.payload) + static_cast<int64_t>(col) * K + 8 * lc;
-            prow[tn] = nullptr;
+            wvoff[tn] = col * static_cast<uint32_t>(K) + 8u * lc;
+            pvoff[tn] = 0;
         }
     }
     auto w_load = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
@@ -297,11 +304,11 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
-                wq[tn][0] = *reinterpret_cast<const uint32_t*>(wrow[tn] + g * 16);
+                wq[tn][0] = *reinterpret_cast<const uint32_t*>(payload + (wvoff[tn] + g * 16u));
                 wq[tn][1] = 0;
-                wp[tn] = prow[tn][g];
+                wp[tn] = *reinterpret_cast<const uint32_t*>(pairs + (pvoff[tn] + g * 4u));
             } else {
-                const uint2 v = *reinterpret_cast<const uint2*>(wrow[tn] + g * 32);
+                const uint2 v = *reinterpret_cast<const uint2*>(payload + (wvoff[tn] + g * 32u));
                 wq[tn][0] = v.x;
                 wq[tn][1] = v.y;
                 wp[tn] = 0;
@@ -319,42 +326,48 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     // with h the step within the chunk and row = tn*16 + li.
     unsigned char* wring = smem + L::WRING + wave * L::WCHUNK;
     const int wrow0 = n0 + wn * TN * 16;
+    // Per lane and chunk instruction j: the record's row offset (fixed) and
+    // which of the chunk's two steps it belongs to.
+    constexpr int NCI = PDW > 0 ? (FMT == kFmtQ4 ? TN / 2 : TN) : 1;
+    uint32_t cvoff[NCI], cpoff[NCI];
+    bool csec[NCI], psec[NCI];
+#pragma unroll
+    for (int j = 0; j < NCI; ++j) {
+        const int rec = j * 64 + lane;
+        if constexpr (FMT == kFmtQ4) {
+            const int row = rec >> 1;
+            const uint32_t col = static_cast<uint32_t>(min(wrow0 + row, N - 1));
+            csec[j] = ((rec & 1) ^ ((row >> 3) & 1)) != 0;
+            psec[j] = (rec & 1) != 0;
+            cvoff[j] = col * static_cast<uint32_t>(K / 2);
+            cpoff[j] = col * static_cast<uint32_t>(G) * 4u;
+        } else {
+            const int row = rec >> 2;
+            const int sub = (rec & 3) ^ ((row >> 2) & 3);
+            const uint32_t col = static_cast<uint32_t>(min(wrow0 + row, N - 1));
+            csec[j] = (sub >> 1) != 0;
+            psec[j] = false;
+            cvoff[j] = col * static_cast<uint32_t>(K) + static_cast<uint32_t>(sub & 1) * 16u;
+            cpoff[j] = 0;
+        }
+    }
     auto w_chunk_issue = [&](int c) {
         if constexpr (PDW > 0) {
             unsigned char* slot = wring + (c & 1) * 4 * L::WCHUNK;
             const int s0 = kChunk * c;
+            const int g0 = group_of(s0);                          // s0 < GS
+            const int g1 = group_of(min(s0 + 1, GS - 1));
             if constexpr (FMT == kFmtQ4) {
-                const unsigned char* payload = static_cast<const unsigned char*>(a.payload);
-                const uint32_t* pairs = static_cast<const uint32_t*>(a.scale);
 #pragma unroll
-                for (int j = 0; j < TN / 2; ++j) {
-                    const int rec = j * 64 + lane;
-                    const int row = rec >> 1;
-                    const int h = (rec & 1) ^ ((row >> 3) & 1);
-                    const int col = min(wrow0 + row, N - 1);
-                    const int g = group_of(min(s0 + h, GS - 1));
-                    dma16(payload + static_cast<int64_t>(col) * (K / 2) + g * 16, slot + j * 1024);
-                }
+                for (int j = 0; j < TN / 2; ++j)
+                    dma16(payload + (cvoff[j] + static_cast<uint32_t>(csec[j] ? g1 : g0) * 16u), slot + j * 1024);
 #pragma unroll
-                for (int j = 0; j < TN / 2; ++j) {
-                    const int rec = j * 64 + lane;
-                    const int row = rec >> 1;
-                    const int h = rec & 1;
-                    const int col = min(wrow0 + row, N - 1);
-                    const int g = group_of(min(s0 + h, GS - 1));
-                    dma4(pairs + static_cast<int64_t>(col) * G + g, slot + TN * 512 + j * 256);
-                }
+                for (int j = 0; j < TN / 2; ++j)
+                    dma4(pairs + (cpoff[j] + static_cast<uint32_t>(psec[j] ? g1 : g0) * 4u), slot + TN * 512 + j * 256);
             } else {
-                const unsigned char* payload = static_cast<const unsigned char*>(a.payload);
 #pragma unroll
-                for (int j = 0; j < TN; ++j) {
-                    const int rec = j * 64 + lane;
-                    const int row = rec >> 2;
-                    const int sub = (rec & 3) ^ ((row >> 2) & 3);
-                    const int col = min(wrow0 + row, N - 1);
-                    const int g = group_of(min(s0 + (sub >> 1), GS - 1));
-                    dma16(payload + static_cast<int64_t>(col) * K + g * 32 + (sub & 1) * 16, slot + j * 1024);
-                }
+                for (int j = 0; j < TN; ++j)
+                    dma16(payload + (cvoff[j] + static_cast<uint32_t>(csec[j] ? g1 : g0) * 32u), slot + j * 1024);
             }
         }
     };
@@ -678,8 +691,10 @@ void release_threshold_once(int device) {
 }  // namespace
 
 bool split_ok(const ProjTask& t) {
+    // K in whole groups, 16-byte aligned rows, and weights addressable by
+    // 32-bit offsets from their base (N*K below 2^32).
     return t.K % 32 == 0 && (reinterpret_cast<uintptr_t>(t.x) & 15) == 0 &&
-           (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0;
+           (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0 && int64_t(t.N) * t.K < (int64_t(1) << 32);
 }
 
 // All projections (sharing M) of this call: split every distinct input once into
