@@ -18,6 +18,9 @@ What is computed, and where the pages define it:
   output row, scale[o] = max|W[o,:]| / 127 and W[o,i] ~ q[o,i] * scale[o].
 * The mixed recipe (int4 model card, same section): int4 for wq/wk/wv/wg and
   ffn.w1/w3, int8 for the residual-writing wo and ffn.w2.
+* FP8 E4M3 weights (FP8 model card "RT-J - FP8 E4M3 checkpoints", section
+  "FP8 Format"): every matrix weight stored directly as PyTorch
+  float8_e4m3fn, no scale; W[o,i] is the E4M3 value of its code.
 * The GEMM itself: y = x . W^T with the weights dequantized first (int4 model
   card, opening paragraph: the kernels dequantize inside the GEMM).
 
@@ -37,7 +40,10 @@ the design notes of the repository):
   error sum_k ((q*s16 + m16) - w)^2 is accumulated in fp64 in index order with
   no fused operations; the first alpha with strictly smaller error wins, so
   ties keep the larger alpha;
-* int8: q = clip(rint(w / scale), -127, 127) in fp64, q = 0 for a zero row.
+* int8: q = clip(rint(w / scale), -127, 127) in fp64, q = 0 for a zero row;
+* FP8: the code of an fp32 weight is what a cast to PyTorch's float8_e4m3fn
+  gives: nearest E4M3 value, ties to the even code, NaN (with the input's
+  sign) for magnitudes that round past 448, for infinities and for NaN.
 """
 from __future__ import annotations
 
@@ -50,6 +56,7 @@ CLIP_GRID = (1.00, 0.95, 0.90, 0.85, 0.80)
 RECIPE_MIXED = {"wq": "q4", "wk": "q4", "wv": "q4", "wg": "q4",
                 "w1": "q4", "w3": "q4", "wo": "q8", "w2": "q8"}
 RECIPE_ALL_Q8 = {name: "q8" for name in RECIPE_MIXED}
+RECIPE_ALL_F8 = {name: "f8" for name in RECIPE_MIXED}   # FP8 card: every matrix weight
 
 
 # ----------------------------------------------------------------------------
@@ -211,11 +218,63 @@ def quantize_q8(W: np.ndarray):
     return q.astype(np.int8), scale
 
 
+# ----------------------------------------------------------------------------
+# FP8 E4M3 weights (FP8 model card "RT-J - FP8 E4M3 checkpoints", section
+# "FP8 Format": every matrix weight is stored directly as PyTorch
+# float8_e4m3fn, with no scale). The E4M3 "fn" encoding: 1 sign bit, 4
+# exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals
+# m * 2^-9; there are no infinities, and S.1111.111 is NaN, so the largest
+# finite magnitude is 1.75 * 2^8 = 448.
+# ----------------------------------------------------------------------------
+F8_NAN = 0x7F
+
+
+def decode_f8(codes) -> np.ndarray:
+    """u8 E4M3 codes -> their values in fp64 (exact), NaN for S.1111.111."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    mag = np.where((c & 0x7F) == F8_NAN, np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def quantize_f8(W: np.ndarray) -> np.ndarray:
+    """fp32 W -> u8 E4M3 codes, as a cast to PyTorch's float8_e4m3fn does it:
+    the magnitude goes to the nearest point of the E4M3 grid, a tie to the
+    point with the even code (even mantissa); a magnitude that rounds past 448
+    (to the place 480 that code 0x7F would hold), an infinity and a NaN all
+    become NaN (0x7F); the sign bit is the input's, -0 included."""
+    w = np.asarray(W, dtype=np.float32).astype(np.float64)
+    a = np.abs(w)
+    grid = np.append(decode_f8(np.arange(F8_NAN, dtype=np.uint8)), 480.0)   # codes 0 .. 0x7F, ascending
+    hi = np.clip(np.searchsorted(grid, np.nan_to_num(a, nan=np.inf), side="left"), 1, F8_NAN)
+    lo = hi - 1
+    d_lo = a - grid[lo]
+    d_hi = grid[hi] - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0)), hi, lo)
+    code = np.where(np.isnan(a) | (a > 480.0) | (code == F8_NAN), F8_NAN, code)
+    sign = np.signbit(w).astype(np.int64) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def dequant_f8(codes) -> np.ndarray:
+    """W[o,i] = the E4M3 value of its code, as fp32 (every E4M3 value is exact in fp32)."""
+    return decode_f8(codes).astype(np.float32)
+
+
+def project_f8(x, codes) -> np.ndarray:
+    return gemm_ref(x, dequant_f8(codes))
+
+
 def quantize(W: np.ndarray, fmt: str):
+    """fp32 W -> (payload, scale): the scale companion is None for f8."""
     if fmt == "q4":
         return quantize_q4(W)
     if fmt == "q8":
         return quantize_q8(W)
+    if fmt == "f8":
+        return quantize_f8(W), None
     raise ValueError(f"unknown format {fmt!r}")
 
 
@@ -224,6 +283,8 @@ def dequant(fmt: str, payload, scale) -> np.ndarray:
         return dequant_q4(payload, scale)
     if fmt == "q8":
         return dequant_q8(payload, scale)
+    if fmt == "f8":
+        return dequant_f8(payload)
     raise ValueError(f"unknown format {fmt!r}")
 
 

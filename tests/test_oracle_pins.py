@@ -267,10 +267,73 @@ def pin_gemm_exact_integer(o):
             assert Fraction(float(y[i, j])) == acc, (i, j)
 
 
+# ---- FP8 E4M3 (FP8 model card, "FP8 Format": float8_e4m3fn weights, no scale) ----
+def _f8_value(code):
+    """The E4M3 value of a code from its bit fields, exactly; None for NaN."""
+    if code & 0x7F == 0x7F:
+        return None
+    e, m = (code >> 3) & 0xF, code & 0x7
+    mag = Fraction(m, 512) if e == 0 else (1 + Fraction(m, 8)) * Fraction(2) ** (e - 7)
+    return -mag if code & 0x80 else mag
+
+
+def pin_f8_golden(o):
+    for line in _rows("f8_examples.txt"):
+        kind, rest = line.split(" ", 1)
+        a, b = (t.strip() for t in rest.split(";"))
+        if kind == "decode":
+            v = float(o.decode_f8(np.array([int(a, 16)], dtype=np.uint8))[0])
+            if b == "nan":
+                assert math.isnan(v), line
+            else:
+                assert v == float(b) and math.copysign(1.0, v) == math.copysign(1.0, float(b)), line
+        else:
+            code = int(o.quantize_f8(np.array([float(a)], dtype=np.float32))[0])
+            assert code == int(b, 16), (line, hex(code))
+
+
+def pin_f8_decode_rational(o):
+    vals = o.decode_f8(np.arange(256, dtype=np.uint8))
+    for c in range(256):
+        ref = _f8_value(c)
+        if ref is None:
+            assert math.isnan(vals[c]), c
+        else:
+            assert Fraction(float(vals[c])) == ref, c
+            if c & 0x80:
+                assert math.copysign(1.0, float(vals[c])) < 0, c
+
+
+def pin_f8_roundtrip(o):
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = o.decode_f8(codes).astype(np.float32)
+    assert np.array_equal(o.quantize_f8(vals), codes)
+
+
+def pin_f8_nearest(o):
+    """Brute force: the code is the nearest E4M3 value, ties to the even code,
+    NaN past the 448/480 midpoint, the sign bit always the input's."""
+    rng = np.random.default_rng(11)
+    w = (rng.standard_normal(600) * 10.0 ** rng.integers(-4, 3, 600)).astype(np.float32)
+    mids = [(_f8_value(c) + _f8_value(c + 1)) / 2 for c in range(0, 126, 7)]
+    w = np.concatenate([w, np.array([float(m) for m in mids] + [-float(m) for m in mids], dtype=np.float32)])
+    got = o.quantize_f8(w)
+    grid = [(c, _f8_value(c)) for c in range(127)] + [(0x7F, Fraction(480))]
+    for x, code in zip(w.tolist(), got.tolist()):
+        ax = abs(Fraction(x))
+        best = min(grid, key=lambda cv: (abs(cv[1] - ax), cv[0] % 2))[0]
+        if best == 0x7F or ax > 480:
+            best = 0x7F
+        assert code == best | (0x80 if math.copysign(1.0, x) < 0 else 0), (x, hex(code), hex(best))
+
+
+PINS_F8 = [pin_f8_golden, pin_f8_decode_rational, pin_f8_roundtrip, pin_f8_nearest]
+
+
 PINS = [pin_nibble_golden, pin_pack_roundtrip, pin_q4_dequant_golden, pin_q4_dequant_identity_probe,
         pin_q4_dequant_rational, pin_q8_dequant_rational, pin_q8_golden, pin_q8_closed_form,
         pin_q4_recon_bound, pin_q4_grid_roundtrip, pin_q4_clip_argmin, pin_q4_degenerate,
-        pin_gemm_triple_loop, pin_gemm_exact_integer]
+        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -291,6 +354,19 @@ def test_numpy_f64_to_f16_is_correctly_rounded():
              6.0e-5, -2 ** -14 * (1 - 2 ** -11), 0.0]
     for v in vals:
         assert float(np.float64(v).astype(np.float16)) == round_rne(Fraction(v), F16), v
+
+
+def test_f8_encoder_agrees_with_torch_cast():
+    """The oracle's E4M3 encoder (written from the encoding's definition) gives
+    the same codes as PyTorch's own cast to float8_e4m3fn, which the FP8 card
+    names as the storage type."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(13)
+    w = (rng.standard_normal(100000) * 10.0 ** rng.integers(-5, 4, 100000)).astype(np.float32)
+    w = np.concatenate([w, np.array([0.0, -0.0, 448, 449, 464, 465, 480, 1e9, np.inf, -np.inf, np.nan,
+                                     2 ** -9, 2 ** -10, 3 * 2 ** -11, 2 ** -149], dtype=np.float32)])
+    ref = torch.from_numpy(w).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.quantize_f8(w), ref)
 
 
 def test_numpy_fp32_matmul_meets_tolerance():
@@ -422,7 +498,37 @@ def _mut_project_q4_transposed(x, payload, pairs):
     return np.asarray(x, np.float64) @ W.astype(np.float64)[:, ::-1].T
 
 
+def _mut_decode_f8_bias8(codes):
+    return oracle.decode_f8(codes) / 2.0
+
+
+def _mut_decode_f8_no_subnormals(codes):
+    v = oracle.decode_f8(codes)
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.where(((c >> 3) & 0xF) == 0, 0.0, v)
+
+
+def _mut_quantize_f8_ties_away(W):
+    w = np.asarray(W, dtype=np.float32)
+    out = oracle.quantize_f8(w)
+    # bump every exact midpoint to the larger magnitude
+    lo = oracle.decode_f8(out & 0x7F)
+    hi = oracle.decode_f8(np.minimum((out & 0x7F) + 1, 0x7E))
+    mid = np.abs(w.astype(np.float64)) == (lo + hi) / 2
+    return np.where(mid & ((out & 0x7F) < 0x7E), out + 1, out).astype(np.uint8)
+
+
+def _mut_quantize_f8_saturate(W):
+    out = oracle.quantize_f8(W)
+    w = np.asarray(W, dtype=np.float32)
+    return np.where(((out & 0x7F) == 0x7F) & ~np.isnan(w), (out & 0x80) | 0x7E, out).astype(np.uint8)
+
+
 MUTANTS = {
+    "decode_f8_bias8": {"decode_f8": _mut_decode_f8_bias8},
+    "decode_f8_no_subnormals": {"decode_f8": _mut_decode_f8_no_subnormals},
+    "quantize_f8_ties_away": {"quantize_f8": _mut_quantize_f8_ties_away},
+    "quantize_f8_saturate": {"quantize_f8": _mut_quantize_f8_saturate},
     "unpack_swapped": {"unpack_q4": _mut_unpack_swapped},
     "dequant_q4_no_min": {"dequant_q4": _mut_dequant_q4_no_min},
     "dequant_q4_pair_swapped": {"dequant_q4": _mut_dequant_q4_pair_swapped},
