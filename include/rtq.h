@@ -63,7 +63,7 @@ typedef enum rtq_status {
 #define RTQ_Q4_GROUP 32
 #define RTQ_MAX_BLOCKS 64
 
-enum { RTQ_FMT_NONE = 0, RTQ_FMT_Q4 = 1, RTQ_FMT_Q8 = 2 };
+enum { RTQ_FMT_NONE = 0, RTQ_FMT_Q4 = 1, RTQ_FMT_Q8 = 2, RTQ_FMT_F8 = 3 };
 
 /* int4 projection: y[M][N] = x[M][K] . dequant(payload, pairs)^T.
  * K must be a multiple of 32 (the group size). */
@@ -74,12 +74,21 @@ rtq_status rtq_gemm_q4(const float* x, const uint8_t* payload, const uint16_t* p
 rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale,
                        float* y, int64_t M, int64_t N, int64_t K, void* stream);
 
+/* FP8 E4M3 projection: y[M][N] = x[M][K] . W^T with W[o][i] the E4M3 ("fn":
+ * bias 7, subnormals, no infinities, S.1111.111 = NaN) value of the byte
+ * codes[o][i], row-major [N][K], no scale ("RT-J - FP8 E4M3 checkpoints",
+ * section "FP8 Format": matrix weights stored directly as float8_e4m3fn).
+ * Any K >= 1; codes must be 16-byte aligned. A NaN code makes its outputs NaN. */
+rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y,
+                       int64_t M, int64_t N, int64_t K, void* stream);
+
 /* One RT-J block's projections (names of the int4 card, section "Quantization
  * format"; the block count and widths of the "Backends" page, section "Meta").
- * fmt is RTQ_FMT_Q4 or RTQ_FMT_Q8 (so both the mixed int4/int8 recipe and the
- * all-int8 recipe are expressible); payload == NULL skips the projection (for
- * example a checkpoint without the attention gate wg). `scale` is the pairs
- * array for int4 and the per-row scale for int8. Each projection reads its own
+ * fmt is RTQ_FMT_Q4, RTQ_FMT_Q8 or RTQ_FMT_F8 (so the mixed int4/int8 recipe,
+ * the all-int8 recipe and the FP8 checkpoint are expressible); payload == NULL
+ * skips the projection (for example a checkpoint without the attention gate
+ * wg). `scale` is the pairs array for int4, the per-row scale for int8 and is
+ * ignored (may be NULL) for FP8. Each projection reads its own
  * x [M][K] and writes its own y [M][N]; projections may share x. */
 typedef struct rtq_proj {
     int32_t fmt;
@@ -108,6 +117,7 @@ rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* 
                           int64_t N, int64_t K, void* stream);
 rtq_status rtq_dequant_q8(const int8_t* q, const float* scale, float* w,
                           int64_t N, int64_t K, void* stream);
+rtq_status rtq_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, void* stream);
 
 /* Quantize a dense fp32 W [N][K] into the int4 format: per 32-group min-MSE
  * clip search over the shrink factors {1.00, 0.95, 0.90, 0.85, 0.80} applied
@@ -125,11 +135,17 @@ rtq_status rtq_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs,
 rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale,
                            int64_t N, int64_t K, void* stream);
 
+/* Encode a dense fp32 W [N][K] as FP8 E4M3 codes the way a cast to PyTorch's
+ * float8_e4m3fn does ("RT-J - FP8 E4M3 checkpoints", section "FP8 Format"):
+ * nearest E4M3 value, ties to the even code; magnitudes that round past 448,
+ * infinities and NaN become NaN (0x7F with the input's sign). */
+rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, void* stream);
+
 /* Arithmetic of the GEMM entry points, process-wide (default RTQ_MATH_SPLIT_BF16).
  *
  * RTQ_MATH_SPLIT_BF16: each fp32 activation is split exactly into three bf16
- *   limbs (x = x1 + x2 + x3, no rounding); the int4/int8 codes are exact in
- *   bf16, so every code*limb product is exact in fp32 and the bf16 matrix
+ *   limbs (x = x1 + x2 + x3, no rounding); the int4/int8 codes and the E4M3
+ *   values are exact in bf16, so every code*limb product is exact in fp32 and the bf16 matrix
  *   cores (v_mfma_f32_16x16x32_bf16) accumulate them in fp32. Per 32-group:
  *   y += scale*sum(code*x) + min*sum(x) (int4), y = scale[o]*sum(q*x) (int8).
  *   Same accuracy class as an fp32 GEMM (fp32 accumulation of exact products).

@@ -145,6 +145,21 @@ def test_quantize_dequant_validation(lib):
     assert lib.rtq_dequant_q8(B, C, A, 0, 64, None) == OK
 
 
+def test_f8_validation(lib):
+    assert lib.rtq_gemm_f8(A, B, D, 80, 512, 0, None) == ERR_SHAPE
+    assert lib.rtq_gemm_f8(A, None, D, 80, 512, 512, None) == ERR_NULL
+    assert lib.rtq_gemm_f8(A, B + 4, D, 80, 512, 512, None) == ERR_ALIGN
+    assert lib.rtq_gemm_f8(A, B, A + 1024, 80, 512, 512, None) == ERR_OVERLAP
+    assert lib.rtq_gemm_f8(None, B, None, 0, 512, 512, None) == OK
+    assert lib.rtq_dequant_f8(None, A, 4, 64, None) == ERR_NULL
+    assert lib.rtq_dequant_f8(B, A, 0, 64, None) == OK
+    assert lib.rtq_quantize_f8(A + 2, B, 4, 64, None) == ERR_ALIGN
+    assert lib.rtq_quantize_f8(A, A + 16, 4, 64, None) == ERR_OVERLAP
+    # an FP8 projection needs no scale companion
+    blk = _block(fmt=rtq.FMT_F8, s=None)
+    assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 0, None) == OK
+
+
 def test_math_mode_switch(lib):
     assert lib.rtq_get_math() == rtq.MATH_SPLIT_BF16
     assert lib.rtq_set_math(7) == ERR_FORMAT

@@ -52,10 +52,13 @@ def assert_same_quant(wg, ref, fmt):
         p, s = ref
         assert np.array_equal(host(wg.payload), p), "int4 codes differ"
         assert np.array_equal(host(wg.pairs).view(np.uint16), s.view(np.uint16)), "int4 pairs differ"
-    else:
+    elif fmt == "q8":
         q, s = ref
         assert np.array_equal(host(wg.payload), q), "int8 codes differ"
         assert np.array_equal(host(wg.scale).view(np.uint32), s.view(np.uint32)), "int8 scales differ"
+    else:
+        codes, _ = ref
+        assert np.array_equal(host(wg.payload), codes), "FP8 codes differ"
 
 
 # ----------------------------------------------------------------------------
@@ -99,6 +102,24 @@ def test_quantize_q8_edge_cases():
     assert_same_quant(gpu_quantize(W, "q8"), oracle.quantize_q8(W), "q8")
 
 
+@pytest.mark.parametrize("N,K,heavy", [(512, 512, None), (512, 2048, "rows"), (33, 100, "cols"), (5, 7, None)])
+def test_quantize_f8_bit_exact(N, K, heavy):
+    say(f"quantize_f8 N={N} K={K} heavy={heavy}")
+    W = synth.weight(16, 0, 0, "wq", N, K, heavy=heavy)
+    assert_same_quant(gpu_quantize(W, "f8"), (oracle.quantize_f8(W), None), "f8")
+
+
+def test_quantize_f8_edge_cases():
+    """Ties, the subnormal range, the 448/464/480 overflow boundary, signed
+    zeros, infinities and NaN (PyTorch's float8_e4m3fn cast semantics)."""
+    specials = np.array([0.0, -0.0, 448, 449, 463.99997, 464, 464.00003, 480, 1e9, np.inf, -np.inf, np.nan,
+                         -448, -465, 2 ** -9, 2 ** -10, 3 * 2 ** -11, 7.5 * 2 ** -9, 2 ** -6, 1.0625, 1.1875,
+                         17, 19, -19, 1e-39, -1e-39, 2 ** -149, 0.0146484375], dtype=np.float32)
+    W = np.resize(specials, (8, 64)).astype(np.float32)
+    W[4:] = synth.weight(16, 1, 0, "wk", 4, 64) * np.float32(10.0) ** np.arange(-3, 1, dtype=np.float32)[:, None]
+    assert_same_quant(gpu_quantize(W, "f8"), (oracle.quantize_f8(W), None), "f8")
+
+
 # ----------------------------------------------------------------------------
 # Unpacking and dequantization: bit-exact.
 # ----------------------------------------------------------------------------
@@ -137,6 +158,18 @@ def test_dequant_q8_bit_exact(N, K):
     assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
 
 
+@pytest.mark.parametrize("N,K", [(16, 16), (512, 512), (7, 33)])
+def test_dequant_f8_bit_exact(N, K):
+    """Every E4M3 code decodes to its exact value (NaN codes to NaN)."""
+    codes = np.resize(np.arange(256, dtype=np.uint8), (N, K)) if N * K <= 256 else \
+        synth.uniform_bytes(N * K, (N, K))
+    got = host(rtq.dequant(rtq.F8Weight(dev(codes))))
+    want = oracle.dequant_f8(codes)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan].view(np.uint32), want[~nan].view(np.uint32))
+
+
 # ----------------------------------------------------------------------------
 # GEMM parity.
 # ----------------------------------------------------------------------------
@@ -172,9 +205,13 @@ def test_gemm_q8_parity(M, N, K, math):
     assert err <= TOL, err
 
 
-@pytest.mark.parametrize("fmt,K", [("q4", 64), ("q4", 96), ("q4", 512), ("q8", 64), ("q8", 160), ("q8", 40)])
+@pytest.mark.parametrize("fmt,K", [("q4", 64), ("q4", 96), ("q4", 512), ("q8", 64), ("q8", 160), ("q8", 40),
+                                   ("f8", 64), ("f8", 40)])
 def test_gemm_identity_is_bit_exact(fmt, K, math):
-    """x = I_K gives y = W^T exactly: checks the in-GEMM unpack/dequant bit for bit."""
+    """x = I_K gives y = W^T exactly: checks the in-GEMM unpack/dequant bit for
+    bit. Zeros compare by value: a -0 weight (FP8 code 0x80) sums to +0 in any
+    IEEE dot product, the oracle's included; the signed zero itself is checked
+    by the dequant tests."""
     say(f"identity {fmt} K={K} math={math}")
     N = 72
     W = synth.weight(13, 0, 0, "wv", N, K, heavy="rows")
@@ -182,8 +219,26 @@ def test_gemm_identity_is_bit_exact(fmt, K, math):
     w = gpu_quantize(W, fmt)
     assert_same_quant(w, ref, fmt)
     y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), w))
-    want = oracle.dequant(fmt, *ref).T
-    assert np.array_equal(y.view(np.uint32), np.ascontiguousarray(want).view(np.uint32))
+    want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T)
+    assert np.array_equal(y, want)
+    nz = want != 0
+    assert np.array_equal(y[nz].view(np.uint32), want[nz].view(np.uint32))
+
+
+F8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (5, 3, 7), (257, 129, 2048), (300, 129, 64)]
+
+
+@pytest.mark.parametrize("M,N,K", F8_SHAPES)
+def test_gemm_f8_parity(M, N, K, math):
+    say(f"gemm_f8 M={M} N={N} K={K} math={math}")
+    W = synth.weight(17, 0, 0, "w1", N, K, heavy="rows")
+    x = synth.activation(17, 0, "x_ffn", M, K)
+    codes = oracle.quantize_f8(W)
+    w = gpu_quantize(W, "f8")
+    assert_same_quant(w, (codes, None), "f8")
+    y = host(rtq.gemm_f8(dev(x), w))
+    err = oracle.rel_fro(y, oracle.project_f8(x, codes))
+    assert err <= TOL, err
 
 
 @pytest.mark.parametrize("M,N,K", [(80, 512, 512), (200, 96, 2048)])
@@ -256,11 +311,12 @@ def make_block(cfg, set_, b, M, recipe, xs=None, heavy=None, skip=()):
     return blk, refs, xs
 
 
-@pytest.mark.parametrize("recipe_name", ["mixed", "all_q8"])
+@pytest.mark.parametrize("recipe_name", ["mixed", "all_q8", "all_f8"])
 def test_block_project_one_block(recipe_name, math):
     say(f"block_project one block recipe={recipe_name}")
-    recipe = rtq.RECIPE_MIXED if recipe_name == "mixed" else rtq.RECIPE_ALL_Q8
-    assert recipe == (oracle.RECIPE_MIXED if recipe_name == "mixed" else oracle.RECIPE_ALL_Q8)
+    recipe = {"mixed": rtq.RECIPE_MIXED, "all_q8": rtq.RECIPE_ALL_Q8, "all_f8": rtq.RECIPE_ALL_F8}[recipe_name]
+    assert recipe == {"mixed": oracle.RECIPE_MIXED, "all_q8": oracle.RECIPE_ALL_Q8,
+                      "all_f8": oracle.RECIPE_ALL_F8}[recipe_name]
     M = 80
     blk, refs, xs = make_block(3, 0, 0, M, recipe)
     rtq.block_project([blk], M)

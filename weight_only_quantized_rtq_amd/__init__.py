@@ -5,9 +5,11 @@ the contraction, the quantizers) runs in the library's HIP kernels. PyTorch
 supplies device memory and the current stream. There is no fallback: if the
 library is missing or fails to load, every call raises.
 
-Formats (RT-J int4 / int8 model cards, section "Quantization format"):
+Formats (RT-J int4 / int8 model cards, section "Quantization format"; FP8
+model card, section "FP8 Format"):
   Q4Weight(payload uint8 [N, K/2], pairs float16 [N, K/32, 2])   (scale, min)
   Q8Weight(payload int8 [N, K],    scale float32 [N])
+  F8Weight(payload uint8 [N, K])   E4M3 ("float8_e4m3fn") codes, no scale
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "librtq.so")
 
-FMT_NONE, FMT_Q4, FMT_Q8 = 0, 1, 2
+FMT_NONE, FMT_Q4, FMT_Q8, FMT_F8 = 0, 1, 2, 3
 Q4_GROUP = 32
 MAX_BLOCKS = 64
 PROJ_NAMES = ("wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2")
@@ -31,13 +33,15 @@ PROJ_NAMES = ("wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2")
 RECIPE_MIXED = {"wq": "q4", "wk": "q4", "wv": "q4", "wg": "q4",
                 "wo": "q8", "w1": "q4", "w3": "q4", "w2": "q8"}
 RECIPE_ALL_Q8 = {n: "q8" for n in PROJ_NAMES}
+RECIPE_ALL_F8 = {n: "f8" for n in PROJ_NAMES}   # FP8 card: every matrix weight E4M3
 
 STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN",
           4: "RTQ_ERR_FORMAT", 5: "RTQ_ERR_HIP", 6: "RTQ_ERR_OVERLAP"}
 
 # Every symbol include/rtq.h declares.
-EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_block_project", "rtq_dequant_q4", "rtq_dequant_q8",
-           "rtq_quantize_q4", "rtq_quantize_q8", "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
+EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
+           "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
+           "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 MATH_SPLIT_BF16, MATH_FP32_MFMA = 0, 1
@@ -74,6 +78,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     for name in ("rtq_gemm_q4", "rtq_gemm_q8"):
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+        f.restype = ctypes.c_int
+    lib.rtq_gemm_f8.argtypes = [vp, vp, vp, i64, i64, i64, vp]
+    lib.rtq_gemm_f8.restype = ctypes.c_int
+    for name in ("rtq_dequant_f8", "rtq_quantize_f8"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, i64, i64, vp]
         f.restype = ctypes.c_int
     lib.rtq_block_project.argtypes = [ctypes.POINTER(_Block), i32, i64, vp]
     lib.rtq_block_project.restype = ctypes.c_int
@@ -206,9 +216,33 @@ class Q8Weight:
                              f"scale {tuple(self.scale.shape)}")
 
 
-def weight_from_tensors(payload: torch.Tensor, scale: torch.Tensor):
+@dataclass
+class F8Weight:
+    payload: torch.Tensor   # uint8 [N, K]: E4M3 codes (a float8_e4m3fn tensor viewed as bytes)
+
+    @property
+    def N(self) -> int:
+        return self.payload.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.payload.shape[1]
+
+    fmt = FMT_F8
+    scale_tensor = None
+
+    def validate(self) -> None:
+        _need(self.payload, torch.uint8, "payload")
+        if self.payload.dim() != 2:
+            raise ValueError(f"FP8 weight must be [N, K], got {tuple(self.payload.shape)}")
+
+
+def weight_from_tensors(payload: torch.Tensor, scale: torch.Tensor | None = None):
     """Format detection from the payload dtype, as the engine's loader does
-    (int4 card, "Usage": the format is read off the tensor dtypes): uint8 -> int4, int8 -> int8."""
+    (int4 card, "Usage": the format is read off the tensor dtypes): uint8 ->
+    int4, int8 -> int8, float8_e4m3fn (FP8 card, "FP8 Format") -> FP8."""
+    if payload.dtype == torch.float8_e4m3fn:
+        return F8Weight(payload.view(torch.uint8))
     if payload.dtype == torch.uint8:
         return Q4Weight(payload, scale)
     if payload.dtype == torch.int8:
@@ -229,6 +263,9 @@ def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream) -> torch.Tensor:
         _need(y, torch.float32, "y")
         if tuple(y.shape) != (M, w.N):
             raise ValueError(f"y must be [{M}, {w.N}], got {tuple(y.shape)}")
+    if w.fmt == FMT_F8:
+        _check(lib.rtq_gemm_f8(_ptr(x), _ptr(w.payload), _ptr(y), M, w.N, w.K, _stream(stream)))
+        return y
     fn = lib.rtq_gemm_q4 if w.fmt == FMT_Q4 else lib.rtq_gemm_q8
     _check(fn(_ptr(x), _ptr(w.payload), _ptr(w.scale_tensor), _ptr(y), M, w.N, w.K, _stream(stream)))
     return y
@@ -248,6 +285,13 @@ def gemm_q8(x: torch.Tensor, w: Q8Weight, y: torch.Tensor | None = None, stream=
     return _gemm(x, w, y, stream)
 
 
+def gemm_f8(x: torch.Tensor, w: F8Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = x . W^T for an FP8 E4M3 weight (rtq_gemm_f8)."""
+    if not isinstance(w, F8Weight):
+        raise TypeError("gemm_f8 needs an F8Weight")
+    return _gemm(x, w, y, stream)
+
+
 def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     return _gemm(x, w, y, stream)
 
@@ -257,6 +301,9 @@ def dequant(w, stream=None) -> torch.Tensor:
     lib = load_library()
     w.validate()
     out = torch.empty((w.N, w.K), dtype=torch.float32, device=w.payload.device)
+    if w.fmt == FMT_F8:
+        _check(lib.rtq_dequant_f8(_ptr(w.payload), _ptr(out), w.N, w.K, _stream(stream)))
+        return out
     fn = lib.rtq_dequant_q4 if w.fmt == FMT_Q4 else lib.rtq_dequant_q8
     _check(fn(_ptr(w.payload), _ptr(w.scale_tensor), _ptr(out), w.N, w.K, _stream(stream)))
     return out
@@ -284,18 +331,30 @@ def quantize_q8(W: torch.Tensor, stream=None) -> Q8Weight:
     return Q8Weight(q, scale)
 
 
+def quantize_f8(W: torch.Tensor, stream=None) -> F8Weight:
+    """FP8 E4M3 codes, as a cast to float8_e4m3fn gives them (rtq_quantize_f8)."""
+    lib = load_library()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
+    _check(lib.rtq_quantize_f8(_ptr(W), _ptr(codes), N, K, _stream(stream)))
+    return F8Weight(codes)
+
+
 def quantize(W: torch.Tensor, fmt: str, stream=None):
     if fmt == "q4":
         return quantize_q4(W, stream)
     if fmt == "q8":
         return quantize_q8(W, stream)
+    if fmt == "f8":
+        return quantize_f8(W, stream)
     raise ValueError(f"unknown format {fmt!r}")
 
 
 @dataclass
 class Projection:
     """One projection of a block: its weight, the input it reads and the output it writes."""
-    weight: object               # Q4Weight | Q8Weight
+    weight: object               # Q4Weight | Q8Weight | F8Weight
     x: torch.Tensor              # float32 [M, K]
     y: torch.Tensor              # float32 [M, N]
 

@@ -59,14 +59,14 @@ rtq_status check_proj(const char* name, int fmt, const float* x, const void* pay
     if (M == 0) return RTQ_OK;
     if (!x) return fail(RTQ_ERR_NULL, "%s: x is NULL", name);
     if (!payload) return fail(RTQ_ERR_NULL, "%s: payload is NULL", name);
-    if (!scale) return fail(RTQ_ERR_NULL, "%s: scale is NULL", name);
+    if (!scale && fmt != rtq::kFmtF8) return fail(RTQ_ERR_NULL, "%s: scale is NULL", name);
     if (!y) return fail(RTQ_ERR_NULL, "%s: y is NULL", name);
     if (!aligned(x, 16)) return fail(RTQ_ERR_ALIGN, "%s: x is not 16-byte aligned", name);
     if (!aligned(y, 16)) return fail(RTQ_ERR_ALIGN, "%s: y is not 16-byte aligned", name);
     if (!aligned(payload, 16)) return fail(RTQ_ERR_ALIGN, "%s: payload is not 16-byte aligned", name);
     if (!aligned(scale, 4)) return fail(RTQ_ERR_ALIGN, "%s: scale is not 4-byte aligned", name);
     const int64_t payload_bytes = fmt == rtq::kFmtQ4 ? N * (K / 2) : N * K;
-    const int64_t scale_bytes = fmt == rtq::kFmtQ4 ? N * (K / RTQ_Q4_GROUP) * 4 : N * 4;
+    const int64_t scale_bytes = fmt == rtq::kFmtQ4 ? N * (K / RTQ_Q4_GROUP) * 4 : fmt == rtq::kFmtQ8 ? N * 4 : 0;
     const Range ry = range_of(y, M * N * 4);
     if (overlaps(ry, range_of(x, M * K * 4)) || overlaps(ry, range_of(payload, payload_bytes)) ||
         overlaps(ry, range_of(scale, scale_bytes)))
@@ -202,6 +202,15 @@ rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale, floa
     return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_q8 launch");
 }
 
+rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y, int64_t M, int64_t N, int64_t K,
+                       void* stream) {
+    clear_error();
+    rtq_status s = check_proj("rtq_gemm_f8", rtq::kFmtF8, x, codes, nullptr, y, M, N, K);
+    if (s != RTQ_OK || M == 0) return s;
+    const rtq::ProjTask t{rtq::kFmtF8, static_cast<int>(N), static_cast<int>(K), codes, nullptr, x, y};
+    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_f8 launch");
+}
+
 rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
     clear_error();
     if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
@@ -221,7 +230,7 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
             if (!d.payload) continue;
             char name[64];
             std::snprintf(name, sizeof(name), "rtq_block_project: block %d %s", b, names[j]);
-            if (d.fmt != RTQ_FMT_Q4 && d.fmt != RTQ_FMT_Q8)
+            if (d.fmt != RTQ_FMT_Q4 && d.fmt != RTQ_FMT_Q8 && d.fmt != RTQ_FMT_F8)
                 return fail(RTQ_ERR_FORMAT, "%s: unknown fmt %d", name, d.fmt);
             if (d.reserved != 0) return fail(RTQ_ERR_SHAPE, "%s: reserved field must be 0", name);
             const rtq_status s = check_proj(name, d.fmt, d.x, d.payload, d.scale, d.y, M, d.N, d.K);
@@ -229,7 +238,8 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
             if (M == 0) continue;
             outs[n_outs++] = range_of(d.y, M * int64_t(d.N) * 4);
             const int64_t pb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 2) : int64_t(d.N) * d.K;
-            const int64_t sb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 32) * 4 : int64_t(d.N) * 4;
+            const int64_t sb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 32) * 4
+                               : d.fmt == RTQ_FMT_Q8 ? int64_t(d.N) * 4 : 0;
             ins[n_ins++] = range_of(d.x, M * int64_t(d.K) * 4);
             ins[n_ins++] = range_of(d.payload, pb);
             ins[n_ins++] = range_of(d.scale, sb);
@@ -303,6 +313,32 @@ rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, i
     if (!aligned(w, 4) || !aligned(scale, 4)) return fail(RTQ_ERR_ALIGN, "rtq_quantize_q8: misaligned pointer");
     return hip_status(rtq::launch_quantize_q8(w, q, scale, N, K, static_cast<hipStream_t>(stream)),
                       "rtq_quantize_q8 launch");
+}
+
+rtq_status rtq_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, void* stream) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+        return fail(RTQ_ERR_SHAPE, "rtq_dequant_f8: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!codes || !w) return fail(RTQ_ERR_NULL, "rtq_dequant_f8: a pointer argument is NULL");
+    if (!aligned(w, 4)) return fail(RTQ_ERR_ALIGN, "rtq_dequant_f8: misaligned pointer");
+    if (overlaps(range_of(w, N * K * 4), range_of(codes, N * K)))
+        return fail(RTQ_ERR_OVERLAP, "rtq_dequant_f8: output overlaps the codes");
+    return hip_status(rtq::launch_dequant_f8(codes, w, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_dequant_f8 launch");
+}
+
+rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, void* stream) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+        return fail(RTQ_ERR_SHAPE, "rtq_quantize_f8: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!w || !codes) return fail(RTQ_ERR_NULL, "rtq_quantize_f8: a pointer argument is NULL");
+    if (!aligned(w, 4)) return fail(RTQ_ERR_ALIGN, "rtq_quantize_f8: misaligned pointer");
+    if (overlaps(range_of(w, N * K * 4), range_of(codes, N * K)))
+        return fail(RTQ_ERR_OVERLAP, "rtq_quantize_f8: output overlaps the weights");
+    return hip_status(rtq::launch_quantize_f8(w, codes, N, K, static_cast<hipStream_t>(stream)),
+                      "rtq_quantize_f8 launch");
 }
 
 }  // extern "C"

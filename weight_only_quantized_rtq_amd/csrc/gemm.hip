@@ -116,7 +116,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, flo
             if constexpr (SAFE) {
 #pragma unroll
                 for (int j = 0; j < 16; ++j)
-                    wsafe[j] = (wrow < N && kb + j < K) ? static_cast<float>(p[kb + j]) : 0.0f;
+                    wsafe[j] = (wrow < N && kb + j < K) ? code8_value<FMT>(static_cast<uint8_t>(p[kb + j])) : 0.0f;
             } else {
                 q8bits = wrow < N ? *reinterpret_cast<const uint4*>(p + kb) : make_uint4(0, 0, 0, 0);
             }
@@ -150,7 +150,7 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, flo
             const uint32_t words[4] = {q8bits.x, q8bits.y, q8bits.z, q8bits.w};
 #pragma unroll
             for (int j = 0; j < 16; ++j)
-                wv[j] = static_cast<float>(static_cast<int8_t>((words[j >> 2] >> (8 * (j & 3))) & 0xffu));
+                wv[j] = code8_value<FMT>(words[j >> 2] >> (8 * (j & 3)));
         }
         float* wd = ws[buf] + wr * kLD + wh * 16;
 #pragma unroll
@@ -361,7 +361,7 @@ __device__ __forceinline__ void stream_tile(const TileArgs& a, int slice, int n_
                     if constexpr (FMT == kFmtQ4) {
                         b[tn] = fmaf(static_cast<float>(nibble(wd[tn][step >> 3], step & 7)), s[tn], m[tn]);
                     } else {
-                        b[tn] = static_cast<float>(static_cast<int8_t>((wd[tn][step >> 2] >> (8 * (step & 3))) & 0xffu));
+                        b[tn] = code8_value<FMT>(wd[tn][step >> 2] >> (8 * (step & 3)));
                     }
                 }
 #pragma unroll
@@ -488,8 +488,10 @@ __global__ __launch_bounds__(256) void grouped_stream_kernel(GroupArgs g) {
     const TileArgs a{g.xs[xi], g.payload[i], g.scale[i], g.y[i], g.M, N, K};
     if (g.fmt[i] == kFmtQ4)
         stream_tile<kFmtQ4, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
-    else
+    else if (g.fmt[i] == kFmtQ8)
         stream_tile<kFmtQ8, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
+    else
+        stream_tile<kFmtF8, TM, kStreamTN>(a, slice, n_slices, ks, chunk, red);
 }
 
 template <int FMT, bool SAFE>
@@ -537,7 +539,8 @@ hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
     if (!safe && math_mode() == kMathSplitBf16 && split_ok(t)) return launch_split(&t, 1, M, stream);
     if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
     if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
-    return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
+    if (t.fmt == kFmtQ8) return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
+    return safe ? launch_one<kFmtF8, true>(a, stream) : launch_one<kFmtF8, false>(a, stream);
 }
 
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {

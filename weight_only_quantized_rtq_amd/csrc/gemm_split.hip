@@ -92,6 +92,22 @@ __device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// 8 FP8 E4M3 codes (two words, low byte first) -> 8 bf16, exactly: an E4M3
+// value has at most 4 significant bits and lies within the bf16 exponent
+// range, so the high half of its fp32 form is the value.
+__device__ __forceinline__ u32x4 codes8f_to_bf16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);
+    u32x4 r;
+    r[0] = pack_hi(a[0], a[1]);
+    r[1] = pack_hi(b[0], b[1]);
+    r[2] = pack_hi(c[0], c[1]);
+    r[3] = pack_hi(d[0], d[1]);
+    return r;
+}
+
 __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
                                                    0, 0, 0);
@@ -417,7 +433,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                 const float mn = half_bits_to_float(cp[tn] >> 16);
                 mreg[tn] = lc == (i & 3) ? mn : mreg[tn];
             } else {
-                b[tn] = codes8_to_bf16(cq[tn][0], cq[tn][1]);
+                if constexpr (FMT == kFmtF8) b[tn] = codes8f_to_bf16(cq[tn][0], cq[tn][1]);
+                else b[tn] = codes8_to_bf16(cq[tn][0], cq[tn][1]);
             }
         }
 #pragma unroll
@@ -616,8 +633,10 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     const int rot = cb % (g_hi - g_lo);
     if (g.fmt[i] == kFmtQ4)
         split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
-    else
+    else if (g.fmt[i] == kFmtQ8)
         split_tile<kFmtQ8, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
+    else
+        split_tile<kFmtF8, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
 }
 
 // Sums the K-chunk partials of split projections in chunk order.
@@ -822,8 +841,10 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             const int mark = timing_begin(stream);
             if (t.fmt == kFmtQ4)
                 split_gemm_kernel<kFmtQ4><<<tmb * tn, 256, 0, stream>>>(a, tn);
-            else
+            else if (t.fmt == kFmtQ8)
                 split_gemm_kernel<kFmtQ8><<<tmb * tn, 256, 0, stream>>>(a, tn);
+            else
+                split_gemm_kernel<kFmtF8><<<tmb * tn, 256, 0, stream>>>(a, tn);
             timing_end(mark, stream);
             e = hipGetLastError();
         }

@@ -158,6 +158,39 @@ inline unsigned blocks_for(int64_t n, int per) {
     return static_cast<unsigned>((n + per - 1) / per);
 }
 
+// FP8 E4M3 codes of fp32 weights, as a cast to PyTorch's float8_e4m3fn gives
+// them (FP8 model card, "FP8 Format"): the nearest point of the E4M3 grid,
+// ties to the even code, NaN (0x7F with the input's sign) past 448 and for
+// infinities and NaN. With e the binary exponent of |w|, clamped below at -6
+// (the smallest normal exponent), |w| * 2^(3-e) lies in [0, 16) and is exact;
+// its rounding to an integer is the mantissa (plus 8 for normal values), so
+// code = 8 * (e + 6) + rint(|w| * 2^(3-e)), and a rounding up to 16 carries
+// into the exponent field by itself.
+__global__ __launch_bounds__(256) void quantize_f8_kernel(const float* __restrict__ w,
+                                                          uint8_t* __restrict__ codes, int64_t total) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256) {
+        const uint32_t bits = __float_as_uint(w[i]);
+        const uint32_t sign = (bits >> 24) & 0x80u;
+        const uint32_t mag = bits & 0x7fffffffu;
+        uint32_t code = 0x7fu;                                   // infinity or NaN
+        if (mag < 0x7f800000u) {
+            const int e = max(static_cast<int>(mag >> 23) - 127, -6);
+            const int q = static_cast<int>(rintf(ldexpf(__uint_as_float(mag), 3 - e)));
+            const int c = 8 * (e + 6) + q;
+            code = c > 0x7e ? 0x7fu : static_cast<uint32_t>(c);
+        }
+        codes[i] = static_cast<uint8_t>(sign | code);
+    }
+}
+
+__global__ __launch_bounds__(256) void dequant_f8_kernel(const uint8_t* __restrict__ codes,
+                                                         float* __restrict__ w, int64_t total) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        w[i] = f8_to_float(codes[i]);
+}
+
 }  // namespace
 
 hipError_t launch_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N,
@@ -189,6 +222,22 @@ hipError_t launch_dequant_q8(const int8_t* q, const float* scale, float* w, int6
                              hipStream_t stream) {
     const int64_t total = N * K;
     dequant_q8_kernel<<<blocks_for(total, 256), 256, 0, stream>>>(q, scale, w, total, K);
+    return hipGetLastError();
+}
+
+}  // namespace rtq
+
+namespace rtq {
+
+hipError_t launch_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t total = N * K;
+    quantize_f8_kernel<<<blocks_for(total, 256), 256, 0, stream>>>(w, codes, total);
+    return hipGetLastError();
+}
+
+hipError_t launch_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, hipStream_t stream) {
+    const int64_t total = N * K;
+    dequant_f8_kernel<<<blocks_for(total, 256), 256, 0, stream>>>(codes, w, total);
     return hipGetLastError();
 }
 

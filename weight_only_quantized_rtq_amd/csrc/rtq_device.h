@@ -92,6 +92,17 @@ inline void seg_fill_coarse(const T (&begin)[SLOTS], T (&coarse)[NC], int count)
     for (int c = 0; c < NC; ++c) coarse[c] = c * kSegStride < count ? begin[c * kSegStride] : begin[0];
 }
 
+// FP8 E4M3 ("fn": bias 7, subnormals, S.1111.111 = NaN) code -> fp32, exact,
+// through the hardware conversion (the byte in bits 0..7).
+__device__ __forceinline__ float f8_to_float(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8(code, 0); }
+
+// The value of a one-byte weight code: int8 for the int8 format, E4M3 for FP8.
+template <int FMT>
+__device__ __forceinline__ float code8_value(uint32_t byte) {
+    if constexpr (FMT == 3) return f8_to_float(byte & 0xffu);
+    else return static_cast<float>(static_cast<int8_t>(byte & 0xffu));
+}
+
 // Low nibble = even index.
 __device__ __forceinline__ uint32_t nibble(uint32_t word, int idx) {
     return (word >> (4 * idx)) & 0xFu;

@@ -6,7 +6,7 @@
 
 namespace rtq {
 
-enum Fmt : int { kFmtQ4 = 1, kFmtQ8 = 2 };
+enum Fmt : int { kFmtQ4 = 1, kFmtQ8 = 2, kFmtF8 = 3 };
 
 hipError_t launch_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N,
                               int64_t K, hipStream_t stream);
@@ -16,6 +16,8 @@ hipError_t launch_dequant_q4(const uint8_t* payload, const uint16_t* pairs, floa
                              int64_t K, hipStream_t stream);
 hipError_t launch_dequant_q8(const int8_t* q, const float* scale, float* w, int64_t N, int64_t K,
                              hipStream_t stream);
+hipError_t launch_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, hipStream_t stream);
+hipError_t launch_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, hipStream_t stream);
 
 // One projection of a grouped launch.
 struct ProjTask {
