@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--warmup-large", type=int, default=2)
     ap.add_argument("--workload", choices=["m80", "m65536", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--recipe", choices=["mixed", "all_q8", "all_f8"], default="mixed",
+                    help="weight formats: the int4 card's mixed int4/int8 recipe (default), the int8 card's "
+                         "all-int8 recipe, or the FP8 card's all-E4M3 weights")
     ap.add_argument("--math", choices=["split", "fp32"], default="split",
                     help="GEMM arithmetic: exact bf16x3 split on the bf16 MFMA (default) or fp32 MFMA")
     ap.add_argument("--compare-fp32", action="store_true",
@@ -59,22 +62,34 @@ def parse():
     return ap.parse_args()
 
 
-def block_bytes_flops(M):
-    import synth
+RECIPES = ("mixed", "all_q8", "all_f8")
+
+
+def recipe_map(name):
     import weight_only_quantized_rtq_amd as rtq
+    return {"mixed": rtq.RECIPE_MIXED, "all_q8": rtq.RECIPE_ALL_Q8, "all_f8": rtq.RECIPE_ALL_F8}[name]
+
+
+def block_bytes_flops(M, recipe="mixed"):
+    """Packed weight bytes and GEMM flops of one RT-J block: int4 0.5 B codes +
+    4 B (scale, min) per 32; int8 1 B codes + 4 B scale per row; FP8 1 B codes."""
+    import synth
+    rec = recipe_map(recipe)
     wbytes = 0
     flops = 0
     for name in synth.PROJ_ORDER:
         N, K, _ = synth.BLOCK_SHAPES[name]
-        if rtq.RECIPE_MIXED[name] == "q4":
+        if rec[name] == "q4":
             wbytes += N * K // 2 + N * (K // 32) * 4
-        else:
+        elif rec[name] == "q8":
             wbytes += N * K + N * 4
+        else:
+            wbytes += N * K
         flops += 2 * M * N * K
     return wbytes, flops
 
 
-def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None):
+def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, recipe="mixed"):
     """Packed weights (quantized on the GPU) for n_sets x 12 blocks, plus inputs
     and outputs, and the host descriptor arrays of each set."""
     dev = "cuda:0"
@@ -95,7 +110,7 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None):
             blk = {}
             for name in synth.PROJ_ORDER:
                 W = torch.from_numpy(synth.weight(cfg, s, b, name, heavy=heavy)).to(dev)
-                w = rtq.quantize(W, rtq.RECIPE_MIXED[name])
+                w = rtq.quantize(W, recipe_map(recipe)[name])
                 del W
                 blk[name] = rtq.Projection(w, xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name])
             blocks.append(blk)
@@ -124,15 +139,15 @@ def time_workload(torch, rtq, sets, M, steps, warmup):
     return wall, kernel_ms, launches
 
 
-def measure(torch, rtq, synth, workload, steps, warmup):
+def measure(torch, rtq, synth, workload, steps, warmup, recipe="mixed"):
     nb = synth.NUM_BLOCKS
     if workload == "m80":
         M = synth.M_GOLDEN
-        sets = build_sets(torch, rtq, synth, 4, M, WEIGHT_SETS, xs_per_block=True)
+        sets = build_sets(torch, rtq, synth, 4, M, WEIGHT_SETS, xs_per_block=True, recipe=recipe)
     else:
         M = synth.M_LARGE
-        sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False)
-    wb, fl = block_bytes_flops(M)
+        sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False, recipe=recipe)
+    wb, fl = block_bytes_flops(M, recipe)
     wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup)
     del sets
     torch.cuda.empty_cache()
@@ -150,14 +165,14 @@ def measure(torch, rtq, synth, workload, steps, warmup):
     }
 
 
-def load_traffic(workload, math):
+def load_traffic(workload, math, recipe="mixed"):
     """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE /
     WRITE_SIZE, copy-kernel calibrated), if recorded for the current sources."""
     import weight_only_quantized_rtq_amd.traffic as tr
-    return tr.lookup(workload, math)
+    return tr.lookup(workload, math) if recipe == "mixed" else None
 
 
-def roofline(res, math, workload):
+def roofline(res, math, workload, recipe="mixed"):
     """Roofline of the main GEMM kernel: algorithmic flops per launch over the
     kernel's average launch duration, against the peak of the matrix unit it
     runs on (split: bf16 MFMA, three limb products per algorithmic multiply-add)."""
@@ -166,7 +181,7 @@ def roofline(res, math, workload):
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
     else:
         peak, issued = PEAK_FP32_MFMA_TFLOPS, 1
-    tr = load_traffic(workload, math)
+    tr = load_traffic(workload, math, recipe)
     out = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
            "frac": round(ach / peak, 5), "traffic": tr["bytes_per_launch"] if tr else None,
            "traffic_detail": tr,
@@ -180,7 +195,7 @@ def roofline(res, math, workload):
     return out
 
 
-def cpu_baseline(cfg, M, seconds, rows=None):
+def cpu_baseline(cfg, M, seconds, rows=None, recipe="mixed"):
     """The oracle (numpy dequant + fp64 GEMM) on a bounded sample: whole
     blocks of this workload, quantized by the oracle's own quantizer."""
     import oracle
@@ -195,13 +210,14 @@ def cpu_baseline(cfg, M, seconds, rows=None):
     for b in range(2):
         projs = []
         for name in synth.PROJ_ORDER:
-            fmt = oracle.RECIPE_MIXED[name]
+            fmt = {"mixed": oracle.RECIPE_MIXED, "all_q8": oracle.RECIPE_ALL_Q8,
+                   "all_f8": oracle.RECIPE_ALL_F8}[recipe][name]
             N, K, xin = synth.BLOCK_SHAPES[name]
             W = synth.weight(cfg, 0, b, name)
             x = synth.activation(cfg, b, xin, Ms)
             projs.append((fmt, x, oracle.quantize(W, fmt)))
         blocks.append(projs)
-    _, flops_block = block_bytes_flops(Ms)
+    _, flops_block = block_bytes_flops(Ms, recipe)
     done = 0
     t0 = time.perf_counter()
     while True:
@@ -232,23 +248,26 @@ def main():
     rtq.set_math(rtq.MATH_SPLIT_BF16 if args.math == "split" else rtq.MATH_FP32_MFMA)
     out = {}
     if args.workload in ("m80", "both"):
-        out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup)
+        out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup, args.recipe)
     if args.workload in ("m65536", "both"):
-        out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large)
+        out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large, args.recipe)
     fp32 = {}
     if args.compare_fp32 and args.math == "split":
         rtq.set_math(rtq.MATH_FP32_MFMA)
         for wl in out:
-            r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1)
+            r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1, args.recipe)
             fp32[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
-                        "roofline": roofline(r, "fp32", wl)}
+                        "roofline": roofline(r, "fp32", wl, args.recipe)}
         rtq.set_math(rtq.MATH_SPLIT_BF16)
 
     prim_name = "m80" if "m80" in out else "m65536"
     prim = out[prim_name]
-    cfg = {"m80": "m80: 12 RT-J blocks (wq/wk/wv/wg/w1/w3 int4 g32, wo/w2 int8), M=80, 16 weight sets "
-                  "cycled (630 MB packed), per-block fp32 activations",
-           "m65536": "m65536: 12 RT-J blocks (mixed int4/int8), M=65536, one weight set, fp32 "
+    wdesc = {"mixed": "wq/wk/wv/wg/w1/w3 int4 g32, wo/w2 int8", "all_q8": "every projection int8",
+             "all_f8": "every projection FP8 E4M3"}[args.recipe]
+    set_mb = WEIGHT_SETS * synth.NUM_BLOCKS * block_bytes_flops(1, args.recipe)[0] / 1e6
+    cfg = {"m80": f"m80: 12 RT-J blocks ({wdesc}), M=80, {WEIGHT_SETS} weight sets cycled "
+                  f"({set_mb:.0f} MB packed), per-block fp32 activations",
+           "m65536": f"m65536: 12 RT-J blocks ({wdesc}), M=65536, one weight set, fp32 "
                      "activations shared by the blocks"}[prim_name]
     line = {
         "metric": "dequant-GEMM TFLOP/s + weight-payload HBM GB/s (frac. of peak), M=80 and M=65536",
@@ -262,13 +281,14 @@ def main():
         "dtype": "bf16x3/f32" if args.math == "split" else "f32",
         "data": "synthetic",
         "config": {"workload": cfg, "M": prim["M"], "n_blocks": synth.NUM_BLOCKS,
-                   "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": "mixed int4/int8",
+                   "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": {"mixed": "mixed int4/int8", "all_q8": "all int8",
+                                                                               "all_f8": "all FP8 E4M3"}[args.recipe],
                    "d_model": synth.D_MODEL, "d_ff": synth.D_FF,
                    "math": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation"
                            if args.math == "split" else "fp32 MFMA on dequantized weights"},
         "weight_gbs": round(prim["weight_gbs"], 2),
         "weight_hbm_frac": round(prim["weight_gbs"] / PEAK_HBM_GBS, 5),
-        "roofline": roofline(prim, args.math, prim_name),
+        "roofline": roofline(prim, args.math, prim_name, args.recipe),
     }
     for wl, r in out.items():
         if wl == prim_name:
@@ -276,11 +296,11 @@ def main():
         line[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                     "weight_gbs": round(r["weight_gbs"], 3), "steps": r["steps"],
                     "frac_of_fp32_mfma_peak": round(r["tflops"] / PEAK_FP32_MFMA_TFLOPS, 4),
-                    "roofline": roofline(r, args.math, wl)}
+                    "roofline": roofline(r, args.math, wl, args.recipe)}
     if fp32:
         line["fp32_mfma_path"] = fp32
     if not args.no_cpu_baseline and prim_name == "m80":
-        line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
     print(json.dumps(line), flush=True)
 
 
