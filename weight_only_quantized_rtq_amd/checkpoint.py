@@ -1,0 +1,176 @@
+"""Quantized RT-J checkpoints: the safetensors storage contract and its tools.
+
+Storage contract (int4 model card "RT-J - int4 (Q4-style, mixed-precision)
+quantized checkpoints" and int8 card, section "Quantization format"; FP8 card
+"RT-J - FP8 E4M3 checkpoints", section "FP8 Format"): plain safetensors.
+
+  int4  <name>           U8   [N, K/2]      two codes per byte, low nibble = even index
+        <name>.q4_scale  F16  [N, K/32, 2]  (scale, min) per group of 32 along K
+  int8  <name>           I8   [N, K]
+        <name>.q_scale   F32  [N]           per-row symmetric scale
+  FP8   <name>           F8_E4M3 [N, K]     no companion; file metadata quantization=fp8_e4m3fn
+
+Every other tensor (encoders, head, norms, biases, mask embeddings) stays as
+it is in the source checkpoint. The format of each tensor is read off its
+dtype, as the engine's loader does (int4 card, "Usage").
+
+    python -m weight_only_quantized_rtq_amd.checkpoint quantize SRC DST --type q4|q8|fp8
+    python -m weight_only_quantized_rtq_amd.checkpoint info FILE
+
+`quantize` is the counterpart of the cards' rt_quantize step: it runs the
+library's GPU quantizers (rtq_quantize_q4 / _q8 / _f8) on the block
+projections. Loading never executes anything from the file (safetensors).
+"""
+from __future__ import annotations
+
+import re
+import sys
+
+import torch
+
+from . import F8Weight, Q4Weight, Q8Weight, quantize
+
+Q4_SCALE = ".q4_scale"
+Q8_SCALE = ".q_scale"
+FP8_METADATA = {"quantization": "fp8_e4m3fn"}
+
+# Block projections by name: the last components wq/wk/wv/wg/wo or (ffn.)w1/w2/w3,
+# optionally followed by ".weight" (the cards name the projections, not the keys).
+PROJ_RE = re.compile(r"(?:^|\.)(wq|wk|wv|wg|wo|w1|w2|w3)(?:\.weight)?$")
+
+# --type -> format of each projection: q4 is the int4 card's mixed recipe
+# (int8 for the residual-writing wo and ffn.w2), q8 the int8 card's all-int8
+# recipe, fp8 the FP8 card's "every two-dimensional matrix weight".
+TYPES = {
+    "q4": {"wq": "q4", "wk": "q4", "wv": "q4", "wg": "q4", "w1": "q4", "w3": "q4", "wo": "q8", "w2": "q8"},
+    "q8": {p: "q8" for p in ("wq", "wk", "wv", "wg", "wo", "w1", "w2", "w3")},
+    "fp8": {p: "f8" for p in ("wq", "wk", "wv", "wg", "wo", "w1", "w2", "w3")},
+}
+
+
+def projection_of(name: str) -> str | None:
+    """The projection a tensor name belongs to (wq ... w3), or None."""
+    m = PROJ_RE.search(name)
+    return m.group(1) if m else None
+
+
+def detect(tensors: dict[str, torch.Tensor]) -> dict[str, object]:
+    """Groups raw tensors into weights by dtype: U8 + .q4_scale -> Q4Weight,
+    I8 + .q_scale -> Q8Weight, float8_e4m3fn -> F8Weight; the companions are
+    consumed; every other tensor is returned unchanged. Raises on a payload
+    whose companion is missing or has the wrong dtype or shape."""
+    out: dict[str, object] = {}
+    used = set()
+    for name, t in tensors.items():
+        if name.endswith(Q4_SCALE) or name.endswith(Q8_SCALE):
+            continue
+        if t.dtype == torch.uint8 and t.dim() == 2:
+            pairs = tensors.get(name + Q4_SCALE)
+            if pairs is None:
+                out[name] = t
+                continue
+            N, half = t.shape
+            if pairs.dtype != torch.float16 or tuple(pairs.shape) != (N, 2 * half // 32, 2):
+                raise ValueError(f"{name}{Q4_SCALE}: expected float16 [{N}, {2 * half // 32}, 2], "
+                                 f"got {pairs.dtype} {tuple(pairs.shape)}")
+            out[name] = Q4Weight(t, pairs)
+            used.add(name + Q4_SCALE)
+        elif t.dtype == torch.int8 and t.dim() == 2:
+            scale = tensors.get(name + Q8_SCALE)
+            if scale is None:
+                raise ValueError(f"{name}: int8 payload without its {Q8_SCALE} companion")
+            if scale.dtype != torch.float32 or tuple(scale.shape) != (t.shape[0],):
+                raise ValueError(f"{name}{Q8_SCALE}: expected float32 [{t.shape[0]}], "
+                                 f"got {scale.dtype} {tuple(scale.shape)}")
+            out[name] = Q8Weight(t, scale)
+            used.add(name + Q8_SCALE)
+        elif t.dtype == torch.float8_e4m3fn and t.dim() == 2:
+            out[name] = F8Weight(t.view(torch.uint8))
+        else:
+            out[name] = t
+    orphans = [n for n in tensors if (n.endswith(Q4_SCALE) or n.endswith(Q8_SCALE)) and n not in used]
+    if orphans:
+        raise ValueError(f"companion tensors without a payload: {orphans[:4]}")
+    return out
+
+
+def load(path: str, device: str = "cuda:0") -> dict[str, object]:
+    """Reads a quantized (or plain) RT-J safetensors file onto `device`."""
+    from safetensors.torch import load_file
+    tensors = load_file(path, device="cpu")
+    return {k: _to(v, device) for k, v in detect(tensors).items()}
+
+
+def _to(w, device):
+    if isinstance(w, Q4Weight):
+        return Q4Weight(w.payload.to(device), w.pairs.to(device))
+    if isinstance(w, Q8Weight):
+        return Q8Weight(w.payload.to(device), w.scale.to(device))
+    if isinstance(w, F8Weight):
+        return F8Weight(w.payload.to(device))
+    return w.to(device)
+
+
+def storage(name: str, w) -> dict[str, torch.Tensor]:
+    """The safetensors entries of one weight (host tensors)."""
+    if isinstance(w, Q4Weight):
+        return {name: w.payload.cpu(), name + Q4_SCALE: w.pairs.cpu()}
+    if isinstance(w, Q8Weight):
+        return {name: w.payload.cpu(), name + Q8_SCALE: w.scale.cpu()}
+    if isinstance(w, F8Weight):
+        return {name: w.payload.cpu().view(torch.float8_e4m3fn)}
+    return {name: w.cpu()}
+
+
+def quantize_tensors(tensors: dict[str, torch.Tensor], qtype: str, device: str = "cuda:0"):
+    """Quantizes the 2-D block projections of a float checkpoint (GPU
+    quantizers); returns the entries of the quantized file."""
+    if qtype not in TYPES:
+        raise ValueError(f"--type must be one of {sorted(TYPES)}, got {qtype!r}")
+    recipe = TYPES[qtype]
+    out: dict[str, torch.Tensor] = {}
+    for name, t in tensors.items():
+        proj = projection_of(name)
+        if proj is None or t.dim() != 2 or not t.is_floating_point():
+            out[name] = t
+            continue
+        fmt = recipe[proj]
+        W = t.to(device=device, dtype=torch.float32).contiguous()
+        if fmt == "q4" and W.shape[1] % 32:
+            raise ValueError(f"{name}: K={W.shape[1]} is not a multiple of the int4 group size 32")
+        out.update(storage(name, quantize(W, fmt)))
+    torch.cuda.synchronize()
+    return out
+
+
+def quantize_file(src: str, dst: str, qtype: str, device: str = "cuda:0") -> None:
+    from safetensors.torch import load_file, save_file
+    out = quantize_tensors(load_file(src, device="cpu"), qtype, device)
+    save_file({k: v.contiguous() for k, v in out.items()}, dst,
+              metadata=FP8_METADATA if qtype == "fp8" else None)
+
+
+def info(path: str) -> str:
+    from safetensors.torch import load_file
+    lines = []
+    for name, w in detect(load_file(path, device="cpu")).items():
+        kind = type(w).__name__ if not isinstance(w, torch.Tensor) else str(w.dtype)
+        shape = (w.N, w.K) if not isinstance(w, torch.Tensor) else tuple(w.shape)
+        lines.append(f"{name}\t{kind}\t{shape}")
+    return "\n".join(lines)
+
+
+def main(argv: list[str]) -> int:
+    if len(argv) >= 3 and argv[0] == "quantize":
+        qtype = argv[argv.index("--type") + 1] if "--type" in argv else "q4"
+        quantize_file(argv[1], argv[2], qtype)
+        return 0
+    if len(argv) == 2 and argv[0] == "info":
+        print(info(argv[1]))
+        return 0
+    print(__doc__, file=sys.stderr)
+    return 2
+
+
+if __name__ == "__main__":
+    sys.exit(main(sys.argv[1:]))
