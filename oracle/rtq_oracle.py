@@ -23,6 +23,10 @@ What is computed, and where the pages define it:
   float8_e4m3fn, no scale; W[o,i] is the E4M3 value of its code.
 * The GEMM itself: y = x . W^T with the weights dequantized first (int4 model
   card, opening paragraph: the kernels dequantize inside the GEMM).
+* The lower-precision variant of that GEMM with bf16 activations:
+  y = bf16(x) . W^T, x rounded once to the nearest bfloat16 (the upper half of
+  an IEEE binary32: 8 significant bits, the fp32 exponent range), ties to the
+  even code, the IEEE 754 default rounding.
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes of the repository):
@@ -265,6 +269,46 @@ def dequant_f8(codes) -> np.ndarray:
 
 def project_f8(x, codes) -> np.ndarray:
     return gemm_ref(x, dequant_f8(codes))
+
+
+# ----------------------------------------------------------------------------
+# bf16 activations. A bfloat16 code is the upper 16 bits of a binary32:
+# sign, 8 exponent bits (bias 127), 7 stored fraction bits; exponent 0 holds
+# the subnormals m * 2^-133. The nearest bf16 of an fp32 value lies between the
+# code that keeps its upper 16 bits (toward zero) and the next code away from
+# zero; a tie goes to the even code, and past the largest finite value
+# (2 - 2^-7) * 2^127 the next code is infinity, taken at its place 2^128.
+# ----------------------------------------------------------------------------
+def _bf16_magnitude(code) -> np.ndarray:
+    """Magnitude of bf16 codes (no sign bit) in fp64; code 0x7F80 -> 2^128."""
+    c = np.asarray(code, dtype=np.int64)
+    e = (c >> 7) & 0xFF
+    m = (c & 0x7F).astype(np.float64)
+    return np.where(e == 0, m * 2.0 ** -133, (1.0 + m / 128.0) * np.exp2(e.astype(np.float64) - 127.0))
+
+
+def round_bf16(x) -> np.ndarray:
+    """fp32 x -> the nearest bf16 value (returned as fp32), ties to the even
+    code; infinities and NaN pass through, the sign is kept."""
+    x = np.asarray(x, dtype=np.float32)
+    bits = x.view(np.uint32).astype(np.int64)
+    sign = bits >> 31
+    lo = (bits & 0x7FFFFFFF) >> 16          # toward zero
+    hi = lo + 1                             # away from zero
+    a = np.abs(x.astype(np.float64))
+    finite = np.isfinite(x)
+    lo_f, hi_f = np.where(finite, lo, 0), np.where(finite, hi, 1)
+    d_lo = a - _bf16_magnitude(lo_f)
+    d_hi = _bf16_magnitude(hi_f) - a
+    code = np.where((d_hi < d_lo) | ((d_hi == d_lo) & (hi_f % 2 == 0)), hi_f, lo_f)
+    out = ((sign << 15) | code) << 16
+    out = out.astype(np.uint32).view(np.float32)
+    return np.where(finite, out, x)
+
+
+def project_bf16(fmt: str, x, payload, scale) -> np.ndarray:
+    """y = bf16(x) . dequant(W)^T in fp64: the bf16-activation variant."""
+    return project(fmt, round_bf16(x), payload, scale)
 
 
 def quantize(W: np.ndarray, fmt: str):

@@ -12,6 +12,7 @@ from fractions import Fraction
 # (significand bits incl. hidden bit, minimum normal exponent, maximum exponent)
 F32 = (24, -126, 127)
 F16 = (11, -14, 15)
+BF16 = (8, -126, 127)
 
 
 def _floor_log2(a: Fraction) -> int:

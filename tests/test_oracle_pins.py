@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import synth
-from tests.exact import F16, F32, rint_half_even, round_rne
+from tests.exact import BF16, F16, F32, rint_half_even, round_rne
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -330,10 +330,57 @@ def pin_f8_nearest(o):
 PINS_F8 = [pin_f8_golden, pin_f8_decode_rational, pin_f8_roundtrip, pin_f8_nearest]
 
 
+# ---- bf16 activations (the lower-precision variant y = bf16(x) . W^T) ----
+def _bits(v):
+    return int(np.array([v], dtype=np.float32).view(np.uint32)[0])
+
+
+def pin_bf16_golden(o):
+    for line in _rows("bf16_examples.txt"):
+        a, b = (int(t.strip(), 16) for t in line.split(";"))
+        x = np.array([a], dtype=np.uint32).view(np.float32)
+        got = _bits(o.round_bf16(x)[0])
+        assert got == b, (line, hex(got))
+
+
+def pin_bf16_nearest(o):
+    """Exact rational rounding (IEEE definition on Fractions) of random fp32
+    values over the whole exponent range, and of constructed midpoints."""
+    rng = np.random.default_rng(17)
+    bits = rng.integers(0, 2 ** 32, size=3000, dtype=np.uint64).astype(np.uint32)
+    bits = bits[((bits >> 23) & 0xFF) != 0xFF]                     # finite only
+    mids = (rng.integers(0, 2 ** 16, size=400, dtype=np.uint64).astype(np.uint32) << 16) | 0x8000
+    mids = mids[((mids >> 23) & 0xFF) != 0xFF]
+    x = np.concatenate([bits, mids]).view(np.float32)
+    got = o.round_bf16(x)
+    for v, g in zip(x.tolist(), got.tolist()):
+        ref = round_rne(Fraction(v), BF16)
+        assert g == ref and math.copysign(1.0, g) == math.copysign(1.0, v), (v, g, ref)
+
+
+def pin_project_bf16(o):
+    """y = bf16(x) . W^T: a triple loop over the exactly rounded x (Fraction
+    rounding, not the oracle's), with the weights of the int8 closed form."""
+    rng = np.random.default_rng(19)
+    x = rng.standard_normal((3, 40)).astype(np.float32)
+    q = rng.integers(-127, 128, size=(5, 40)).astype(np.int8)
+    scale = (rng.random(5) * 0.01 + 0.001).astype(np.float32)
+    xr = np.array([[round_rne(Fraction(float(v)), BF16) for v in row] for row in x])
+    # the int8 closed form, single-rounded to fp32 (each q*scale is exact in fp64)
+    W = (q.astype(np.float64) * scale.astype(np.float64)[:, None]).astype(np.float32).astype(np.float64)
+    ref = _loop_gemm(xr, W)
+    got = o.project_bf16("q8", x, q, scale)
+    assert np.allclose(got, ref, rtol=1e-12, atol=0), np.abs(got - ref).max()
+    assert not np.allclose(got, _loop_gemm(x.astype(np.float64), W), rtol=1e-6, atol=0)
+
+
+PINS_BF16 = [pin_bf16_golden, pin_bf16_nearest, pin_project_bf16]
+
+
 PINS = [pin_nibble_golden, pin_pack_roundtrip, pin_q4_dequant_golden, pin_q4_dequant_identity_probe,
         pin_q4_dequant_rational, pin_q8_dequant_rational, pin_q8_golden, pin_q8_closed_form,
         pin_q4_recon_bound, pin_q4_grid_roundtrip, pin_q4_clip_argmin, pin_q4_degenerate,
-        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8
+        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8 + PINS_BF16
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -498,6 +545,33 @@ def _mut_project_q4_transposed(x, payload, pairs):
     return np.asarray(x, np.float64) @ W.astype(np.float64)[:, ::-1].T
 
 
+def test_bf16_rounding_agrees_with_torch_cast():
+    """The oracle's bf16 rounding (written from the format's definition) gives
+    the same bits as PyTorch's float32 -> bfloat16 cast."""
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(23)
+    x = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    x = x[((x >> 23) & 0xFF) != 0xFF].view(np.float32)
+    x = np.concatenate([x, (rng.standard_normal(100000)).astype(np.float32),
+                        np.array([np.inf, -np.inf, 0.0, -0.0], dtype=np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    assert np.array_equal(oracle.round_bf16(x).view(np.uint32), ref.view(np.uint32))
+
+
+def _mut_round_bf16_truncate(x):
+    b = np.asarray(x, dtype=np.float32).view(np.uint32) & np.uint32(0xFFFF0000)
+    return b.view(np.float32)
+
+
+def _mut_round_bf16_ties_away(x):
+    b = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    return (((b + 0x8000) & 0xFFFF0000).astype(np.uint32)).view(np.float32)
+
+
+def _mut_project_bf16_unrounded(fmt, x, payload, scale):
+    return oracle.project(fmt, x, payload, scale)
+
+
 def _mut_decode_f8_bias8(codes):
     return oracle.decode_f8(codes) / 2.0
 
@@ -525,6 +599,9 @@ def _mut_quantize_f8_saturate(W):
 
 
 MUTANTS = {
+    "round_bf16_truncate": {"round_bf16": _mut_round_bf16_truncate},
+    "round_bf16_ties_away": {"round_bf16": _mut_round_bf16_ties_away},
+    "project_bf16_unrounded": {"project_bf16": _mut_project_bf16_unrounded},
     "decode_f8_bias8": {"decode_f8": _mut_decode_f8_bias8},
     "decode_f8_no_subnormals": {"decode_f8": _mut_decode_f8_no_subnormals},
     "quantize_f8_ties_away": {"quantize_f8": _mut_quantize_f8_ties_away},
