@@ -15,7 +15,8 @@ Workloads (synthetic, seeded; shapes of the "Backends" page, section "Meta"):
 
 Prints one JSON line. `value` is dequant-GEMM TFLOP/s (2*M*N*K per
 projection) on the m80 workload; the m65536 figures ride along under
-"m65536".
+"m65536". The lower-precision bf16-activation mode (x rounded to bf16) is
+timed on both workloads and reported apart, under "bf16_activation_path".
 """
 from __future__ import annotations
 
@@ -35,8 +36,10 @@ PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix
 PEAK_BF16_MFMA_TFLOPS = 2516.6     # MI355X dense bf16 matrix
 WEIGHT_SETS = 16
 KERNELS = {  # main GEMM kernel of each (math, workload), as rocprofv3 names it
-    ("split", "m80"): "split_grouped_kernel<5>",
-    ("split", "m65536"): "split_gemm_kernel<1|2>",
+    ("split", "m80"): "split_grouped_kernel<5, 3>",
+    ("split", "m65536"): "split_gemm_kernel<1|2, 3>",
+    ("bf16", "m80"): "split_grouped_kernel<5, 1>",
+    ("bf16", "m65536"): "split_gemm_kernel<1|2, 1>",
     ("fp32", "m80"): "grouped_stream_kernel<5>",
     ("fp32", "m65536"): "gemm_kernel<1|2,2,2,4,4>",
 }
@@ -54,8 +57,11 @@ def parse():
     ap.add_argument("--recipe", choices=["mixed", "all_q8", "all_f8"], default="mixed",
                     help="weight formats: the int4 card's mixed int4/int8 recipe (default), the int8 card's "
                          "all-int8 recipe, or the FP8 card's all-E4M3 weights")
-    ap.add_argument("--math", choices=["split", "fp32"], default="split",
-                    help="GEMM arithmetic: exact bf16x3 split on the bf16 MFMA (default) or fp32 MFMA")
+    ap.add_argument("--math", choices=["split", "fp32", "bf16"], default="split",
+                    help="GEMM arithmetic: exact bf16x3 split on the bf16 MFMA (default), fp32 MFMA, or "
+                         "activations rounded to bf16 (lower precision)")
+    ap.add_argument("--no-bf16-path", action="store_true",
+                    help="skip the separately reported bf16-activation timing")
     ap.add_argument("--compare-fp32", action="store_true",
                     help="also time the fp32-MFMA path (few steps) and report it alongside")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -179,6 +185,8 @@ def roofline(res, math, workload, recipe="mixed"):
     ach = res["kernel_tflops"]
     if math == "split":
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
+    elif math == "bf16":
+        peak, issued = PEAK_BF16_MFMA_TFLOPS, 1
     else:
         peak, issued = PEAK_FP32_MFMA_TFLOPS, 1
     tr = load_traffic(workload, math, recipe)
@@ -245,7 +253,8 @@ def main():
     import weight_only_quantized_rtq_amd as rtq
     rtq.load_library()
     torch.cuda.init()
-    rtq.set_math(rtq.MATH_SPLIT_BF16 if args.math == "split" else rtq.MATH_FP32_MFMA)
+    modes = {"split": rtq.MATH_SPLIT_BF16, "fp32": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16}
+    rtq.set_math(modes[args.math])
     out = {}
     if args.workload in ("m80", "both"):
         out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup, args.recipe)
@@ -258,6 +267,17 @@ def main():
             r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1, args.recipe)
             fp32[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                         "roofline": roofline(r, "fp32", wl, args.recipe)}
+        rtq.set_math(rtq.MATH_SPLIT_BF16)
+    bf16 = {}
+    if not args.no_bf16_path and args.math == "split":
+        rtq.set_math(rtq.MATH_BF16)
+        for wl in out:
+            st, wu = (args.steps, args.warmup) if wl == "m80" else (args.steps_large, args.warmup_large)
+            r = measure(torch, rtq, synth, wl, st, wu, args.recipe)
+            bf16[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
+                        "weight_gbs": round(r["weight_gbs"], 2),
+                        "weight_hbm_frac": round(r["weight_gbs"] / PEAK_HBM_GBS, 5), "steps": r["steps"],
+                        "roofline": roofline(r, "bf16", wl, args.recipe)}
         rtq.set_math(rtq.MATH_SPLIT_BF16)
 
     prim_name = "m80" if "m80" in out else "m65536"
@@ -278,14 +298,16 @@ def main():
         "warmup": args.warmup if prim_name == "m80" else args.warmup_large,
         "ms_per_step": round(prim["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16x3/f32" if args.math == "split" else "f32",
+        "dtype": {"split": "bf16x3/f32", "fp32": "f32", "bf16": "bf16/f32"}[args.math],
         "data": "synthetic",
         "config": {"workload": cfg, "M": prim["M"], "n_blocks": synth.NUM_BLOCKS,
                    "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": {"mixed": "mixed int4/int8", "all_q8": "all int8",
                                                                                "all_f8": "all FP8 E4M3"}[args.recipe],
                    "d_model": synth.D_MODEL, "d_ff": synth.D_FF,
-                   "math": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation"
-                           if args.math == "split" else "fp32 MFMA on dequantized weights"},
+                   "math": {"split": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation",
+                            "fp32": "fp32 MFMA on dequantized weights",
+                            "bf16": "activations rounded to bf16 (lower precision), exact weight products, "
+                                    "fp32 accumulation"}[args.math]},
         "weight_gbs": round(prim["weight_gbs"], 2),
         "weight_hbm_frac": round(prim["weight_gbs"] / PEAK_HBM_GBS, 5),
         "roofline": roofline(prim, args.math, prim_name, args.recipe),
@@ -299,6 +321,11 @@ def main():
                     "roofline": roofline(r, args.math, wl, args.recipe)}
     if fp32:
         line["fp32_mfma_path"] = fp32
+    if bf16:
+        line["bf16_activation_path"] = {
+            "note": "x rounded to the nearest bf16 (lower precision: 3e-3 bar, not 1e-5), one bf16 MFMA per "
+                    "product; reported apart from the fp32-activation figures above",
+            **bf16}
     if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
     print(json.dumps(line), flush=True)

@@ -151,9 +151,17 @@ rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K,
  *   Same accuracy class as an fp32 GEMM (fp32 accumulation of exact products).
  * RTQ_MATH_FP32_MFMA: the weights are dequantized to fp32 while staging and the
  *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction.
- * Both satisfy the same parity bar against the fp64 reference. Calls already
- * enqueued are not affected. Returns RTQ_ERR_FORMAT for an unknown mode. */
-enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1 };
+ * Both satisfy the same parity bar against the fp64 reference.
+ * RTQ_MATH_BF16: bf16 activations. Each x is rounded once to the nearest bf16
+ *   (ties to even) and takes the place of the three limbs: y = bf16(x) . W^T
+ *   with the exact weight side and fp32 accumulation of the first mode, a third
+ *   of its matrix work. The result carries the rounding of x (about 2^-9
+ *   relative per element), so it is a lower-precision mode. Shapes the split
+ *   path does not take (int8/FP8 K not a multiple of 32, x or payload not
+ *   16-byte aligned, N*K >= 2^32) run on the fp32 kernels in every mode.
+ * Calls already enqueued are not affected. Returns RTQ_ERR_FORMAT for an
+ * unknown mode. */
+enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2 };
 rtq_status rtq_set_math(int32_t mode);
 int32_t rtq_get_math(void);
 

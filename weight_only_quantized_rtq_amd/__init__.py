@@ -44,7 +44,7 @@ EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rt
            "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
-MATH_SPLIT_BF16, MATH_FP32_MFMA = 0, 1
+MATH_SPLIT_BF16, MATH_FP32_MFMA, MATH_BF16 = 0, 1, 2
 
 
 class RtqError(RuntimeError):
@@ -114,7 +114,8 @@ def version() -> str:
 
 
 def set_math(mode: int) -> None:
-    """MATH_SPLIT_BF16 (default) or MATH_FP32_MFMA for the GEMM entry points (rtq_set_math)."""
+    """MATH_SPLIT_BF16 (default, exact fp32 activations), MATH_FP32_MFMA, or
+    MATH_BF16 (activations rounded to bf16) for the GEMM entry points (rtq_set_math)."""
     _check(load_library().rtq_set_math(mode))
 
 

@@ -536,15 +536,17 @@ bool grouped_ok(const ProjTask& t) {
 hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
     const TileArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
     const bool safe = !grouped_ok(t);
-    if (!safe && math_mode() == kMathSplitBf16 && split_ok(t)) return launch_split(&t, 1, M, stream);
+    const int nl = split_limbs(math_mode());
+    if (!safe && nl && split_ok(t)) return launch_split(&t, 1, M, nl, stream);
     if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
     if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
     if (t.fmt == kFmtQ8) return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
     return safe ? launch_one<kFmtF8, true>(a, stream) : launch_one<kFmtF8, false>(a, stream);
 }
 
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
-    if (math_mode() == kMathSplitBf16) return launch_split(tasks, count, M, stream);
+namespace {
+
+hipError_t launch_grouped_fp32(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
     if (M > kSmallMaxM) {
         // Many row tiles: every projection alone already fills the GPU; one
         // launch each keeps the XCD-contiguous tile order.
@@ -612,6 +614,26 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
         if (e != hipSuccess) return e;
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
+    const int nl = split_limbs(math_mode());
+    if (!nl) return launch_grouped_fp32(tasks, count, M, stream);
+    // Split path for every task it takes; the rest (weights past 32-bit
+    // offsets) run on the fp32 kernels.
+    ProjTask split[8 * 64], rest[8 * 64];
+    int n_split = 0, n_rest = 0;
+    for (int i = 0; i < count; ++i) {
+        if (split_ok(tasks[i])) split[n_split++] = tasks[i];
+        else rest[n_rest++] = tasks[i];
+    }
+    if (n_split) {
+        const hipError_t e = launch_split(split, n_split, M, nl, stream);
+        if (e != hipSuccess) return e;
+    }
+    return n_rest ? launch_grouped_fp32(rest, n_rest, M, stream) : hipSuccess;
 }
 
 }  // namespace rtq

@@ -20,6 +20,11 @@
 // VALU; the min term is a K/32-long contraction run on the fp32 matrix cores
 // (v_mfma_f32_16x16x4_f32, four groups per instruction).
 //
+// bf16 activations (one limb). The same kernels with NL = 1 take x rounded to
+// the nearest bf16 (ties to even) as their only limb: one MFMA per group and
+// tile instead of three, y = bf16(x) . W^T with the same exact weight side and
+// fp32 accumulation; the group sums X_g are those of the rounded values.
+//
 // Data movement.
 //  1. A pre-pass splits every distinct activation once into a limb image in a
 //     device workspace (three bf16 planes in MFMA operand order with an XOR
@@ -113,19 +118,27 @@ __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
                                                    0, 0, 0);
 }
 
+// Nearest bf16 of two fp32 values (ties to even), packed: a low, b high.
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 // ---------------------------------------------------------------------------
-// Limb image of one activation x [M][K] (G = K/32 groups, RB row blocks of 16,
-// RB*16 >= M; rows >= M are zero):
-//   block (g, rb) of 3 KB at byte ((g*RB + rb)*3 + limb) * 1024, limb 0 = x1
-//   (high), 1 = x2, 2 = x3; inside a limb, row r (0..15) and 16-byte chunk c
-//   (k = 8c..8c+7 of the group) sit at (r*4 + (c ^ ((r>>2)&3))) * 16;
+// Limb image of one activation x [M][K] with NL limbs (G = K/32 groups, RB row
+// blocks of 16, RB*16 >= M; rows >= M are zero):
+//   block (g, rb) of NL KB at byte ((g*RB + rb)*NL + limb) * 1024; with NL = 3
+//   limb 0 = x1 (high), 1 = x2, 2 = x3, with NL = 1 the bf16-rounded x; inside
+//   a limb, row r (0..15) and 16-byte chunk c (k = 8c..8c+7 of the group) sit
+//   at (r*4 + (c ^ ((r>>2)&3))) * 16;
 //   then the group sums X[g][row] (fp32, RB*16 rows per group).
 // For a fixed group the RB blocks are contiguous, so a row block of BM rows is
-// one contiguous run of BM/16 * 3 KB.
+// one contiguous run of BM/16 * NL KB.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int64_t image_plane_bytes(int G, int RB) { return int64_t(G) * RB * 3072; }
-__host__ __device__ inline int64_t image_bytes(int G, int RB) {
-    return image_plane_bytes(G, RB) + int64_t(G) * RB * 16 * 4;
+__host__ __device__ inline int64_t image_plane_bytes(int G, int RB, int NL) { return int64_t(G) * RB * 1024 * NL; }
+__host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
+    return image_plane_bytes(G, RB, NL) + int64_t(G) * RB * 16 * 4;
 }
 __device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
@@ -146,6 +159,7 @@ static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB
 // One thread per (row, 8-wide chunk). A wave covers one 16-row block of one
 // group (4 threads per row), so each limb it writes is one contiguous 1 KB run,
 // and the group sum of a row is two shuffles in a fixed order.
+template <int NL>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     const int b = blockIdx.x;
     const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
@@ -171,8 +185,17 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
         for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
     uint32_t h[4], m[4], l[4];
+    if constexpr (NL == 3) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], h[j], m[j], l[j]);
+        for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], h[j], m[j], l[j]);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            h[j] = bf16x2_rne(v[2 * j], v[2 * j + 1]);
+            v[2 * j] = bitsf(h[j] << 16);               // the group sum is over the rounded values
+            v[2 * j + 1] = bitsf(h[j] & 0xffff0000u);
+        }
+    }
     float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
     const float s1 = __shfl_xor(s, 1, 64);
     s = (c & 1) ? s1 + s : s + s1;                  // chunks (0+1), (2+3)
@@ -180,12 +203,14 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
     s = (c & 2) ? s2 + s : s + s2;                  // (0+1) + (2+3)
     if (!live) return;
     unsigned char* img = p.img[i];
-    unsigned char* blk = img + blk_id * 3072 + swz(r, c) * 16;
+    unsigned char* blk = img + blk_id * (NL * 1024) + swz(r, c) * 16;
     *reinterpret_cast<uint4*>(blk + 0) = make_uint4(h[0], h[1], h[2], h[3]);
-    *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(m[0], m[1], m[2], m[3]);
-    *reinterpret_cast<uint4*>(blk + 2048) = make_uint4(l[0], l[1], l[2], l[3]);
+    if constexpr (NL == 3) {
+        *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(m[0], m[1], m[2], m[3]);
+        *reinterpret_cast<uint4*>(blk + 2048) = make_uint4(l[0], l[1], l[2], l[3]);
+    }
     if (c == 0) {
-        float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB));
+        float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, NL));
         X[static_cast<int64_t>(g) * RB * 16 + row] = s;
     }
 }
@@ -211,10 +236,10 @@ constexpr int kChunk = 2;         // steps per weight chunk when the weights str
 // the wave's TN*16 rows for kChunk steps: int4 as 16-byte code records (one
 // per row and group) plus 4-byte (scale, min) records, int8 as two 16-byte
 // halves per row and group (TN * 1024 bytes either way).
-template <int BM, int TN = 1, int PDW = 0>
+template <int BM, int TN = 1, int PDW = 0, int NL = 3>
 struct Lds {
     static constexpr int NSTAGE = PDW > 0 ? PDW + 1 : kStages;    // x stages
-    static constexpr int STAGE = (BM / 16) * 3072;
+    static constexpr int STAGE = (BM / 16) * NL * 1024;
     static constexpr int XRING = NSTAGE * STAGE;
     // Group-sum slot: waves 0 and 2 copy rows 0..63, waves 1 and 3 rows
     // XSLOT-64 .. XSLOT-1 (the same rows twice, identical bytes).
@@ -222,7 +247,7 @@ struct Lds {
     static constexpr int WRING = XRING + kRing * XSLOT * 4;
     static constexpr int WCHUNK = TN * 1024;
     static constexpr int TOTAL = WRING + (PDW > 0 ? 2 * 4 * WCHUNK : 0);
-    static constexpr int COPIES = (BM / 16) * 3;                   // 1 KB copies per stage
+    static constexpr int COPIES = (BM / 16) * NL;                  // 1 KB copies per stage
     static constexpr int PER_WAVE = (COPIES + 3) / 4;
     static_assert(BM <= XSLOT, "group-sum slot holds every row of the tile");
 };
@@ -255,10 +280,11 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
 // Weights: with PDW == 0 each wave loads its codes and pairs into registers one
 // step ahead (enough when they come from L2); with PDW > 0 they are copied by
 // DMA into a per-wave LDS ring PDW steps ahead (for weights streamed from HBM).
-template <int FMT, int WM, int WN, int TM, int TN, int PDW = 0>
+template <int FMT, int WM, int WN, int TM, int TN, int PDW, int NL>
 __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
-    using L = Lds<BM, TN, PDW>;
+    using L = Lds<BM, TN, PDW, NL>;
+    static_assert(NL == 1 || NL == 3, "limbs");
     static_assert(WM * WN == 4, "four waves");
     static_assert(PDW <= 3, "prefetch depth");
     const int tid = threadIdx.x;
@@ -277,13 +303,13 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 
     // ---- async stage copies: 1 KB per wave instruction, all waves issue the same count.
     //      Every copy is a uniform base plus a fixed per-lane byte offset. ----
-    const unsigned char* xsum = a.img + image_plane_bytes(G, RB);
+    const unsigned char* xsum = a.img + image_plane_bytes(G, RB, NL);
     const uint32_t lane16 = static_cast<uint32_t>(lane) * 16u;
     const uint32_t xrow4 = static_cast<uint32_t>(min(m0 + (wave & 1) * (L::XSLOT - 64) + lane, RB * 16 - 1)) * 4u;
     auto group_of = [&](int i) { const int g = rot + i; return a.g_lo + (g >= GS ? g - GS : g); };
     auto stage_copy = [&](int i) {
         const int g = group_of(i);
-        const unsigned char* src = a.img + (static_cast<int64_t>(g) * RB + rb0) * 3072;
+        const unsigned char* src = a.img + (static_cast<int64_t>(g) * RB + rb0) * (NL * 1024);
         unsigned char* dst = smem + (i % L::NSTAGE) * L::STAGE;
 #pragma unroll
         for (int j = 0; j < L::PER_WAVE; ++j) {
@@ -439,15 +465,21 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-            const unsigned char* blk = base + (wm * TM + tm) * 3072 + aoff;
+            const unsigned char* blk = base + (wm * TM + tm) * (NL * 1024) + aoff;
             const u32x4 xh = *reinterpret_cast<const u32x4*>(blk);
-            const u32x4 xm = *reinterpret_cast<const u32x4*>(blk + 1024);
-            const u32x4 xl = *reinterpret_cast<const u32x4*>(blk + 2048);
+            u32x4 xm = {}, xl = {};
+            if constexpr (NL == 3) {
+                xm = *reinterpret_cast<const u32x4*>(blk + 1024);
+                xl = *reinterpret_cast<const u32x4*>(blk + 2048);
+            }
             if constexpr (FMT == kFmtQ4) {
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
-                    floatx4 p = mfma_bf16(xl, b[tn], floatx4{0.f, 0.f, 0.f, 0.f});
-                    p = mfma_bf16(xm, b[tn], p);
+                    floatx4 p = floatx4{0.f, 0.f, 0.f, 0.f};
+                    if constexpr (NL == 3) {
+                        p = mfma_bf16(xl, b[tn], p);
+                        p = mfma_bf16(xm, b[tn], p);
+                    }
                     p = mfma_bf16(xh, b[tn], p);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[tm][tn][e] = fmaf(s[tn], p[e], acc[tm][tn][e]);
@@ -455,8 +487,10 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             } else {
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
-                    acc[tm][tn] = mfma_bf16(xl, b[tn], acc[tm][tn]);
-                    acc[tm][tn] = mfma_bf16(xm, b[tn], acc[tm][tn]);
+                    if constexpr (NL == 3) {
+                        acc[tm][tn] = mfma_bf16(xl, b[tn], acc[tm][tn]);
+                        acc[tm][tn] = mfma_bf16(xm, b[tn], acc[tm][tn]);
+                    }
                     acc[tm][tn] = mfma_bf16(xh, b[tn], acc[tm][tn]);
                 }
             }
@@ -572,12 +606,12 @@ constexpr int kLWM = 1, kLWN = 4, kLTM = 8, kLTN = 2;
 constexpr int kLBM = kLWM * kLTM * 16;
 constexpr int kLBN = kLWN * kLTN * 16;
 
-template <int FMT>
+template <int FMT, int NL>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, 1, 0, NL>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int nt = w % tiles_n;
-    split_tile<FMT, kLWM, kLWN, kLTM, kLTN>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
+    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, 0, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
 // Small M (<= 80): one row block of TM*16 rows; 4 waves side by side along N,
@@ -614,9 +648,9 @@ __host__ __device__ inline int split_chunks(int K) {
     return (G + kChunkGroups - 1) / kChunkGroups;
 }
 
-template <int TM>
+template <int TM, int NL>
 __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, kSmallPDW>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, kSmallPDW, NL>::TOTAL];
     // Find this workgroup's projection: tiles are numbered projection by
     // projection, (column block, K chunk) within one.
     const int w = blockIdx.x;
@@ -632,11 +666,11 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     const SplitArgs a{g.ws + g.img_off[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo};
     const int rot = cb % (g_hi - g_lo);
     if (g.fmt[i] == kFmtQ4)
-        split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
     else if (g.fmt[i] == kFmtQ8)
-        split_tile<kFmtQ8, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ8, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
     else
-        split_tile<kFmtF8, 1, 4, TM, 4, kSmallPDW>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtF8, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
 }
 
 // Sums the K-chunk partials of split projections in chunk order.
@@ -670,7 +704,7 @@ struct Input {
     int64_t offset;     // of its image in the workspace
 };
 
-hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB, hipStream_t stream) {
+hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB, int NL, hipStream_t stream) {
     int done = 0;
     while (done < n_in) {
         PrepArgs p{};
@@ -689,7 +723,10 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
         }
         p.block_begin[p.count] = blocks;
         seg_fill_coarse(p.block_begin, p.block_coarse, p.count);
-        prep_kernel<<<blocks, 256, 0, stream>>>(p);
+        if (NL == 1)
+            prep_kernel<1><<<blocks, 256, 0, stream>>>(p);
+        else
+            prep_kernel<3><<<blocks, 256, 0, stream>>>(p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -716,9 +753,32 @@ bool split_ok(const ProjTask& t) {
            (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0 && int64_t(t.N) * t.K < (int64_t(1) << 32);
 }
 
+template <int NL>
+void launch_grouped_tm(int tm, int tiles, const SplitGroupArgs& g, hipStream_t stream) {
+    switch (tm) {
+        case 1: split_grouped_kernel<1, NL><<<tiles, 256, 0, stream>>>(g); break;
+        case 2: split_grouped_kernel<2, NL><<<tiles, 256, 0, stream>>>(g); break;
+        case 3: split_grouped_kernel<3, NL><<<tiles, 256, 0, stream>>>(g); break;
+        case 4: split_grouped_kernel<4, NL><<<tiles, 256, 0, stream>>>(g); break;
+        default: split_grouped_kernel<5, NL><<<tiles, 256, 0, stream>>>(g); break;
+    }
+}
+
+template <int NL>
+void launch_large(int fmt, int blocks, const SplitArgs& a, int tn, hipStream_t stream) {
+    if (fmt == kFmtQ4)
+        split_gemm_kernel<kFmtQ4, NL><<<blocks, 256, 0, stream>>>(a, tn);
+    else if (fmt == kFmtQ8)
+        split_gemm_kernel<kFmtQ8, NL><<<blocks, 256, 0, stream>>>(a, tn);
+    else
+        split_gemm_kernel<kFmtF8, NL><<<blocks, 256, 0, stream>>>(a, tn);
+}
+
 // All projections (sharing M) of this call: split every distinct input once into
-// a stream-ordered workspace, run the GEMMs, release the workspace.
-hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream_t stream) {
+// a stream-ordered workspace, run the GEMMs, release the workspace. NL = 3:
+// exact three-limb split; NL = 1: x rounded to bf16.
+hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream) {
+    if (NL != 1 && NL != 3) return hipErrorInvalidValue;
     const int M = static_cast<int>(M64);
     const int tm_small = (M + 15) / 16;
     // The grouped small-M launch addresses the limb images by 32-bit offsets;
@@ -741,7 +801,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             if (found < 0) {
                 found = n_in++;
                 inputs[found] = Input{tasks[i].x, tasks[i].K, ws_bytes};
-                ws_bytes += (image_bytes(tasks[i].K / 32, RB) + 255) / 256 * 256;
+                ws_bytes += (image_bytes(tasks[i].K / 32, RB, NL) + 255) / 256 * 256;
             }
             img_of[i] = found;
         }
@@ -764,7 +824,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
     hipError_t e = hipMallocAsync(&ws, static_cast<size_t>(ws_bytes), stream);
     if (e != hipSuccess) return e;
     unsigned char* wsb = static_cast<unsigned char*>(ws);
-    e = run_prep(inputs, n_in, wsb, M, RB, stream);
+    e = run_prep(inputs, n_in, wsb, M, RB, NL, stream);
 
     if (e == hipSuccess && small) {
         int order[8 * 64];
@@ -816,13 +876,10 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             }
             seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
             const int mark = timing_begin(stream);
-            switch (tm_small) {
-                case 1: split_grouped_kernel<1><<<tiles, 256, 0, stream>>>(g); break;
-                case 2: split_grouped_kernel<2><<<tiles, 256, 0, stream>>>(g); break;
-                case 3: split_grouped_kernel<3><<<tiles, 256, 0, stream>>>(g); break;
-                case 4: split_grouped_kernel<4><<<tiles, 256, 0, stream>>>(g); break;
-                default: split_grouped_kernel<5><<<tiles, 256, 0, stream>>>(g); break;
-            }
+            if (NL == 1)
+                launch_grouped_tm<1>(tm_small, tiles, g, stream);
+            else
+                launch_grouped_tm<3>(tm_small, tiles, g, stream);
             timing_end(mark, stream);
             e = hipGetLastError();
             if (e == hipSuccess && red.count) {
@@ -839,12 +896,10 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, hipStream
             const int tn = (t.N + kLBN - 1) / kLBN;
             const int tmb = (M + kLBM - 1) / kLBM;
             const int mark = timing_begin(stream);
-            if (t.fmt == kFmtQ4)
-                split_gemm_kernel<kFmtQ4><<<tmb * tn, 256, 0, stream>>>(a, tn);
-            else if (t.fmt == kFmtQ8)
-                split_gemm_kernel<kFmtQ8><<<tmb * tn, 256, 0, stream>>>(a, tn);
+            if (NL == 1)
+                launch_large<1>(t.fmt, tmb * tn, a, tn, stream);
             else
-                split_gemm_kernel<kFmtF8><<<tmb * tn, 256, 0, stream>>>(a, tn);
+                launch_large<3>(t.fmt, tmb * tn, a, tn, stream);
             timing_end(mark, stream);
             e = hipGetLastError();
         }
