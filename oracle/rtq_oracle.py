@@ -23,6 +23,9 @@ What is computed, and where the pages define it:
   float8_e4m3fn, no scale; W[o,i] is the E4M3 value of its code.
 * The GEMM itself: y = x . W^T with the weights dequantized first (int4 model
   card, opening paragraph: the kernels dequantize inside the GEMM).
+* The projection bias: the checkpoints keep biases in fp32 next to the
+  quantized matrices (int4 model card, "Quantization format"), and a
+  projection with a bias computes y = x . W^T + b, b[o] added to every row;
 * The lower-precision variant of that GEMM with bf16 activations:
   y = bf16(x) . W^T, x rounded once to the nearest bfloat16 (the upper half of
   an IEEE binary32: 8 significant bits, the fp32 exponent range), ties to the
@@ -309,6 +312,12 @@ def round_bf16(x) -> np.ndarray:
 def project_bf16(fmt: str, x, payload, scale) -> np.ndarray:
     """y = bf16(x) . dequant(W)^T in fp64: the bf16-activation variant."""
     return project(fmt, round_bf16(x), payload, scale)
+
+
+def project_bias(fmt: str, x, payload, scale, bias) -> np.ndarray:
+    """y = x . dequant(W)^T + b in fp64, b[o] added to column o of every row."""
+    y = project(fmt, x, payload, scale)
+    return y + np.asarray(bias, dtype=np.float32).astype(np.float64)[None, :]
 
 
 def quantize(W: np.ndarray, fmt: str):

@@ -377,10 +377,36 @@ def pin_project_bf16(o):
 PINS_BF16 = [pin_bf16_golden, pin_bf16_nearest, pin_project_bf16]
 
 
+def pin_project_bias(o):
+    """y = x . W^T + b: a triple loop with the bias added per output column, on
+    an exactly representable case (small integers), and b alone for x = 0."""
+    rng = np.random.default_rng(29)
+    x = rng.integers(-3, 4, size=(4, 64)).astype(np.float32)
+    payload = rng.integers(0, 256, size=(6, 32), dtype=np.uint8)
+    pairs = np.zeros((6, 2, 2), dtype=np.float16)
+    pairs[..., 0] = 0.5
+    pairs[..., 1] = -4.0
+    bias = np.array([0.25, -1.5, 3.0, 0.0, -0.125, 7.0], dtype=np.float32)
+    got = o.project_bias("q4", x, payload, pairs, bias)
+    for i in range(4):
+        for j in range(6):
+            acc = Fraction(0)
+            for k in range(64):
+                byte = int(payload[j, k // 2])
+                code = byte & 15 if k % 2 == 0 else byte >> 4
+                acc += int(x[i, k]) * (Fraction(code, 2) - 4)
+            assert Fraction(float(got[i, j])) == acc + Fraction(float(bias[j])), (i, j)
+    zero = o.project_bias("q4", np.zeros((3, 64), dtype=np.float32), payload, pairs, bias)
+    assert np.array_equal(zero, np.broadcast_to(bias.astype(np.float64), (3, 6)))
+
+
+PINS_BIAS = [pin_project_bias]
+
+
 PINS = [pin_nibble_golden, pin_pack_roundtrip, pin_q4_dequant_golden, pin_q4_dequant_identity_probe,
         pin_q4_dequant_rational, pin_q8_dequant_rational, pin_q8_golden, pin_q8_closed_form,
         pin_q4_recon_bound, pin_q4_grid_roundtrip, pin_q4_clip_argmin, pin_q4_degenerate,
-        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8 + PINS_BF16
+        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8 + PINS_BF16 + PINS_BIAS
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -572,6 +598,16 @@ def _mut_project_bf16_unrounded(fmt, x, payload, scale):
     return oracle.project(fmt, x, payload, scale)
 
 
+def _mut_project_bias_rows(fmt, x, payload, scale, bias):
+    y = oracle.project(fmt, x, payload, scale)
+    b = np.asarray(bias, dtype=np.float64)
+    return y + np.resize(b, y.shape[0])[:, None]
+
+
+def _mut_project_bias_dropped(fmt, x, payload, scale, bias):
+    return oracle.project(fmt, x, payload, scale)
+
+
 def _mut_decode_f8_bias8(codes):
     return oracle.decode_f8(codes) / 2.0
 
@@ -599,6 +635,8 @@ def _mut_quantize_f8_saturate(W):
 
 
 MUTANTS = {
+    "project_bias_rows": {"project_bias": _mut_project_bias_rows},
+    "project_bias_dropped": {"project_bias": _mut_project_bias_dropped},
     "round_bf16_truncate": {"round_bf16": _mut_round_bf16_truncate},
     "round_bf16_ties_away": {"round_bf16": _mut_round_bf16_ties_away},
     "project_bf16_unrounded": {"project_bf16": _mut_project_bf16_unrounded},
