@@ -89,7 +89,12 @@ rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y,
  * skips the projection (for example a checkpoint without the attention gate
  * wg). `scale` is the pairs array for int4, the per-row scale for int8 and is
  * ignored (may be NULL) for FP8. Each projection reads its own
- * x [M][K] and writes its own y [M][N]; projections may share x. */
+ * x [M][K] and writes its own y [M][N]; projections may share x.
+ * `bias`, when not NULL, is an fp32 [N] vector (4-byte aligned) and the
+ * projection computes y = x . W^T + bias, bias[o] added to column o of every
+ * row: the checkpoints keep biases in fp32 beside the quantized matrices
+ * ("RT-J - int4 (Q4-style, mixed-precision) quantized checkpoints", section
+ * "Quantization format"). A bias is an input: no y may overlap it. */
 typedef struct rtq_proj {
     int32_t fmt;
     int32_t N;
@@ -99,6 +104,7 @@ typedef struct rtq_proj {
     const void* scale;
     const float* x;
     float* y;
+    const float* bias;         /* fp32 [N] added to every row of y, or NULL */
 } rtq_proj;
 
 typedef struct rtq_block {

@@ -130,6 +130,13 @@ def test_block_project_validation(lib):
     blk.wo.fmt, blk.wo.N, blk.wo.K = rtq.FMT_Q8, 512, 512
     blk.wo.payload, blk.wo.scale, blk.wo.x, blk.wo.y = B + 2**24, C + 2**24, D, A + 2**30
     assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 80, None) == ERR_OVERLAP
+    # a bias must be 4-byte aligned and is an input: no y may overlap it
+    blk = _block()
+    blk.wq.bias = C + 2**24 + 2
+    assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 80, None) == ERR_ALIGN
+    assert b"bias" in lib.rtq_last_error()
+    blk.wq.bias = D + 1024
+    assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 80, None) == ERR_OVERLAP
     # an empty block (no payloads) and M = 0 are no-ops
     assert lib.rtq_block_project((rtq._Block * 1)(), 1, 80, None) == OK
     assert lib.rtq_block_project(arr, 1, 0, None) == OK
@@ -171,11 +178,28 @@ def test_math_mode_switch(lib):
     assert lib.rtq_set_math(rtq.MATH_SPLIT_BF16) == OK
 
 
-def test_struct_layout_matches_header():
-    # rtq_proj: 4 x int32 then 4 pointers; rtq_block: 8 of them in name order.
-    assert ctypes.sizeof(rtq._Proj) == 48
-    assert rtq._Proj.payload.offset == 16 and rtq._Proj.y.offset == 40
-    assert ctypes.sizeof(rtq._Block) == 8 * 48
+def test_struct_layout_matches_header(tmp_path):
+    """The binding's ctypes mirror of rtq_proj / rtq_block has the layout the C
+    compiler gives the header's structs."""
+    fields = [f[0] for f in rtq._Proj._fields_]
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "rtq.h"\nint main(void) {\n'
+                   '  printf("%zu %zu", sizeof(rtq_proj), sizeof(rtq_block));\n'
+                   + "".join(f'  printf(" %zu", offsetof(rtq_proj, {f}));\n' for f in fields)
+                   + "".join(f'  printf(" %zu", offsetof(rtq_block, {n}));\n' for n in rtq.PROJ_NAMES)
+                   + "  return 0;\n}\n")
+    exe = tmp_path / "layout"
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    subprocess.run([cc, "-std=c99", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()]
+    want = [ctypes.sizeof(rtq._Proj), ctypes.sizeof(rtq._Block)]
+    want += [getattr(rtq._Proj, f).offset for f in fields]
+    want += [getattr(rtq._Block, n).offset for n in rtq.PROJ_NAMES]
+    assert got == want
     assert [f[0] for f in rtq._Block._fields_] == list(rtq.PROJ_NAMES)
 
 

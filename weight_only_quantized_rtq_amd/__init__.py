@@ -56,7 +56,7 @@ class RtqError(RuntimeError):
 class _Proj(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("N", ctypes.c_int32), ("K", ctypes.c_int32),
                 ("reserved", ctypes.c_int32), ("payload", ctypes.c_void_p), ("scale", ctypes.c_void_p),
-                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+                ("x", ctypes.c_void_p), ("y", ctypes.c_void_p), ("bias", ctypes.c_void_p)]
 
 
 class _Block(ctypes.Structure):
@@ -293,8 +293,14 @@ def gemm_f8(x: torch.Tensor, w: F8Weight, y: torch.Tensor | None = None, stream=
     return _gemm(x, w, y, stream)
 
 
-def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    return _gemm(x, w, y, stream)
+def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None, bias=None) -> torch.Tensor:
+    """y = x . W^T (+ bias, fp32 [N], through a one-projection rtq_block_project)."""
+    if bias is None:
+        return _gemm(x, w, y, stream)
+    if y is None:
+        y = torch.empty((x.shape[0], w.N), dtype=torch.float32, device=x.device)
+    block_project([{"wq": Projection(w, x, y, bias)}], x.shape[0], stream)
+    return y
 
 
 def dequant(w, stream=None) -> torch.Tensor:
@@ -358,6 +364,7 @@ class Projection:
     weight: object               # Q4Weight | Q8Weight | F8Weight
     x: torch.Tensor              # float32 [M, K]
     y: torch.Tensor              # float32 [M, N]
+    bias: torch.Tensor | None = None   # float32 [N], added to every row of y
 
 
 def pack_blocks(blocks: list[dict[str, Projection]], M: int):
@@ -383,6 +390,13 @@ def pack_blocks(blocks: list[dict[str, Projection]], M: int):
             d.fmt, d.N, d.K, d.reserved = w.fmt, w.N, w.K, 0
             d.payload, d.scale = _ptr(w.payload), _ptr(w.scale_tensor)
             d.x, d.y = _ptr(p.x), _ptr(p.y)
+            if p.bias is not None:
+                _need(p.bias, torch.float32, f"{name}.bias")
+                if tuple(p.bias.shape) != (w.N,):
+                    raise ValueError(f"block {b} {name}: bias {tuple(p.bias.shape)} does not match N={w.N}")
+                d.bias = _ptr(p.bias)
+            else:
+                d.bias = None
             keep.append(p)
     return arr, keep
 

@@ -221,7 +221,7 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
     rtq::ProjTask grouped[RTQ_MAX_BLOCKS * 8];
     rtq::ProjTask single[RTQ_MAX_BLOCKS * 8];
     Range outs[RTQ_MAX_BLOCKS * 8];
-    Range ins[RTQ_MAX_BLOCKS * 8 * 3];
+    Range ins[RTQ_MAX_BLOCKS * 8 * 4];
     int n_grouped = 0, n_single = 0, n_outs = 0, n_ins = 0;
     for (int b = 0; b < n_blocks; ++b) {
         const rtq_proj* p = &blocks[b].wq;
@@ -235,6 +235,7 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
             if (d.reserved != 0) return fail(RTQ_ERR_SHAPE, "%s: reserved field must be 0", name);
             const rtq_status s = check_proj(name, d.fmt, d.x, d.payload, d.scale, d.y, M, d.N, d.K);
             if (s != RTQ_OK) return s;
+            if (d.bias && !aligned(d.bias, 4)) return fail(RTQ_ERR_ALIGN, "%s: bias is not 4-byte aligned", name);
             if (M == 0) continue;
             outs[n_outs++] = range_of(d.y, M * int64_t(d.N) * 4);
             const int64_t pb = d.fmt == RTQ_FMT_Q4 ? int64_t(d.N) * (d.K / 2) : int64_t(d.N) * d.K;
@@ -243,7 +244,8 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
             ins[n_ins++] = range_of(d.x, M * int64_t(d.K) * 4);
             ins[n_ins++] = range_of(d.payload, pb);
             ins[n_ins++] = range_of(d.scale, sb);
-            const rtq::ProjTask t{d.fmt, d.N, d.K, d.payload, d.scale, d.x, d.y};
+            ins[n_ins++] = range_of(d.bias, d.bias ? int64_t(d.N) * 4 : 0);
+            const rtq::ProjTask t{d.fmt, d.N, d.K, d.payload, d.scale, d.x, d.y, d.bias};
             if (rtq::grouped_ok(t)) grouped[n_grouped++] = t;
             else single[n_single++] = t;
         }

@@ -539,9 +539,12 @@ hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
     const int nl = split_limbs(math_mode());
     if (!safe && nl && split_ok(t)) return launch_split(&t, 1, M, nl, stream);
     if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
-    if (t.fmt == kFmtQ4) return launch_one<kFmtQ4, false>(a, stream);
-    if (t.fmt == kFmtQ8) return safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
-    return safe ? launch_one<kFmtF8, true>(a, stream) : launch_one<kFmtF8, false>(a, stream);
+    hipError_t e;
+    if (t.fmt == kFmtQ4) e = launch_one<kFmtQ4, false>(a, stream);
+    else if (t.fmt == kFmtQ8) e = safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
+    else e = safe ? launch_one<kFmtF8, true>(a, stream) : launch_one<kFmtF8, false>(a, stream);
+    if (e == hipSuccess && t.bias) e = launch_bias_add(&t, 1, M, stream);
+    return e;
 }
 
 namespace {
@@ -549,9 +552,12 @@ namespace {
 hipError_t launch_grouped_fp32(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
     if (M > kSmallMaxM) {
         // Many row tiles: every projection alone already fills the GPU; one
-        // launch each keeps the XCD-contiguous tile order.
+        // launch each keeps the XCD-contiguous tile order. Biases are left
+        // to the caller (launch_grouped_fp32_bias).
         for (int i = 0; i < count; ++i) {
-            const hipError_t e = launch_gemm(tasks[i], M, stream);
+            ProjTask t = tasks[i];
+            t.bias = nullptr;
+            const hipError_t e = launch_gemm(t, M, stream);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -618,9 +624,15 @@ hipError_t launch_grouped_fp32(const ProjTask* tasks, int count, int64_t M, hipS
 
 }  // namespace
 
+hipError_t launch_grouped_fp32_bias(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
+    // The fp32 grouped kernels write y; the biases follow in one pass.
+    const hipError_t e = launch_grouped_fp32(tasks, count, M, stream);
+    return e == hipSuccess ? launch_bias_add(tasks, count, M, stream) : e;
+}
+
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
     const int nl = split_limbs(math_mode());
-    if (!nl) return launch_grouped_fp32(tasks, count, M, stream);
+    if (!nl) return launch_grouped_fp32_bias(tasks, count, M, stream);
     // Split path for every task it takes; the rest (weights past 32-bit
     // offsets) run on the fp32 kernels.
     ProjTask split[8 * 64], rest[8 * 64];
@@ -633,7 +645,7 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
         const hipError_t e = launch_split(split, n_split, M, nl, stream);
         if (e != hipSuccess) return e;
     }
-    return n_rest ? launch_grouped_fp32(rest, n_rest, M, stream) : hipSuccess;
+    return n_rest ? launch_grouped_fp32_bias(rest, n_rest, M, stream) : hipSuccess;
 }
 
 }  // namespace rtq

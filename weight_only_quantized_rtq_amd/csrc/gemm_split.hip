@@ -225,6 +225,7 @@ struct SplitArgs {
     float* y;                     // output (or this K chunk's partial), [M][N]
     int M, N, K, RB;
     int g_lo, g_cnt;              // groups [g_lo, g_lo + g_cnt) of K
+    const float* bias;            // fp32 [N] added in the epilogue, or nullptr
 };
 
 constexpr int kStages = 2;        // LDS ring depth (loads run one group ahead)
@@ -232,13 +233,15 @@ constexpr int kRing = 8;          // group sums kept for the deferred min term
 constexpr int kChunk = 2;         // steps per weight chunk when the weights stream through LDS
 
 // LDS map of a workgroup: x stages, group-sum ring and, when the weights
-// stream through LDS (PDW > 0), two weight-chunk slots per wave. A chunk holds
-// the wave's TN*16 rows for kChunk steps: int4 as 16-byte code records (one
-// per row and group) plus 4-byte (scale, min) records, int8 as two 16-byte
-// halves per row and group (TN * 1024 bytes either way).
-template <int BM, int TN = 1, int PDW = 0, int NL = 3>
+// stream through LDS (WL > 0), WL + 1 weight-chunk slots per wave. A chunk
+// holds the wave's TN*16 rows for kChunk steps: int4 as 16-byte code records
+// (one per row and group) plus 4-byte (scale, min) records, int8 as two
+// 16-byte halves per row and group (TN * 1024 bytes either way). With the
+// weights in LDS the x stages run XL steps ahead (XL + 1 stages).
+template <int BM, int TN = 1, int XL = 0, int WL = 0, int NL = 3>
 struct Lds {
-    static constexpr int NSTAGE = PDW > 0 ? PDW + 1 : kStages;    // x stages
+    static constexpr int NSTAGE = WL > 0 ? XL + 1 : kStages;      // x stages
+    static constexpr int NWSLOT = WL + 1;                         // weight-chunk slots per wave
     static constexpr int STAGE = (BM / 16) * NL * 1024;
     static constexpr int XRING = NSTAGE * STAGE;
     // Group-sum slot: waves 0 and 2 copy rows 0..63, waves 1 and 3 rows
@@ -246,7 +249,7 @@ struct Lds {
     static constexpr int XSLOT = BM <= 96 ? 96 : 128;
     static constexpr int WRING = XRING + kRing * XSLOT * 4;
     static constexpr int WCHUNK = TN * 1024;
-    static constexpr int TOTAL = WRING + (PDW > 0 ? 2 * 4 * WCHUNK : 0);
+    static constexpr int TOTAL = WRING + (WL > 0 ? NWSLOT * 4 * WCHUNK : 0);
     static constexpr int COPIES = (BM / 16) * NL;                  // 1 KB copies per stage
     static constexpr int PER_WAVE = (COPIES + 3) / 4;
     static_assert(BM <= XSLOT, "group-sum slot holds every row of the tile");
@@ -257,6 +260,18 @@ template <int N>
 __device__ __forceinline__ void wait_vm() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xf00);
+}
+
+// Wait until at most n (uniform, 0 <= n) vector-memory operations are in
+// flight; n above MAXN waits for MAXN.
+template <int MAXN>
+__device__ __forceinline__ void wait_vm_upto(int n) {
+    if constexpr (MAXN == 0) {
+        wait_vm<0>();
+    } else {
+        if (n >= MAXN) wait_vm<MAXN>();
+        else wait_vm_upto<MAXN - 1>(n);
+    }
 }
 
 __device__ __forceinline__ void dma16(const void* src, void* lds_base) {
@@ -277,16 +292,17 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
 // image already in L2 instead of all missing on the same lines together.
 // Iteration i is called step i below; the group it processes is (rot + i) % G.
 //
-// Weights: with PDW == 0 each wave loads its codes and pairs into registers one
-// step ahead (enough when they come from L2); with PDW > 0 they are copied by
-// DMA into a per-wave LDS ring PDW steps ahead (for weights streamed from HBM).
-template <int FMT, int WM, int WN, int TM, int TN, int PDW, int NL>
+// Weights: with WL == 0 each wave loads its codes and pairs into registers one
+// step ahead (enough when they come from L2), and the x stages run one step
+// ahead; with WL > 0 the weights are copied by DMA into a per-wave LDS ring WL
+// chunks ahead (for weights streamed from HBM) and the x stages XL steps ahead.
+template <int FMT, int WM, int WN, int TM, int TN, int XL, int WL, int NL>
 __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
-    using L = Lds<BM, TN, PDW, NL>;
+    using L = Lds<BM, TN, XL, WL, NL>;
     static_assert(NL == 1 || NL == 3, "limbs");
     static_assert(WM * WN == 4, "four waves");
-    static_assert(PDW <= 3, "prefetch depth");
+    static_assert(WL == 0 || (XL >= 1 && XL <= 2 * WL && WL <= 3), "prefetch leads");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     // The wave index is uniform: made explicit so that everything derived
@@ -358,8 +374,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     };
 
-    // Weight chunks (PDW > 0): chunk c holds the weights of steps kChunk*c and
-    // kChunk*c + 1 for this wave's TN*16 rows, in slot c & 1. Each lane copies
+    // Weight chunks (WL > 0): chunk c holds the weights of steps kChunk*c and
+    // kChunk*c + 1 for this wave's TN*16 rows, in slot c % (WL + 1). Each lane copies
     // whole 16-byte records (int4: the 32 codes of one row and group; int8:
     // half of them), so one instruction covers 64 (row, group) records.
     // Record order is swizzled so that the per-step reads are bank-spread:
@@ -370,7 +386,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     const int wrow0 = n0 + wn * TN * 16;
     // Per lane and chunk instruction j: the record's row offset (fixed) and
     // which of the chunk's two steps it belongs to.
-    constexpr int NCI = PDW > 0 ? (FMT == kFmtQ4 ? TN / 2 : TN) : 1;
+    constexpr int NCI = WL > 0 ? (FMT == kFmtQ4 ? TN / 2 : TN) : 1;
     uint32_t cvoff[NCI], cpoff[NCI];
     bool csec[NCI], psec[NCI];
 #pragma unroll
@@ -394,8 +410,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     }
     auto w_chunk_issue = [&](int c) {
-        if constexpr (PDW > 0) {
-            unsigned char* slot = wring + (c & 1) * 4 * L::WCHUNK;
+        if constexpr (WL > 0) {
+            unsigned char* slot = wring + (c % L::NWSLOT) * 4 * L::WCHUNK;
             const int s0 = kChunk * c;
             const int g0 = group_of(s0);                          // s0 < GS
             const int g1 = group_of(min(s0 + 1, GS - 1));
@@ -414,7 +430,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     };
     auto w_read = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
-        const unsigned char* slot = wring + ((i / kChunk) & 1) * 4 * L::WCHUNK;
+        const unsigned char* slot = wring + ((i / kChunk) % L::NWSLOT) * 4 * L::WCHUNK;
         const int h = i % kChunk;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -515,43 +531,53 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     };
 
-    // ---- main loop: while step i computes, step i+1 streams into the other
-    //      LDS stage (and the weights of step i+1, or of step i+PDW through the
-    //      weight ring). A stage or ring slot is refilled only after the barrier
-    //      that follows every wave's last read of it. ----
+    // ---- main loop: while step i computes, later steps stream into the other
+    //      LDS stages and weight slots. A stage or slot is refilled only after
+    //      the barrier that follows every wave's last read of it. ----
     uint32_t wq[TN][2], wp[TN], cq[TN][2], cp[TN];
-    // With PDW > 0 (PDW == 2): the x stage of step j goes out in iteration
-    // j - 2 (steps 0 and 1 in the prologue) as NX vector-memory ops, and weight
-    // chunk c in iteration kChunk*(c - 1) (chunk 0 in the prologue), just
-    // before that iteration's x stage, as NWC ops. So what step i needs was
-    // issued no later than its x stage, and the only ops issued after that
-    // stage are those of iteration i - 1: the x stage of step i + 1 and, for
-    // odd i, weight chunk (i + 1) / 2, both only when i + 1 < GS.
+    // Schedule with WL > 0, counted in iterations j (negative j = prologue):
+    // iteration j issues weight chunk j/2 + WL when j is even (NWC ops, first
+    // step j + 2*WL), then the x stage of step j + XL (NX ops), each only if
+    // that step exists. What step i needs (its x stage and chunk i/2) was
+    // therefore issued no later than its x stage, in iteration i - XL (since
+    // XL <= 2*WL), and the ops issued after it are those of iterations
+    // i - XL + 1 .. i - 1: waiting until at most that many are in flight
+    // (loads complete in order) means step i has landed.
     constexpr int NX = L::PER_WAVE + 1;
     constexpr int NWC = TN;
-    static_assert(PDW == 0 || (PDW == 2 && kChunk == 2 && TN % 2 == 0), "weight-chunk schedule");
-    if constexpr (PDW == 0) {
+    static_assert(WL == 0 || (kChunk == 2 && TN % 2 == 0), "weight-chunk schedule");
+    auto chunk_at = [&](int j) { return (j & 1) == 0 && j + 2 * WL < GS; };   // iteration j issues a chunk
+    auto stage_at = [&](int j) { return j + XL >= 0 && j + XL < GS; };       // iteration j issues an x stage
+    if constexpr (WL == 0) {
         stage_copy(0);
         w_load(0, wq, wp);
     } else {
-        w_chunk_issue(0);
-        stage_copy(0);
-        if (1 < GS) stage_copy(1);
+#pragma unroll
+        for (int j = -2 * WL; j < 0; ++j) {
+            if (chunk_at(j)) w_chunk_issue(j / 2 + WL);
+            if (stage_at(j)) stage_copy(j + XL);
+        }
     }
     for (int i = 0; i < GS; ++i) {
-        if constexpr (PDW == 0) {
+        if constexpr (WL == 0) {
             wait_vm<0>();                                 // this wave's part of step i has landed
+        } else if (i + 2 * WL <= GS) {
+            // every op of the window exists: (XL-1) x stages and the chunks of
+            // its even iterations
+            if (i & 1) wait_vm<(XL - 1) * NX + (XL / 2) * NWC>();
+            else wait_vm<(XL - 1) * NX + ((XL - 1) / 2) * NWC>();
         } else {
-            if (i + 1 >= GS) wait_vm<0>();
-            else if (i & 1) wait_vm<NX + NWC>();
-            else wait_vm<NX>();
+            int n = 0;
+#pragma unroll
+            for (int d = 1; d < XL; ++d) n += (stage_at(i - d) ? NX : 0) + (chunk_at(i - d) ? NWC : 0);
+            wait_vm_upto<(XL - 1) * NX + (XL / 2) * NWC>(n);
         }
         // Barrier without a memory fence: the LDS data of step i came in by DMA
         // and is complete after the wait above (in every wave, after the barrier);
         // nothing else writes LDS, and a fence would also wait for later steps.
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (PDW == 0) {
+        if constexpr (WL == 0) {
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 cq[tn][0] = wq[tn][0];
@@ -564,8 +590,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             }
         } else {
             w_read(i, cq, cp);
-            if (i % kChunk == 0 && i + kChunk < GS) w_chunk_issue(i / kChunk + 1);
-            if (i + PDW < GS) stage_copy(i + PDW);
+            if (chunk_at(i)) w_chunk_issue(i / 2 + WL);
+            if (stage_at(i)) stage_copy(i + XL);
         }
         __builtin_amdgcn_sched_barrier(0);
         compute(i, cq, cp);
@@ -579,6 +605,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         if (col >= N) continue;
         float sc = 1.0f;
         if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
+        const float bv = a.bias ? a.bias[col] : 0.0f;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
@@ -587,6 +614,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                 if (row < M) {
                     float v = acc[tm][tn][e];
                     if constexpr (FMT == kFmtQ8) v *= sc;
+                    if (a.bias) v += bv;
                     a.y[static_cast<int64_t>(row) * N + col] = v;
                 }
             }
@@ -608,10 +636,10 @@ constexpr int kLBN = kLWN * kLTN * 16;
 
 template <int FMT, int NL>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, 1, 0, NL>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, 1, 0, 0, NL>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int nt = w % tiles_n;
-    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, 0, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
+    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, 0, 0, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
 // Small M (<= 80): one row block of TM*16 rows; 4 waves side by side along N,
@@ -641,7 +669,9 @@ static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within
 // groups (512 of K), so every workgroup does about the same work.
 constexpr int kSmallBN = 256;
 constexpr int kMaxGroupedTiles = 1 << 30;   // workgroups of one grouped launch
-constexpr int kSmallPDW = 2;        // x stages and weights (streamed from HBM) two steps ahead
+// Prefetch leads of the small-M kernel: x stages XL steps ahead, weight chunks
+// (streamed from HBM) WL chunks ahead, per limb count.
+template <int NL> struct SmallLead { static constexpr int XL = 2, WL = 1; };
 constexpr int kChunkGroups = 16;
 __host__ __device__ inline int split_chunks(int K) {
     const int G = K / 32;
@@ -650,10 +680,13 @@ __host__ __device__ inline int split_chunks(int K) {
 
 template <int TM, int NL>
 __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, kSmallPDW, NL>::TOTAL];
+    constexpr int XL = SmallLead<NL>::XL, WL = SmallLead<NL>::WL;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, XL, WL, NL>::TOTAL];
     // Find this workgroup's projection: tiles are numbered projection by
-    // projection, (column block, K chunk) within one.
-    const int w = blockIdx.x;
+    // projection, (column block, K chunk) within one. Consecutive tiles go to
+    // one XCD, so the column tiles that read the same activation image share
+    // that XCD's L2 instead of each fetching the image from memory.
+    const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
     const int begin = g.tile_begin[i];
     const int K = g.k[i];
@@ -663,36 +696,64 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
     const int cb = local / ks, kc = local % ks;
     const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
     float* y = g.y[i] + static_cast<int64_t>(ks > 1 ? kc : 0) * g.M * g.n[i];
-    const SplitArgs a{g.ws + g.img_off[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo};
+    // Biases of grouped projections are added by finish_kernel.
+    const SplitArgs a{g.ws + g.img_off[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo,
+                      nullptr};
     const int rot = cb % (g_hi - g_lo);
     if (g.fmt[i] == kFmtQ4)
-        split_tile<kFmtQ4, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ4, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else if (g.fmt[i] == kFmtQ8)
-        split_tile<kFmtQ8, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else
-        split_tile<kFmtF8, 1, 4, TM, 4, kSmallPDW, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtF8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
 }
 
-// Sums the K-chunk partials of split projections in chunk order.
-constexpr int kMaxReduce = 96;
-struct ReduceArgs {
+// Finishes projections after their GEMM launch: sums the K-chunk partials in
+// chunk order and adds the bias, y = (P_0 + ... + P_{ks-1}) + bias. With
+// ks == 1 the single "partial" is y itself and the bias is added in place.
+constexpr int kMaxFinish = 96;
+struct FinishArgs {
     int count;
     int pad;
-    const float* part[kMaxReduce];
-    float* y[kMaxReduce];
-    int64_t elems[kMaxReduce];
-    int ks[kMaxReduce];
+    const float* part[kMaxFinish];  // chunk c of entry i at part[i] + c * elems[i]
+    float* y[kMaxFinish];
+    const float* bias[kMaxFinish];  // fp32 [n] or nullptr
+    int64_t elems[kMaxFinish];      // M * n
+    int ks[kMaxFinish];
+    int n[kMaxFinish];
 };
-static_assert(sizeof(ReduceArgs) <= 4096, "kernel arguments must stay within 4 KiB");
+static_assert(sizeof(FinishArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
-__global__ __launch_bounds__(256) void reduce_kernel(ReduceArgs r) {
+__global__ __launch_bounds__(256) void finish_kernel(FinishArgs r) {
     const int i = blockIdx.y;
     const int64_t n = r.elems[i];
-    for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n; e += int64_t(gridDim.x) * 256) {
+    const int N = r.n[i];
+    const float* bias = r.bias[i];
+    const int64_t stride = int64_t(gridDim.x) * 256;
+    int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    int col = static_cast<int>(e % N);                 // column of element e, kept in step with e
+    const int col_step = static_cast<int>(stride % N);
+    for (; e < n; e += stride) {
         float s = r.part[i][e];
         for (int c = 1; c < r.ks[i]; ++c) s += r.part[i][c * n + e];
+        if (bias) s += bias[col];
         r.y[i][e] = s;
+        col += col_step;
+        if (col >= N) col -= N;
     }
+}
+
+// Adds one projection to a finish launch; returns the blocks it asks for.
+int finish_entry(FinishArgs& r, const float* part, float* y, const float* bias, int64_t elems, int ks, int N) {
+    const int c = r.count++;
+    r.part[c] = part;
+    r.y[c] = y;
+    r.bias[c] = bias;
+    r.elems[c] = elems;
+    r.ks[c] = ks;
+    r.n[c] = N;
+    const int64_t need = (elems + 255) / 256;
+    return need < 1024 ? static_cast<int>(need) : 1024;
 }
 
 // ---------------------------------------------------------------------------
@@ -839,7 +900,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             order[j + 1] = v;
         }
         int done = 0;
-        ReduceArgs red{};
+        FinishArgs red{};
         int red_blocks = 0;
         while (e == hipSuccess && done < count) {
             SplitGroupArgs g{};
@@ -863,14 +924,9 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
                 g.tile_begin[c] = tiles;
                 g.fmt[c] = static_cast<uint8_t>(t.fmt);
                 tiles += (t.N + kSmallBN - 1) / kSmallBN * ks;
-                if (ks > 1) {
-                    const int r = red.count++;
-                    red.part[r] = reinterpret_cast<const float*>(wsb + part_off[ti]);
-                    red.y[r] = t.y;
-                    red.elems[r] = int64_t(M) * t.N;
-                    red.ks[r] = ks;
-                    const int64_t need = (red.elems[r] + 255) / 256;
-                    const int nb = need < 1024 ? static_cast<int>(need) : 1024;
+                if (ks > 1 || t.bias) {
+                    const float* part = ks > 1 ? reinterpret_cast<const float*>(wsb + part_off[ti]) : t.y;
+                    const int nb = finish_entry(red, part, t.y, t.bias, int64_t(M) * t.N, ks, t.N);
                     red_blocks = red_blocks > nb ? red_blocks : nb;
                 }
             }
@@ -883,16 +939,17 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             timing_end(mark, stream);
             e = hipGetLastError();
             if (e == hipSuccess && red.count) {
-                reduce_kernel<<<dim3(red_blocks, red.count), 256, 0, stream>>>(red);
+                finish_kernel<<<dim3(red_blocks, red.count), 256, 0, stream>>>(red);
                 e = hipGetLastError();
-                red = ReduceArgs{};
+                red = FinishArgs{};
                 red_blocks = 0;
             }
         }
     } else if (e == hipSuccess) {
         for (int i = 0; i < count && e == hipSuccess; ++i) {
             const ProjTask& t = tasks[i];
-            const SplitArgs a{wsb + inputs[img_of[i]].offset, t.payload, t.scale, t.y, M, t.N, t.K, RB, 0, t.K / 32};
+            const SplitArgs a{wsb + inputs[img_of[i]].offset, t.payload, t.scale, t.y, M, t.N, t.K, RB, 0, t.K / 32,
+                              t.bias};
             const int tn = (t.N + kLBN - 1) / kLBN;
             const int tmb = (M + kLBM - 1) / kLBM;
             const int mark = timing_begin(stream);
@@ -906,6 +963,25 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
     }
     const hipError_t f = hipFreeAsync(ws, stream);
     return e != hipSuccess ? e : f;
+}
+
+hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
+    FinishArgs r{};
+    int blocks = 0;
+    for (int i = 0; i <= count; ++i) {
+        if (r.count == kMaxFinish || (i == count && r.count)) {
+            finish_kernel<<<dim3(blocks, r.count), 256, 0, stream>>>(r);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            r = FinishArgs{};
+            blocks = 0;
+        }
+        if (i == count || !tasks[i].bias) continue;
+        const ProjTask& t = tasks[i];
+        const int nb = finish_entry(r, t.y, t.y, t.bias, M * t.N, 1, t.N);
+        blocks = blocks > nb ? blocks : nb;
+    }
+    return hipSuccess;
 }
 
 }  // namespace rtq

@@ -28,6 +28,7 @@ struct ProjTask {
     const void* scale;
     const float* x;
     float* y;
+    const float* bias;      // fp32 [N] or nullptr
 };
 
 // Kernel timing marks (rtq_timing_enable): returns a slot or -1 when off.
@@ -53,5 +54,9 @@ bool grouped_ok(const ProjTask& task);
 // split_ok(). Uses a stream-ordered workspace (hipMallocAsync).
 bool split_ok(const ProjTask& task);
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
+
+// y += bias (broadcast over the M rows) for every task that has a bias, in
+// place, after the GEMM kernels that wrote y (same stream).
+hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 
 }  // namespace rtq
