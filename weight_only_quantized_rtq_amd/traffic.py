@@ -17,11 +17,22 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h"
 # (workload, math) -> record; filled from the counter runs described in the
 # profiles folder.
 RECORDS: dict = {
-    # split_grouped_kernel<5>, 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split"): {"fetch_kib": 78314.479, "write_kib": 35210.438,
+    # split_grouped_kernel<5, 3>, 12 blocks at M = 80: 33 dispatches per counter run
+    ("m80", "split"): {"fetch_kib": 38386.992, "write_kib": 33894.269,
                        "fetch_factor": 1.99987, "write_factor": 1.0,
                        "algorithmic_bytes": 80658432,
-                       "sources_sha256": "f71792551aab15bf913f391339442beec0de86c70d00a1f1218ff3afe2367dc7"},
+                       "sources_sha256": "1810f8eb432914eb90fac8cb4677ae204c47a9b0e5f9695dceb4babfe53614d8"},
+    # split_grouped_kernel<5, 1> (bf16 activations), same workload
+    ("m80", "bf16"): {"fetch_kib": 27752.294, "write_kib": 34606.119,
+                      "fetch_factor": 1.99987, "write_factor": 1.0,
+                      "algorithmic_bytes": 80658432,
+                      "sources_sha256": "1810f8eb432914eb90fac8cb4677ae204c47a9b0e5f9695dceb4babfe53614d8"},
+    # split_gemm_kernel<1|2, 3>, 12 blocks at M = 65536: 288 dispatches per counter run
+    # (3 steps x 96 projections); algorithmic bytes are the per-launch average
+    ("m65536", "split"): {"fetch_kib": 180619.507, "write_kib": 249474.057,
+                          "fetch_factor": 1.99987, "write_factor": 1.0,
+                          "algorithmic_bytes": 419840512,
+                          "sources_sha256": "1810f8eb432914eb90fac8cb4677ae204c47a9b0e5f9695dceb4babfe53614d8"},
 }
 
 
