@@ -64,6 +64,8 @@ def parse():
                     help="skip the separately reported bf16-activation timing")
     ap.add_argument("--compare-fp32", action="store_true",
                     help="also time the fp32-MFMA path (few steps) and report it alongside")
+    ap.add_argument("--bias", action="store_true",
+                    help="give every projection an fp32 bias (y = x.W^T + b) to time the bias epilogue")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     return ap.parse_args()
 
@@ -95,6 +97,9 @@ def block_bytes_flops(M, recipe="mixed"):
     return wbytes, flops
 
 
+BIAS = False
+
+
 def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, recipe="mixed"):
     """Packed weights (quantized on the GPU) for n_sets x 12 blocks, plus inputs
     and outputs, and the host descriptor arrays of each set."""
@@ -109,6 +114,8 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, reci
         xs = [shared] * nb
     ys = [{n: torch.empty((M, synth.BLOCK_SHAPES[n][0]), dtype=torch.float32, device=dev)
            for n in synth.PROJ_ORDER} for _ in range(nb)]
+    bs = [{n: (torch.from_numpy(synth.activation(cfg, b, "h", 1, synth.BLOCK_SHAPES[n][0])[0]).to(dev)
+               if BIAS else None) for n in synth.PROJ_ORDER} for b in range(nb)]
     sets = []
     for s in range(n_sets):
         blocks = []
@@ -118,7 +125,7 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, reci
                 W = torch.from_numpy(synth.weight(cfg, s, b, name, heavy=heavy)).to(dev)
                 w = rtq.quantize(W, recipe_map(recipe)[name])
                 del W
-                blk[name] = rtq.Projection(w, xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name])
+                blk[name] = rtq.Projection(w, xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name], bs[b][name])
             blocks.append(blk)
         sets.append((blocks, rtq.pack_blocks(blocks, M)))
     torch.cuda.synchronize()
@@ -251,6 +258,8 @@ def main():
     import torch
     import synth
     import weight_only_quantized_rtq_amd as rtq
+    global BIAS
+    BIAS = args.bias
     rtq.load_library()
     torch.cuda.init()
     modes = {"split": rtq.MATH_SPLIT_BF16, "fp32": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16}
@@ -303,7 +312,7 @@ def main():
         "config": {"workload": cfg, "M": prim["M"], "n_blocks": synth.NUM_BLOCKS,
                    "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": {"mixed": "mixed int4/int8", "all_q8": "all int8",
                                                                                "all_f8": "all FP8 E4M3"}[args.recipe],
-                   "d_model": synth.D_MODEL, "d_ff": synth.D_FF,
+                   "d_model": synth.D_MODEL, "d_ff": synth.D_FF, "bias": bool(args.bias),
                    "math": {"split": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation",
                             "fp32": "fp32 MFMA on dequantized weights",
                             "bf16": "activations rounded to bf16 (lower precision), exact weight products, "

@@ -89,6 +89,28 @@ def test_projection_names():
     assert ck.TYPES["q4"]["wo"] == "q8" and ck.TYPES["q4"]["w2"] == "q8" and ck.TYPES["q4"]["w1"] == "q4"
 
 
+def test_block_weights_groups_by_block_with_biases(tmp_path):
+    path, _ = _oracle_file(tmp_path)
+    w = ck.load(path, device="cpu")
+    blocks = ck.block_weights(w)
+    assert len(blocks) == 1 and set(blocks[0]) == {"wq", "wo", "w1"}
+    assert blocks[0]["w1"][1] is w["blocks.0.ffn.w1.bias"]
+    assert blocks[0]["wq"][1] is None and blocks[0]["wo"][1] is None
+    # blocks in index order, two blocks
+    two = {"blocks.10.attn.wq": w["blocks.0.attn.wq.weight"], "blocks.2.attn.wq": w["blocks.0.attn.wq.weight"]}
+    assert [set(b) for b in ck.block_weights(two)] == [{"wq"}, {"wq"}]
+    # a bias of the wrong shape, a duplicate projection, a quantized tensor outside any block
+    bad = dict(w)
+    bad["blocks.0.ffn.w1.bias"] = torch.zeros(31)
+    with pytest.raises(ValueError, match="float32"):
+        ck.block_weights(bad)
+    with pytest.raises(ValueError, match="two wq"):
+        ck.block_weights({"blocks.0.attn.wq": w["blocks.0.attn.wq.weight"],
+                          "blocks.0.x.wq.weight": w["blocks.0.attn.wq.weight"]})
+    with pytest.raises(ValueError, match="numbered block"):
+        ck.block_weights({"head.wq": w["blocks.0.attn.wq.weight"]})
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("qtype", ["q4", "q8", "fp8"])
 def test_quantize_file_matches_oracle(tmp_path, qtype):
@@ -99,7 +121,9 @@ def test_quantize_file_matches_oracle(tmp_path, qtype):
     for name in synth.PROJ_ORDER:
         key = f"blocks.0.{'ffn.' if name in ('w1', 'w2', 'w3') else 'attn.'}{name}.weight"
         src[key] = torch.from_numpy(synth.weight(22, 0, 0, name))
-    src["blocks.0.ffn.w1.bias"] = torch.ones(2048)
+    for name in synth.PROJ_ORDER:
+        key = f"blocks.0.{'ffn.' if name in ('w1', 'w2', 'w3') else 'attn.'}{name}.bias"
+        src[key] = torch.from_numpy(synth.activation(23, 0, "h", 1, synth.BLOCK_SHAPES[name][0])[0])
     spath, dpath = os.path.join(tmp_path, "src.safetensors"), os.path.join(tmp_path, "dst.safetensors")
     save_file(src, spath)
     ck.quantize_file(spath, dpath, qtype)
@@ -107,7 +131,7 @@ def test_quantize_file_matches_oracle(tmp_path, qtype):
     assert torch.equal(w["blocks.0.ffn.w1.bias"].cpu(), src["blocks.0.ffn.w1.bias"])
     recipe = ck.TYPES[qtype]
     xs = {n: synth.activation(22, 0, n, M) for n in synth.INPUT_WIDTH}
-    blk, refs = {}, {}
+    refs = {}
     for key, W in src.items():
         name = ck.projection_of(key)
         if name is None or key.endswith("bias"):
@@ -118,12 +142,13 @@ def test_quantize_file_matches_oracle(tmp_path, qtype):
         assert np.array_equal(got.payload.cpu().numpy(), ref[0]), key
         if fmt != "f8":
             assert np.array_equal(got.scale_tensor.cpu().numpy().view(np.uint8), ref[1].view(np.uint8)), key
-        N, K, xin = synth.BLOCK_SHAPES[name]
-        blk[name] = rtq.Projection(got, torch.from_numpy(xs[xin]).cuda(),
-                                   torch.empty((M, N), dtype=torch.float32, device="cuda:0"))
-        refs[name] = (fmt, ref, xin)
-    rtq.block_project([blk], M)
+        refs[name] = (fmt, ref, synth.BLOCK_SHAPES[name][2], src[ck.bias_key(key)].numpy())
+    # loaded checkpoint -> block projections (with their biases) -> GPU
+    (block,) = ck.block_weights(w)
+    dxs = {p: torch.from_numpy(xs[synth.BLOCK_SHAPES[p][2]]).cuda() for p in block}
+    dys = {p: torch.empty((M, block[p][0].N), dtype=torch.float32, device="cuda:0") for p in block}
+    rtq.block_project([ck.projections(block, dxs, dys)], M)
     torch.cuda.synchronize()
-    for name, (fmt, ref, xin) in refs.items():
-        err = oracle.rel_fro(blk[name].y.cpu().numpy(), oracle.project(fmt, xs[xin], *ref))
+    for name, (fmt, ref, xin, bias) in refs.items():
+        err = oracle.rel_fro(dys[name].cpu().numpy(), oracle.project_bias(fmt, xs[xin], *ref, bias))
         assert err <= 1e-5, (name, err)

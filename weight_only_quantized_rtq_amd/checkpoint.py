@@ -28,7 +28,7 @@ import sys
 
 import torch
 
-from . import F8Weight, Q4Weight, Q8Weight, quantize
+from . import F8Weight, PROJ_NAMES, Projection, Q4Weight, Q8Weight, quantize
 
 Q4_SCALE = ".q4_scale"
 Q8_SCALE = ".q_scale"
@@ -52,6 +52,45 @@ def projection_of(name: str) -> str | None:
     """The projection a tensor name belongs to (wq ... w3), or None."""
     m = PROJ_RE.search(name)
     return m.group(1) if m else None
+
+
+# The block a projection belongs to: the last integer component of its name
+# before the projection ("blocks.3.attn.wq.weight" -> 3).
+BLOCK_RE = re.compile(r"(?:^|\.)(\d+)\.(?:[A-Za-z_][\w]*\.)*(?:wq|wk|wv|wg|wo|w1|w2|w3)(?:\.weight)?$")
+
+
+def bias_key(name: str) -> str:
+    """Key of a projection's fp32 bias: "<...>.w1.weight" -> "<...>.w1.bias"."""
+    return name[: -len(".weight")] + ".bias" if name.endswith(".weight") else name + ".bias"
+
+
+def block_weights(weights: dict[str, object]) -> list[dict[str, tuple]]:
+    """Groups the quantized projections of a loaded checkpoint by block:
+    result[b][proj] = (weight, bias or None), blocks in index order. Biases are
+    the fp32 1-D tensors at bias_key(name); a projection without one gets None."""
+    blocks: dict[int, dict[str, tuple]] = {}
+    for name, w in weights.items():
+        if not isinstance(w, (Q4Weight, Q8Weight, F8Weight)):
+            continue
+        proj = projection_of(name)
+        m = BLOCK_RE.search(name)
+        if proj is None or m is None:
+            raise ValueError(f"{name}: a quantized tensor that is not a numbered block projection")
+        b = int(m.group(1))
+        if proj in blocks.setdefault(b, {}):
+            raise ValueError(f"block {b} has two {proj} tensors")
+        bias = weights.get(bias_key(name))
+        if bias is not None:
+            if not isinstance(bias, torch.Tensor) or bias.dtype != torch.float32 or tuple(bias.shape) != (w.N,):
+                raise ValueError(f"{bias_key(name)}: expected float32 [{w.N}]")
+        blocks[b][proj] = (w, bias)
+    return [blocks[b] for b in sorted(blocks)]
+
+
+def projections(block: dict[str, tuple], xs: dict[str, torch.Tensor], ys: dict[str, torch.Tensor]):
+    """One block's rtq_block_project inputs: xs[proj] / ys[proj] are the input
+    and output of each projection present in the block."""
+    return {p: Projection(w, xs[p], ys[p], bias) for p, (w, bias) in block.items() if p in PROJ_NAMES}
 
 
 def detect(tensors: dict[str, torch.Tensor]) -> dict[str, object]:
