@@ -64,6 +64,9 @@ def parse():
                     help="skip the separately reported bf16-activation timing")
     ap.add_argument("--compare-fp32", action="store_true",
                     help="also time the fp32-MFMA path (few steps) and report it alongside")
+    ap.add_argument("--m-sweep", default="1,2,4,8,16,32,48,80",
+                    help="M values of the diagnostic sweep on the m80 weight sets, run with --workload both "
+                         "('' to skip)")
     ap.add_argument("--bias", action="store_true",
                     help="give every projection an fp32 bias (y = x.W^T + b) to time the bias epilogue")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -176,6 +179,39 @@ def measure(torch, rtq, synth, workload, steps, warmup, recipe="mixed"):
         "kernel_weight_gbs": bytes_step / per_step / (launch_ms * 1e-3) / 1e9,
         "flops_per_step": flops_step, "weight_bytes_per_step": bytes_step, "steps": steps,
     }
+
+
+def m_sweep(torch, rtq, synth, Ms, steps=200, warmup=20, recipe="mixed"):
+    """Diagnostic: the m80 weight sets (12 blocks x 16 sets) at other M, to show
+    where the weight stream stops being the only cost. Same timing as the main
+    workload; the weights are quantized once and shared across M."""
+    dev = "cuda:0"
+    nb = synth.NUM_BLOCKS
+    weights = [[{name: rtq.quantize(torch.from_numpy(synth.weight(4, s, b, name)).to(dev), recipe_map(recipe)[name])
+                 for name in synth.PROJ_ORDER} for b in range(nb)] for s in range(WEIGHT_SETS)]
+    wb, _ = block_bytes_flops(1, recipe)
+    out = []
+    for M in Ms:
+        xs = [{n: torch.from_numpy(synth.activation(4, b, n, M)).to(dev) for n in synth.INPUT_WIDTH} for b in range(nb)]
+        ys = [{n: torch.empty((M, synth.BLOCK_SHAPES[n][0]), dtype=torch.float32, device=dev)
+               for n in synth.PROJ_ORDER} for _ in range(nb)]
+        sets = []
+        for s in range(WEIGHT_SETS):
+            blocks = [{name: rtq.Projection(weights[s][b][name], xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name])
+                       for name in synth.PROJ_ORDER} for b in range(nb)]
+            sets.append((blocks, rtq.pack_blocks(blocks, M)))
+        wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup)
+        _, fl = block_bytes_flops(M, recipe)
+        ms = wall / steps * 1e3
+        per_launch = kernel_ms / launches
+        out.append({"M": M, "ms_per_step": round(ms, 5), "tflops": round(fl * nb / (ms * 1e-3) / 1e12, 3),
+                    "weight_gbs": round(wb * nb / (ms * 1e-3) / 1e9, 1),
+                    "kernel_ms_per_launch": round(per_launch, 5),
+                    "weight_gbs_in_kernel": round(wb * nb / (launches / steps) / (per_launch * 1e-3) / 1e9, 1)})
+        del sets, xs, ys
+    del weights
+    torch.cuda.empty_cache()
+    return out
 
 
 def load_traffic(workload, math, recipe="mixed"):
@@ -335,6 +371,11 @@ def main():
             "note": "x rounded to the nearest bf16 (lower precision: 3e-3 bar, not 1e-5), one bf16 MFMA per "
                     "product; reported apart from the fp32-activation figures above",
             **bf16}
+    if args.m_sweep and args.workload == "both":
+        line["m_sweep"] = {
+            "note": f"diagnostic: the m80 weight sets at other M ({args.math} arithmetic); per-step and "
+                    "in-kernel weight GB/s against the 8000 GB/s HBM peak",
+            "points": m_sweep(torch, rtq, synth, [int(v) for v in args.m_sweep.split(",")], recipe=args.recipe)}
     if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
     print(json.dumps(line), flush=True)
