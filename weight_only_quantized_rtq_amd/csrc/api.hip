@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <vector>
 
 #include "rtq_internal.h"
 
@@ -218,10 +219,14 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
         return fail(RTQ_ERR_SHAPE, "rtq_block_project: n_blocks=%d out of range [1, %d]", n_blocks, RTQ_MAX_BLOCKS);
     if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "rtq_block_project: M=%lld out of range", (long long)M);
     static const char* names[8] = {"wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2"};
-    rtq::ProjTask grouped[RTQ_MAX_BLOCKS * 8];
-    rtq::ProjTask single[RTQ_MAX_BLOCKS * 8];
-    Range outs[RTQ_MAX_BLOCKS * 8];
-    Range ins[RTQ_MAX_BLOCKS * 8 * 4];
+    // Per-thread buffers, sized once for the largest call (no stack arrays of
+    // this size, no allocation per call).
+    thread_local std::vector<rtq::ProjTask> grouped_buf(RTQ_MAX_BLOCKS * 8), single_buf(RTQ_MAX_BLOCKS * 8);
+    thread_local std::vector<Range> outs_buf(RTQ_MAX_BLOCKS * 8), ins_buf(RTQ_MAX_BLOCKS * 8 * 4);
+    rtq::ProjTask* grouped = grouped_buf.data();
+    rtq::ProjTask* single = single_buf.data();
+    Range* outs = outs_buf.data();
+    Range* ins = ins_buf.data();
     int n_grouped = 0, n_single = 0, n_outs = 0, n_ins = 0;
     for (int b = 0; b < n_blocks; ++b) {
         const rtq_proj* p = &blocks[b].wq;

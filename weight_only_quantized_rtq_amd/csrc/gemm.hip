@@ -8,6 +8,8 @@
 // accumulators. The format is that of the RT-J int4 / int8 model cards,
 // section "Quantization format"; the dequantize-inside-the-GEMM design is the
 // one their opening paragraphs describe.
+#include <vector>
+
 #include "rtq_device.h"
 #include "rtq_internal.h"
 
@@ -635,7 +637,10 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream
     if (!nl) return launch_grouped_fp32_bias(tasks, count, M, stream);
     // Split path for every task it takes; the rest (weights past 32-bit
     // offsets) run on the fp32 kernels.
-    ProjTask split[8 * 64], rest[8 * 64];
+    thread_local std::vector<ProjTask> split_buf(8 * 64), rest_buf(8 * 64);
+    if (count > static_cast<int>(split_buf.size())) return hipErrorInvalidValue;
+    ProjTask* split = split_buf.data();
+    ProjTask* rest = rest_buf.data();
     int n_split = 0, n_rest = 0;
     for (int i = 0; i < count; ++i) {
         if (split_ok(tasks[i])) split[n_split++] = tasks[i];

@@ -35,6 +35,8 @@
 //  3. Each wave streams its own packed weight columns from global memory into
 //     registers in MFMA operand layout (4 bytes of int4 codes or 8 bytes of int8
 //     codes per lane per group): the packed payload is read once per row block.
+#include <mutex>
+
 #include "rtq_device.h"
 #include "rtq_internal.h"
 
@@ -795,7 +797,9 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
 }
 
 void release_threshold_once(int device) {
+    static std::mutex mu;
     static bool done[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
     if (device < 0 || device >= 64 || done[device]) return;
     hipMemPool_t pool;
     if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
