@@ -3,11 +3,13 @@
 // The packed weights are streamed once per output tile, unpacked and
 // dequantized in registers while the tile is staged into LDS (int4: code*s+m
 // with the group's fp16 pair; int8: the integer itself, the row scale being
-// applied once in the epilogue since it factors out of the K sum), and the
-// contraction runs on the fp32 MFMA (v_mfma_f32_16x16x4_f32) with fp32
-// accumulators. The format is that of the RT-J int4 / int8 model cards,
-// section "Quantization format"; the dequantize-inside-the-GEMM design is the
-// one their opening paragraphs describe.
+// applied once in the epilogue since it factors out of the K sum; FP8: the
+// E4M3 value), and the contraction runs on the fp32 MFMA
+// (v_mfma_f32_16x16x4_f32) with fp32 accumulators. The formats are those of
+// the RT-J int4 / int8 model cards, section "Quantization format", and of the
+// FP8 card, section "FP8 Format"; the dequantize-inside-the-GEMM design is the
+// one their opening paragraphs describe. These kernels write x . W^T; a bias
+// is added afterwards by the finish pass (launch_bias_add).
 #include <vector>
 
 #include "rtq_device.h"

@@ -1,20 +1,22 @@
 // Dequant-in-GEMM on the bf16 matrix cores with exact fp32 products.
 //
-// y[M][N] = x[M][K] . W^T with W in its packed int4 / int8 form (RT-J int4 and
-// int8 model cards, section "Quantization format"), dequantized inside the
-// GEMM as the cards' opening paragraphs describe.
+// y[M][N] = x[M][K] . W^T (+ bias) with W in its packed int4 / int8 form (RT-J
+// int4 and int8 model cards, section "Quantization format") or as FP8 E4M3
+// codes (RT-J FP8 card, section "FP8 Format"), dequantized inside the GEMM as
+// the cards' opening paragraphs describe.
 //
 // Arithmetic. Every fp32 activation is split, exactly, into three bf16 limbs:
 //   x1 = x with the low 16 bits of its encoding cleared  (top 8 significant bits)
 //   r  = x - x1                                           (exact, <= 16 bits)
 //   x2 = r with the low 16 bits cleared, x3 = r - x2      (x3 has <= 8 bits: exact in bf16)
-// so x == x1 + x2 + x3. The int4 codes (0..15) and int8 codes (-127..127) are
-// exact in bf16, so every product code * limb is exact in fp32, and
-// v_mfma_f32_16x16x32_bf16 accumulates them in fp32: the per-group code sum
-// P_g[m][o] = sum_{k in g} code[o][k] * x[m][k] is an fp32 dot product of the
-// exact values. One MFMA covers exactly one 32-wide int4 group, so
+// so x == x1 + x2 + x3. The int4 codes (0..15), int8 codes (-127..127) and
+// E4M3 values are exact in bf16, so every product code * limb is exact in
+// fp32, and v_mfma_f32_16x16x32_bf16 accumulates them in fp32: the per-group
+// code sum P_g[m][o] = sum_{k in g} code[o][k] * x[m][k] is an fp32 dot product
+// of the exact values. One MFMA covers exactly one 32-wide int4 group, so
 //   int4: y = sum_g scale_g[o] * P_g  +  sum_g min_g[o] * X_g[m],   X_g[m] = sum_{k in g} x[m][k]
 //   int8: y = scale[o] * sum_k q[o][k] * x[m][k]
+//   FP8:  y = sum_k w[o][k] * x[m][k]
 // which is W = code*scale + min (int4) and W = q*scale (int8) by
 // distributivity. The scale term is one fp32 FMA per output per group on the
 // VALU; the min term is a K/32-long contraction run on the fp32 matrix cores
@@ -26,15 +28,20 @@
 // fp32 accumulation; the group sums X_g are those of the rounded values.
 //
 // Data movement.
-//  1. A pre-pass splits every distinct activation once into a limb image in a
-//     device workspace (three bf16 planes in MFMA operand order with an XOR
-//     swizzle that makes the LDS reads conflict-free, plus the group sums X_g).
-//  2. The GEMM streams each 32-wide group of its row block from that image into
-//     a three-stage LDS ring with global_load_lds_dwordx4 (direct to LDS: no
-//     registers, no VALU), one group ahead of the compute, one barrier per group.
-//  3. Each wave streams its own packed weight columns from global memory into
-//     registers in MFMA operand layout (4 bytes of int4 codes or 8 bytes of int8
-//     codes per lane per group): the packed payload is read once per row block.
+//  1. A pre-pass (prep_kernel) splits every distinct activation once into a
+//     limb image in a device workspace: NL bf16 planes in MFMA operand order,
+//     with an XOR swizzle that makes the LDS reads conflict-free, plus X_g.
+//  2. The GEMM copies each 32-wide group of its row block from that image into
+//     an LDS ring with global_load_lds_dwordx4 (direct to LDS: no registers, no
+//     VALU), ahead of the compute, one barrier per group.
+//  3. Weights. Small M (split_grouped_kernel, every projection of the call in
+//     one launch): each wave copies its rows as 16-byte (row, group) records
+//     into a private LDS ring, two groups per copy, a chunk ahead; K is cut into
+//     chunks of at most 16 groups, and finish_kernel sums the chunks' partials
+//     in order (and adds biases). Large M (split_gemm_kernel, 128 x 128 tiles):
+//     each wave loads its codes into registers one group ahead, from L2.
+//  4. Workgroup ids are remapped so that each XCD runs a contiguous range of
+//     tiles: the tiles that share an activation image share that XCD's L2.
 #include <mutex>
 
 #include "rtq_device.h"
