@@ -10,6 +10,7 @@ from __future__ import annotations
 
 import hashlib
 import os
+import re
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h")
@@ -36,11 +37,20 @@ RECORDS: dict = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank space: what the compiler sees
+    (the kernel sources hold no string literals with comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def sources_sha256() -> str:
+    """SHA-256 of the kernel sources' code (comments and layout ignored)."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(CSRC, name)) as f:
+            h.update(name.encode() + b"\0" + _code_only(f.read()).encode())
     return h.hexdigest()
 
 
