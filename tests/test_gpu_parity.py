@@ -395,3 +395,37 @@ def test_full_size_twelve_blocks_sampled(M, heavy, math):
     say(f"  worst sampled rel err {worst:.3e}")
     del blocks
     torch.cuda.empty_cache()
+
+
+def test_calls_run_on_the_callers_streams():
+    """Two 12-projection calls issued back to back on two non-default streams
+    (each with its own workspace), then a third on the first stream that reuses
+    the outputs of the first as inputs only after an event: every result equals
+    the oracle's, so each call ran in its own stream's order."""
+    M = 80
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()     # default priority
+    torch.cuda.synchronize()
+    calls = []
+    for cfg, st in ((6, s1), (7, s2)):
+        blk, refs, xs = make_block(cfg, 0, 0, M, rtq.RECIPE_MIXED)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(st):
+            rtq.block_project([blk], M, stream=st)
+        calls.append((blk, refs, xs, st))
+    # chain on s1: the wq output of call 1 feeds a second int8 projection
+    blk1, refs1, xs1, _ = calls[0]
+    W = synth.weight(8, 0, 0, "wo")
+    w = gpu_quantize(W, "q8")
+    ref_w = oracle.quantize(W, "q8")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        y2 = torch.empty((M, 512), dtype=torch.float32, device=DEV)
+        rtq.block_project([{"wo": rtq.Projection(w, blk1["wq"].y, y2)}], M, stream=s1)
+    s1.synchronize()
+    s2.synchronize()
+    for blk, refs, xs, _ in calls:
+        for name, (fmt, ref, xin) in refs.items():
+            err = oracle.rel_fro(host(blk[name].y), oracle.project(fmt, xs[xin], *ref))
+            assert err <= TOL, (name, err)
+    x2 = host(blk1["wq"].y)
+    assert oracle.rel_fro(host(y2), oracle.project("q8", x2, *ref_w)) <= TOL
