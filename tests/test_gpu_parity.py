@@ -429,3 +429,22 @@ def test_calls_run_on_the_callers_streams():
             assert err <= TOL, (name, err)
     x2 = host(blk1["wq"].y)
     assert oracle.rel_fro(host(y2), oracle.project("q8", x2, *ref_w)) <= TOL
+
+
+@pytest.mark.parametrize("M,K", [(80, 512), (200, 96), (17, 40)])
+def test_f8_nan_code_makes_its_column_nan(M, K, math):
+    """An E4M3 NaN code (S.1111.111) in row o of W makes column o of y NaN in
+    every row; every other column still matches the oracle."""
+    N = 48
+    W = synth.weight(18, 0, 0, "wq", N, K)
+    codes = oracle.quantize_f8(W)
+    codes[5, K // 3] = 0x7F
+    codes[31, K - 1] = 0xFF
+    x = synth.activation(18, 0, "x_attn", M, K)
+    y = host(rtq.gemm_f8(dev(x), rtq.F8Weight(dev(codes))))
+    nan_cols = np.zeros(N, dtype=bool)
+    nan_cols[[5, 31]] = True
+    assert np.isnan(y[:, nan_cols]).all()
+    assert np.isfinite(y[:, ~nan_cols]).all()
+    ref = oracle.project_f8(x, codes)
+    assert oracle.rel_fro(y[:, ~nan_cols], ref[:, ~nan_cols]) <= TOL
