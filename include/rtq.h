@@ -24,10 +24,21 @@
  *     scale    float32 [N]          scale[o] = max|W[o][:]| / 127
  *     W[o][i] = q[o][i] * scale[o]
  *
+ *   FP8 E4M3 ("RT-J - FP8 E4M3 checkpoints", section "FP8 Format"): one
+ *   float8_e4m3fn code per weight, no scale.
+ *     codes    uint8   [N][K]       W[o][i] = the E4M3 value of codes[o][i]
+ *
  * Conventions for every call below:
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
- *     never allocates, frees or retains device memory and keeps no state
- *     besides a thread-local error string.
+ *     never retains a caller's pointer past the call's work on its stream.
+ *   - Memory and state of the library itself: a GEMM call on the split path
+ *     takes one stream-ordered workspace (limb images of x, K-chunk partials)
+ *     with hipMallocAsync on the caller's stream from the device's default
+ *     memory pool and returns it with hipFreeAsync on the same stream; the
+ *     pool's release threshold is raised once per device, so steady-state
+ *     calls reuse pool memory. Process-wide state: the arithmetic mode
+ *     (rtq_set_math) and the timing events (rtq_timing_enable); per thread:
+ *     the last error message.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
  *     selects the null stream). Nothing is synchronized. Faults during
  *     execution surface at the caller's next synchronization.
@@ -35,7 +46,7 @@
  *     returns its status and launches nothing. rtq_last_error() then holds a
  *     message naming the argument.
  *   - M == 0 is a no-op returning RTQ_OK. N >= 1 and K >= 1 are required;
- *     M, N, K must each be below 2^31.
+ *     M, N, K must each be below 2^31 and M*N, M*K, N*K at most 2^44.
  *   - Base pointers must be 16-byte aligned (4-byte for scale / pair arrays).
  *   - The output must not overlap any input. Inputs may alias each other.
  *   - Launch failures return RTQ_ERR_HIP with the runtime's message copied

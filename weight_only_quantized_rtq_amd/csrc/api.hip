@@ -33,6 +33,10 @@ rtq_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Largest element count of one tensor (64 TB of fp32, beyond any device):
+// with every dimension below 2^31 the products below cannot overflow, and the
+// byte ranges of the overlap checks (elements * 4) stay far below 2^63.
+constexpr int64_t kMaxElems = int64_t(1) << 44;
 
 std::atomic<int> g_math{rtq::kMathSplitBf16};
 
@@ -55,6 +59,9 @@ rtq_status check_proj(const char* name, int fmt, const float* x, const void* pay
     if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: M=%lld out of range [0, 2^31)", name, (long long)M);
     if (N < 1 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [1, 2^31)", name, (long long)N);
     if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems)
+        return fail(RTQ_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld exceed 2^44 elements in one tensor", name,
+                    (long long)M, (long long)N, (long long)K);
     if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
         return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
     if (M == 0) return RTQ_OK;
@@ -79,6 +86,8 @@ rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, con
                     int64_t N, int64_t K) {
     if (N < 0 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [0, 2^31)", name, (long long)N);
     if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (N * K > kMaxElems)
+        return fail(RTQ_ERR_SHAPE, "%s: N=%lld K=%lld exceed 2^44 elements", name, (long long)N, (long long)K);
     if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
         return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
     if (N == 0) return RTQ_OK;
@@ -293,7 +302,7 @@ rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* 
 
 rtq_status rtq_dequant_q8(const int8_t* q, const float* scale, float* w, int64_t N, int64_t K, void* stream) {
     clear_error();
-    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "rtq_dequant_q8: N=%lld K=%lld out of range", (long long)N, (long long)K);
     if (N == 0) return RTQ_OK;
     if (!q || !scale || !w) return fail(RTQ_ERR_NULL, "rtq_dequant_q8: a pointer argument is NULL");
@@ -313,7 +322,7 @@ rtq_status rtq_quantize_q4(const float* w, uint8_t* payload, uint16_t* pairs, in
 
 rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, int64_t K, void* stream) {
     clear_error();
-    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "rtq_quantize_q8: N=%lld K=%lld out of range", (long long)N, (long long)K);
     if (N == 0) return RTQ_OK;
     if (!w || !q || !scale) return fail(RTQ_ERR_NULL, "rtq_quantize_q8: a pointer argument is NULL");
@@ -324,7 +333,7 @@ rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N, i
 
 rtq_status rtq_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, void* stream) {
     clear_error();
-    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "rtq_dequant_f8: N=%lld K=%lld out of range", (long long)N, (long long)K);
     if (N == 0) return RTQ_OK;
     if (!codes || !w) return fail(RTQ_ERR_NULL, "rtq_dequant_f8: a pointer argument is NULL");
@@ -337,7 +346,7 @@ rtq_status rtq_dequant_f8(const uint8_t* codes, float* w, int64_t N, int64_t K, 
 
 rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, void* stream) {
     clear_error();
-    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim)
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "rtq_quantize_f8: N=%lld K=%lld out of range", (long long)N, (long long)K);
     if (N == 0) return RTQ_OK;
     if (!w || !codes) return fail(RTQ_ERR_NULL, "rtq_quantize_f8: a pointer argument is NULL");
