@@ -159,6 +159,9 @@ def _need(t: torch.Tensor, dtype: torch.dtype, name: str) -> None:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        # the library launches on the current device's streams
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
 
