@@ -33,10 +33,11 @@ rtq_status hip_status(hipError_t e, const char* what) {
 }
 
 constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
-// Largest element count of one tensor (64 TB of fp32, beyond any device):
-// with every dimension below 2^31 the products below cannot overflow, and the
-// byte ranges of the overlap checks (elements * 4) stay far below 2^63.
-constexpr int64_t kMaxElems = int64_t(1) << 44;
+// Largest element count of one tensor (1 TB of fp32, beyond any device):
+// with every dimension below 2^31 the products below cannot overflow, the
+// byte ranges of the overlap checks (elements * 4) stay far below 2^63, and
+// every kernel grid and tile count derived from a tensor fits 32 bits.
+constexpr int64_t kMaxElems = int64_t(1) << 38;
 
 std::atomic<int> g_math{rtq::kMathSplitBf16};
 
@@ -60,7 +61,7 @@ rtq_status check_proj(const char* name, int fmt, const float* x, const void* pay
     if (N < 1 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [1, 2^31)", name, (long long)N);
     if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
     if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems)
-        return fail(RTQ_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld exceed 2^44 elements in one tensor", name,
+        return fail(RTQ_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld exceed 2^38 elements in one tensor", name,
                     (long long)M, (long long)N, (long long)K);
     if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
         return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
@@ -87,7 +88,7 @@ rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, con
     if (N < 0 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [0, 2^31)", name, (long long)N);
     if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
     if (N * K > kMaxElems)
-        return fail(RTQ_ERR_SHAPE, "%s: N=%lld K=%lld exceed 2^44 elements", name, (long long)N, (long long)K);
+        return fail(RTQ_ERR_SHAPE, "%s: N=%lld K=%lld exceed 2^38 elements", name, (long long)N, (long long)K);
     if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)
         return fail(RTQ_ERR_SHAPE, "%s: K=%lld is not a multiple of the int4 group size 32", name, (long long)K);
     if (N == 0) return RTQ_OK;

@@ -20,14 +20,10 @@ constexpr int kGroup = 32;
 // operation rounded on its own (no contraction), so the codes and pairs are a
 // deterministic function of the fp32 input.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void quantize_q4_kernel(const float* __restrict__ w,
-                                                          uint8_t* __restrict__ payload,
-                                                          uint32_t* __restrict__ pairs,
-                                                          int64_t n_groups, int64_t groups_per_row,
-                                                          int64_t K) {
+__device__ __forceinline__ void quantize_q4_group(const float* __restrict__ w, uint8_t* __restrict__ payload,
+                                                  uint32_t* __restrict__ pairs, int64_t gid,
+                                                  int64_t groups_per_row, int64_t K) {
 #pragma clang fp contract(off)
-    const int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (gid >= n_groups) return;
     const int64_t row = gid / groups_per_row;
     const int64_t grp = gid - row * groups_per_row;
     const float4* src = reinterpret_cast<const float4*>(w + row * K + grp * kGroup);
@@ -91,6 +87,16 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const float* __restric
     pairs[gid] = best_pair;
 }
 
+__global__ __launch_bounds__(256) void quantize_q4_kernel(const float* __restrict__ w,
+                                                          uint8_t* __restrict__ payload,
+                                                          uint32_t* __restrict__ pairs,
+                                                          int64_t n_groups, int64_t groups_per_row,
+                                                          int64_t K) {
+    for (int64_t gid = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; gid < n_groups;
+         gid += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        quantize_q4_group(w, payload, pairs, gid, groups_per_row, K);
+}
+
 // ---------------------------------------------------------------------------
 // int8 quantizer: one 256-thread workgroup per row.
 // ---------------------------------------------------------------------------
@@ -129,33 +135,36 @@ __global__ __launch_bounds__(256) void dequant_q4_kernel(const uint32_t* __restr
                                                          const uint32_t* __restrict__ pairs,
                                                          float* __restrict__ w, int64_t n_words,
                                                          int64_t words_per_row, int64_t K) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= n_words) return;
-    const int64_t row = t / words_per_row;
-    const int64_t word = t - row * words_per_row;       // covers k = 8*word .. 8*word+7
-    const uint32_t bits = payload[t];
-    const uint32_t pr = pairs[row * (K / kGroup) + (word * 8) / kGroup];
-    const float s = half_bits_to_float(pr & 0xffffu);
-    const float m = half_bits_to_float(pr >> 16);
-    float o[8];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < n_words;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x) {
+        const int64_t row = t / words_per_row;
+        const int64_t word = t - row * words_per_row;       // covers k = 8*word .. 8*word+7
+        const uint32_t bits = payload[t];
+        const uint32_t pr = pairs[row * (K / kGroup) + (word * 8) / kGroup];
+        const float s = half_bits_to_float(pr & 0xffffu);
+        const float m = half_bits_to_float(pr >> 16);
+        float o[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = fmaf(static_cast<float>(nibble(bits, i)), s, m);
-    float4* dst = reinterpret_cast<float4*>(w + row * K + word * 8);
-    dst[0] = make_float4(o[0], o[1], o[2], o[3]);
-    dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+        for (int i = 0; i < 8; ++i) o[i] = fmaf(static_cast<float>(nibble(bits, i)), s, m);
+        float4* dst = reinterpret_cast<float4*>(w + row * K + word * 8);
+        dst[0] = make_float4(o[0], o[1], o[2], o[3]);
+        dst[1] = make_float4(o[4], o[5], o[6], o[7]);
+    }
 }
 
 __global__ __launch_bounds__(256) void dequant_q8_kernel(const int8_t* __restrict__ q,
                                                          const float* __restrict__ scale,
                                                          float* __restrict__ w, int64_t total, int64_t K) {
-    const int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-    if (t >= total) return;
-    const int64_t row = t / K;
-    w[t] = static_cast<float>(q[t]) * scale[row];
+    for (int64_t t = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; t < total;
+         t += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        w[t] = static_cast<float>(q[t]) * scale[t / K];
 }
 
+// Grid of an element-wise kernel (every one loops grid-stride): enough
+// workgroups to cover n items once, at most 2^20.
 inline unsigned blocks_for(int64_t n, int per) {
-    return static_cast<unsigned>((n + per - 1) / per);
+    const int64_t b = (n + per - 1) / per;
+    return static_cast<unsigned>(b < (int64_t(1) << 20) ? (b > 0 ? b : 1) : (int64_t(1) << 20));
 }
 
 // FP8 E4M3 codes of fp32 weights, as a cast to PyTorch's float8_e4m3fn gives
