@@ -46,7 +46,7 @@
  *     returns its status and launches nothing. rtq_last_error() then holds a
  *     message naming the argument.
  *   - M == 0 is a no-op returning RTQ_OK. N >= 1 and K >= 1 are required;
- *     M, N, K must each be below 2^31 and M*N, M*K, N*K at most 2^38.
+ *     M, N, K must each be below 2^30 and M*N, M*K, N*K at most 2^38.
  *   - Base pointers must be 16-byte aligned (4-byte for scale / pair arrays).
  *   - The output must not overlap any input. Inputs may alias each other.
  *   - Launch failures return RTQ_ERR_HIP with the runtime's message copied

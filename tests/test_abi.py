@@ -79,12 +79,14 @@ def test_shape_errors(lib):
 def test_element_count_limit(lib):
     """Products of the dimensions are capped (2^38 elements per tensor) before
     any byte-range arithmetic, so no overflow reaches the overlap checks."""
-    assert call_q4(lib, M=2**30, N=2**30, K=64) == ERR_SHAPE
+    assert call_q4(lib, M=2**29, N=2**29, K=64) == ERR_SHAPE
     assert b"2^38" in lib.rtq_last_error()
-    assert call_q8(lib, M=2, N=2**31 - 1, K=2**31 - 1) == ERR_SHAPE
-    assert lib.rtq_dequant_q8(B, C, A, 2**30, 2**30, None) == ERR_SHAPE
-    assert lib.rtq_quantize_f8(A, B, 2**31 - 1, 2**31 - 1, None) == ERR_SHAPE
-    assert lib.rtq_quantize_q4(A, B, C, 2**30, 2**30, None) == ERR_SHAPE
+    assert call_q8(lib, M=2, N=2**29, K=2**29) == ERR_SHAPE
+    assert lib.rtq_dequant_q8(B, C, A, 2**29, 2**29, None) == ERR_SHAPE
+    assert lib.rtq_quantize_f8(A, B, 2**29, 2**29, None) == ERR_SHAPE
+    assert lib.rtq_quantize_q4(A, B, C, 2**29, 2**29, None) == ERR_SHAPE
+    # each dimension below 2^30
+    assert call_q4(lib, M=2**30) == ERR_SHAPE and call_q8(lib, N=2**30) == ERR_SHAPE
 
 
 def test_m_zero_is_a_noop(lib):

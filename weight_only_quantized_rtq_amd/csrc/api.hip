@@ -32,7 +32,9 @@ rtq_status hip_status(hipError_t e, const char* what) {
     return fail(RTQ_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+// Largest dimension: kernels form padded row and column indices (up to a
+// dimension plus a tile) in 32-bit integers.
+constexpr int64_t kMaxDim = (int64_t(1) << 30) - 1;
 // Largest element count of one tensor (1 TB of fp32, beyond any device):
 // with every dimension below 2^31 the products below cannot overflow, the
 // byte ranges of the overlap checks (elements * 4) stay far below 2^63, and
@@ -57,9 +59,9 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi && a.lo != a
 // Checks shared by the projection entry points. `name` prefixes messages.
 rtq_status check_proj(const char* name, int fmt, const float* x, const void* payload,
                       const void* scale, const float* y, int64_t M, int64_t N, int64_t K) {
-    if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: M=%lld out of range [0, 2^31)", name, (long long)M);
-    if (N < 1 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [1, 2^31)", name, (long long)N);
-    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (M < 0 || M > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: M=%lld out of range [0, 2^30)", name, (long long)M);
+    if (N < 1 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [1, 2^30)", name, (long long)N);
+    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^30)", name, (long long)K);
     if (M * N > kMaxElems || M * K > kMaxElems || N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "%s: M=%lld N=%lld K=%lld exceed 2^38 elements in one tensor", name,
                     (long long)M, (long long)N, (long long)K);
@@ -85,8 +87,8 @@ rtq_status check_proj(const char* name, int fmt, const float* x, const void* pay
 
 rtq_status check_nk(const char* name, int fmt, const void* a, const void* b, const void* c,
                     int64_t N, int64_t K) {
-    if (N < 0 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [0, 2^31)", name, (long long)N);
-    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^31)", name, (long long)K);
+    if (N < 0 || N > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: N=%lld out of range [0, 2^30)", name, (long long)N);
+    if (K < 1 || K > kMaxDim) return fail(RTQ_ERR_SHAPE, "%s: K=%lld out of range [1, 2^30)", name, (long long)K);
     if (N * K > kMaxElems)
         return fail(RTQ_ERR_SHAPE, "%s: N=%lld K=%lld exceed 2^38 elements", name, (long long)N, (long long)K);
     if (fmt == rtq::kFmtQ4 && K % RTQ_Q4_GROUP != 0)

@@ -523,7 +523,7 @@ hipError_t launch_one_untimed(const TileArgs& a, hipStream_t stream) {
         gemm_kernel<FMT, 1, 4, 5, 2, SAFE><<<tm * tn, Small::NT, 0, stream>>>(a, tn, 0);
     } else {
         const int tn = (a.N + Large::BN - 1) / Large::BN;
-        const int tm = (a.M + Large::BM - 1) / Large::BM;
+        const int tm = static_cast<int>((int64_t(a.M) + Large::BM - 1) / Large::BM);
         gemm_kernel<FMT, 2, 2, 4, 4, SAFE><<<tm * tn, Large::NT, 0, stream>>>(a, tn, 1);
     }
     return hipGetLastError();

@@ -852,7 +852,7 @@ void launch_large(int fmt, int blocks, const SplitArgs& a, int tn, hipStream_t s
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream) {
     if (NL != 1 && NL != 3) return hipErrorInvalidValue;
     const int M = static_cast<int>(M64);
-    const int tm_small = (M + 15) / 16;
+    const int tm_small = static_cast<int>((int64_t(M) + 15) / 16);
     // The grouped small-M launch addresses the limb images by 32-bit offsets;
     // a call whose images would not fit (enormous K) takes the tiled path.
     bool small = M <= 80;
@@ -862,7 +862,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
     int n_in = 0;
     int64_t ws_bytes = 0;
     for (;;) {
-        RB = small ? tm_small : ((M + kLBM - 1) / kLBM) * (kLBM / 16);
+        RB = small ? tm_small : static_cast<int>((int64_t(M) + kLBM - 1) / kLBM) * (kLBM / 16);
         // Distinct inputs (pointer, K).
         n_in = 0;
         ws_bytes = 0;
@@ -962,7 +962,7 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             const SplitArgs a{wsb + inputs[img_of[i]].offset, t.payload, t.scale, t.y, M, t.N, t.K, RB, 0, t.K / 32,
                               t.bias};
             const int tn = (t.N + kLBN - 1) / kLBN;
-            const int tmb = (M + kLBM - 1) / kLBM;
+            const int tmb = static_cast<int>((int64_t(M) + kLBM - 1) / kLBM);
             const int mark = timing_begin(stream);
             if (NL == 1)
                 launch_large<1>(t.fmt, tmb * tn, a, tn, stream);
