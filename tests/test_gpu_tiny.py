@@ -1,0 +1,144 @@
+"""GPU parity of the tiny-M path (M <= 16 and K in {256, 512, 1024, 2048}):
+one launch, whole K per workgroup, x stages built in the kernel. Checked
+against the oracle in every arithmetic mode (the bf16 mode against its own
+bf16(x) reference at 1e-5 and fp32 x at 3e-3), at ragged N, every K the path
+takes, M from 1 to 16, with and without biases, and through the block
+projection at the benchmark's shapes."""
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle  # noqa: E402
+import synth  # noqa: E402
+import weight_only_quantized_rtq_amd as rtq  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+MODES = {"split_bf16": rtq.MATH_SPLIT_BF16, "fp32_mfma": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16}
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+@pytest.fixture(params=list(MODES), ids=list(MODES))
+def mode(request):
+    rtq.set_math(MODES[request.param])
+    yield request.param
+    rtq.set_math(rtq.MATH_SPLIT_BF16)
+
+
+def check(y, mode, fmt, x, ref, b=None):
+    bias = 0.0 if b is None else b.astype(np.float64)[None, :]
+    if mode == "bf16":
+        tight = oracle.rel_fro(y, oracle.project_bf16(fmt, x, *ref) + bias)
+        assert tight <= 1e-5, ("against bf16(x)", tight)
+        loose = oracle.rel_fro(y, oracle.project(fmt, x, *ref) + bias)
+        assert loose <= 3e-3, ("against fp32 x", loose)
+    else:
+        err = oracle.rel_fro(y, oracle.project(fmt, x, *ref) + bias)
+        assert err <= 1e-5, err
+
+
+CASES = [(fmt, M, N, K) for fmt in ("q4", "q8", "f8")
+         for (M, N, K) in [(1, 512, 512), (3, 100, 256), (5, 300, 1024), (16, 520, 2048), (8, 64, 2048),
+                           (16, 257, 512), (2, 17, 1024)]]
+
+
+@pytest.mark.parametrize("fmt,M,N,K", CASES)
+def test_tiny_gemm_parity(fmt, M, N, K, mode):
+    say(f"tiny {fmt} M={M} N={N} K={K} mode={mode}")
+    W = synth.weight(61, 0, 0, "w1", N, K, heavy="rows")
+    x = synth.activation(61, 0, "x_ffn", M, K)
+    ref = oracle.quantize(W, fmt)
+    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt)))
+    check(y, mode, fmt, x, ref)
+
+
+@pytest.mark.parametrize("M", [1, 16])
+def test_tiny_block_project_twelve_blocks_with_biases(M, mode):
+    """The benchmark's 12 blocks (mixed recipe) at small M, biases on half the
+    projections, every output checked."""
+    say(f"tiny 12 blocks M={M} mode={mode}")
+    blocks, refs = [], []
+    for b in range(synth.NUM_BLOCKS):
+        xs = {n: synth.activation(62, b, n, M) for n in synth.INPUT_WIDTH}
+        dxs = {n: dev(v) for n, v in xs.items()}
+        blk, ref = {}, {}
+        for j, name in enumerate(synth.PROJ_ORDER):
+            N, K, xin = synth.BLOCK_SHAPES[name]
+            W = synth.weight(62, 0, b, name)
+            fmt = rtq.RECIPE_MIXED[name]
+            bias = synth.activation(63, b, "h", 1, N)[0] if (b + j) % 2 == 0 else None
+            blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), dxs[xin],
+                                       torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV),
+                                       None if bias is None else dev(bias))
+            ref[name] = (fmt, oracle.quantize(W, fmt), xs[xin], bias)
+        blocks.append(blk)
+        refs.append(ref)
+    rtq.block_project(blocks, M)
+    for b in range(synth.NUM_BLOCKS):
+        for name, (fmt, r, x, bias) in refs[b].items():
+            check(host(blocks[b][name].y), mode, fmt, x, r, bias)
+
+
+def test_tiny_exact_integer_and_identity():
+    """Integer x and dyadic (scale, min): bit-exact; x = rows of I: y = W^T rows, bit for bit."""
+    M, N, K = 16, 256, 512
+    x = synth.uniform_ints(M, (M, K), -4, 4).astype(np.float32)
+    payload = synth.uniform_bytes(N, (N, K // 2))
+    pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
+    pairs[..., 0] = 0.25
+    pairs[..., 1] = -2.0
+    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs))))
+    assert np.array_equal(y.astype(np.float64), oracle.project_q4(x, payload, pairs))
+    W = synth.weight(64, 0, 0, "wq", 96, 256, heavy="rows")
+    for fmt in ("q4", "q8", "f8"):
+        ref = oracle.quantize(W, fmt)
+        eye = np.eye(256, dtype=np.float32)
+        for r0 in (0, 240):                               # two 16-row windows of the identity
+            yi = host(rtq.gemm(dev(eye[r0:r0 + 16]), rtq.quantize(dev(W), fmt)))
+            want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T[r0:r0 + 16])
+            assert np.array_equal(yi, want), fmt
+
+
+def test_tiny_full_size_weight_sets_sampled():
+    """The m80 weight-set shapes at M = 8 (12 blocks, 16 sets) in the benchmark's
+    launch configuration, sampled outputs against the oracle."""
+    M = 8
+    rng = np.random.default_rng(65)
+    for s in (0, 15):
+        blocks, refs = [], []
+        for b in range(synth.NUM_BLOCKS):
+            xs = {n: synth.activation(4, b, n, M) for n in synth.INPUT_WIDTH}
+            dxs = {n: dev(v) for n, v in xs.items()}
+            blk, ref = {}, {}
+            for name in synth.PROJ_ORDER:
+                N, K, xin = synth.BLOCK_SHAPES[name]
+                W = synth.weight(4, s, b, name)
+                fmt = rtq.RECIPE_MIXED[name]
+                blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), dxs[xin],
+                                           torch.empty((M, N), dtype=torch.float32, device=DEV))
+                ref[name] = (fmt, W, xs[xin])
+            blocks.append(blk)
+            refs.append(ref)
+        rtq.block_project(blocks, M)
+        torch.cuda.synchronize()
+        for b in range(synth.NUM_BLOCKS):
+            for name, (fmt, W, x) in refs[b].items():
+                cols = np.sort(rng.choice(W.shape[0], 32, replace=False))
+                ref_w = oracle.quantize(W[cols], fmt)
+                y = host(blocks[b][name].y[:, torch.as_tensor(cols, device=DEV)])
+                assert oracle.rel_fro(y, oracle.project(fmt, x, *ref_w)) <= 1e-5, (s, b, name)
