@@ -1,9 +1,11 @@
-"""GPU parity of the tiny-M path (M <= 16 and K in {256, 512, 1024, 2048}):
-one launch, whole K per workgroup, x stages built in the kernel. Checked
-against the oracle in every arithmetic mode (the bf16 mode against its own
-bf16(x) reference at 1e-5 and fp32 x at 3e-3), at ragged N, every K the path
-takes, M from 1 to 16, with and without biases, and through the block
-projection at the benchmark's shapes."""
+"""GPU parity of the direct small-M path (M <= 32 and K in {256, 512, 1024,
+2048}): one launch, whole K per workgroup, x stages built in the kernel, one
+or two row tiles. Checked against the oracle in every arithmetic mode (the
+bf16 mode against its own bf16(x) reference at 1e-5 and fp32 x at 3e-3), at
+ragged N, every K the path takes, M from 1 to 32 on both sides of the row tile
+boundary, with and without biases, and through the block projection at the
+benchmark's shapes. The cases with M above 32 check the hand-off to the
+grouped kernel (pre-pass, K chunks) at the same shapes."""
 import sys
 
 import numpy as np
@@ -54,12 +56,14 @@ def check(y, mode, fmt, x, ref, b=None):
 
 CASES = [(fmt, M, N, K) for fmt in ("q4", "q8", "f8")
          for (M, N, K) in [(1, 512, 512), (3, 100, 256), (5, 300, 1024), (16, 520, 2048), (8, 64, 2048),
-                           (16, 257, 512), (2, 17, 1024)]]
+                           (16, 257, 512), (2, 17, 1024),
+                           (17, 300, 512), (32, 257, 1024), (33, 100, 2048), (48, 520, 256),
+                           (49, 64, 512), (64, 130, 2048), (80, 512, 512), (80, 96, 1024), (79, 33, 256)]]
 
 
 @pytest.mark.parametrize("fmt,M,N,K", CASES)
-def test_tiny_gemm_parity(fmt, M, N, K, mode):
-    say(f"tiny {fmt} M={M} N={N} K={K} mode={mode}")
+def test_direct_gemm_parity(fmt, M, N, K, mode):
+    say(f"direct {fmt} M={M} N={N} K={K} mode={mode}")
     W = synth.weight(61, 0, 0, "w1", N, K, heavy="rows")
     x = synth.activation(61, 0, "x_ffn", M, K)
     ref = oracle.quantize(W, fmt)
@@ -67,11 +71,11 @@ def test_tiny_gemm_parity(fmt, M, N, K, mode):
     check(y, mode, fmt, x, ref)
 
 
-@pytest.mark.parametrize("M", [1, 16])
-def test_tiny_block_project_twelve_blocks_with_biases(M, mode):
+@pytest.mark.parametrize("M", [1, 16, 40, 80])
+def test_direct_block_project_twelve_blocks_with_biases(M, mode):
     """The benchmark's 12 blocks (mixed recipe) at small M, biases on half the
     projections, every output checked."""
-    say(f"tiny 12 blocks M={M} mode={mode}")
+    say(f"direct 12 blocks M={M} mode={mode}")
     blocks, refs = [], []
     for b in range(synth.NUM_BLOCKS):
         xs = {n: synth.activation(62, b, n, M) for n in synth.INPUT_WIDTH}
@@ -94,9 +98,10 @@ def test_tiny_block_project_twelve_blocks_with_biases(M, mode):
             check(host(blocks[b][name].y), mode, fmt, x, r, bias)
 
 
-def test_tiny_exact_integer_and_identity():
+@pytest.mark.parametrize("M", [16, 80])
+def test_direct_exact_integer_and_identity(M):
     """Integer x and dyadic (scale, min): bit-exact; x = rows of I: y = W^T rows, bit for bit."""
-    M, N, K = 16, 256, 512
+    N, K = 256, 512
     x = synth.uniform_ints(M, (M, K), -4, 4).astype(np.float32)
     payload = synth.uniform_bytes(N, (N, K // 2))
     pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
@@ -108,16 +113,17 @@ def test_tiny_exact_integer_and_identity():
     for fmt in ("q4", "q8", "f8"):
         ref = oracle.quantize(W, fmt)
         eye = np.eye(256, dtype=np.float32)
-        for r0 in (0, 240):                               # two 16-row windows of the identity
-            yi = host(rtq.gemm(dev(eye[r0:r0 + 16]), rtq.quantize(dev(W), fmt)))
-            want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T[r0:r0 + 16])
+        for r0 in (0, 256 - M):                           # two M-row windows of the identity
+            yi = host(rtq.gemm(dev(eye[r0:r0 + M]), rtq.quantize(dev(W), fmt)))
+            want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T[r0:r0 + M])
             assert np.array_equal(yi, want), fmt
 
 
-def test_tiny_full_size_weight_sets_sampled():
-    """The m80 weight-set shapes at M = 8 (12 blocks, 16 sets) in the benchmark's
-    launch configuration, sampled outputs against the oracle."""
-    M = 8
+@pytest.mark.parametrize("M", [8, 80])
+def test_direct_full_size_weight_sets_sampled(M):
+    """The benchmark's weight-set shapes (12 blocks, two of the 16 sets) at M = 8
+    and at M = 80, the benchmark's own launch configuration, sampled outputs
+    against the oracle."""
     rng = np.random.default_rng(65)
     for s in (0, 15):
         blocks, refs = [], []

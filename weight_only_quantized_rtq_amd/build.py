@@ -10,6 +10,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -18,13 +19,13 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librtq.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_split.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_split.hip", "gemm_direct.hip"]
+OBJDIR = os.path.join(PKG, "_build")
 
 FLAGS = [
     f"--offload-arch={ARCH}",
     "-O3",
     "-std=c++17",
-    "-shared",
     "-fPIC",
     "-Wall",
     "-Wno-unused-function",
@@ -42,10 +43,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build librtq.so)")
 
 
-def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", *srcs, "-o", tmp]
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -53,6 +51,20 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{res.stdout}\n{res.stderr}")
     if verbose and res.stderr.strip():
         print(res.stderr, file=sys.stderr)
+
+
+def build(verbose: bool = False) -> str:
+    """Compiles every source to an object in parallel, then links librtq.so."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    cc = hipcc()
+    objs = [os.path.join(OBJDIR, os.path.splitext(s)[0] + ".o") for s in SOURCES]
+    cmds = [[cc, *FLAGS, f"-I{INCLUDE}", f"-I{CSRC}", "-c", os.path.join(CSRC, s), "-o", o]
+            for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=max(1, min(len(cmds), os.cpu_count() or 1))) as pool:
+        for f in [pool.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    tmp = LIB + ".tmp"
+    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, LIB)
     return LIB
 

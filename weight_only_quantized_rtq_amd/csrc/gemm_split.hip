@@ -35,7 +35,8 @@
 //     an LDS ring with global_load_lds_dwordx4 (direct to LDS: no registers, no
 //     VALU), ahead of the compute, one barrier per group.
 //  3. Weights. Small M (split_grouped_kernel, every projection of the call in
-//     one launch): each wave copies its rows as 16-byte (row, group) records
+//     one launch; calls with M <= 32 whose every K is 256, 512, 1024 or 2048
+//     run gemm_direct.hip instead): each wave copies its rows as 16-byte (row, group) records
 //     into a private LDS ring, two groups per copy, a chunk ahead; K is cut into
 //     chunks of at most 16 groups, and finish_kernel sums the chunks' partials
 //     in order (and adds biases). Large M (split_gemm_kernel, 128 x 128 tiles):
@@ -44,102 +45,12 @@
 //     tiles: the tiles that share an activation image share that XCD's L2.
 #include <mutex>
 
-#include "rtq_device.h"
 #include "rtq_internal.h"
+#include "split_device.h"
 
 namespace rtq {
 
 namespace {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint32_t fbits(float f) { return __builtin_bit_cast(uint32_t, f); }
-__device__ __forceinline__ float bitsf(uint32_t u) { return __builtin_bit_cast(float, u); }
-
-// Exact three-limb split of two fp32 values into packed bf16x2 words (element
-// a in the low half, b in the high half).
-__device__ __forceinline__ void split2(float a, float b, uint32_t& h, uint32_t& mid, uint32_t& lo) {
-    const uint32_t ha = fbits(a) & 0xffff0000u, hb = fbits(b) & 0xffff0000u;
-    const float ra = a - bitsf(ha), rb = b - bitsf(hb);
-    const uint32_t ma = fbits(ra) & 0xffff0000u, mb = fbits(rb) & 0xffff0000u;
-    const float sa = ra - bitsf(ma), sb = rb - bitsf(mb);
-    h = (ha >> 16) | hb;
-    mid = (ma >> 16) | mb;
-    lo = (fbits(sa) >> 16) | (fbits(sb) & 0xffff0000u);
-}
-
-// Value of the lane N places further along its 16-lane row (DPP row_ror:N).
-template <int N>
-__device__ __forceinline__ float row_ror(float v) {
-    static_assert(N >= 1 && N <= 15, "rotation");
-    return bitsf(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(fbits(v)), 0x120 + N, 0xf, 0xf, true)));
-}
-
-// Byte k of a word -> fp32 (v_cvt_f32_ubyte{k}: exact).
-__device__ __forceinline__ float ubyte0(uint32_t x) { float r; asm("v_cvt_f32_ubyte0 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte1(uint32_t x) { float r; asm("v_cvt_f32_ubyte1 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte2(uint32_t x) { float r; asm("v_cvt_f32_ubyte2 %0, %1" : "=v"(r) : "v"(x)); return r; }
-__device__ __forceinline__ float ubyte3(uint32_t x) { float r; asm("v_cvt_f32_ubyte3 %0, %1" : "=v"(r) : "v"(x)); return r; }
-
-// High halves of two fp32 (bf16 truncation of exact small integers) -> one bf16x2 word.
-__device__ __forceinline__ uint32_t pack_hi(float even, float odd) {
-    return __builtin_amdgcn_perm(fbits(odd), fbits(even), 0x07060302u);
-}
-
-// 8 int4 codes (one payload word, low nibble first) -> 8 bf16 (exact integers).
-__device__ __forceinline__ u32x4 codes4_to_bf16(uint32_t w) {
-    const uint32_t lo = w & 0x0f0f0f0fu;           // codes 0,2,4,6 in bytes 0..3
-    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;    // codes 1,3,5,7
-    u32x4 r;
-    r[0] = pack_hi(ubyte0(lo), ubyte0(hi));
-    r[1] = pack_hi(ubyte1(lo), ubyte1(hi));
-    r[2] = pack_hi(ubyte2(lo), ubyte2(hi));
-    r[3] = pack_hi(ubyte3(lo), ubyte3(hi));
-    return r;
-}
-
-// 8 int8 codes (two words) -> 8 bf16 (exact integers).
-__device__ __forceinline__ u32x4 codes8_to_bf16(uint32_t w0, uint32_t w1) {
-    u32x4 r;
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        const uint32_t w = d < 2 ? w0 : w1;
-        const int sh = 16 * (d & 1);
-        const float e = static_cast<float>(static_cast<int8_t>((w >> sh) & 0xffu));
-        const float o = static_cast<float>(static_cast<int8_t>((w >> (sh + 8)) & 0xffu));
-        r[d] = pack_hi(e, o);
-    }
-    return r;
-}
-
-// 8 FP8 E4M3 codes (two words, low byte first) -> 8 bf16, exactly: an E4M3
-// value has at most 4 significant bits and lies within the bf16 exponent
-// range, so the high half of its fp32 form is the value.
-__device__ __forceinline__ u32x4 codes8f_to_bf16(uint32_t w0, uint32_t w1) {
-    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
-    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
-    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
-    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);
-    u32x4 r;
-    r[0] = pack_hi(a[0], a[1]);
-    r[1] = pack_hi(b[0], b[1]);
-    r[2] = pack_hi(c[0], c[1]);
-    r[3] = pack_hi(d[0], d[1]);
-    return r;
-}
-
-__device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c,
-                                                   0, 0, 0);
-}
-
-// Nearest bf16 of two fp32 values (ties to even), packed: a low, b high.
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    const bf16x2 v = {static_cast<__bf16>(a), static_cast<__bf16>(b)};
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // ---------------------------------------------------------------------------
 // Limb image of one activation x [M][K] with NL limbs (G = K/32 groups, RB row
@@ -156,7 +67,6 @@ __host__ __device__ inline int64_t image_plane_bytes(int G, int RB, int NL) { re
 __host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
     return image_plane_bytes(G, RB, NL) + int64_t(G) * RB * 16 * 4;
 }
-__device__ __forceinline__ int swz(int r, int c) { return r * 4 + (c ^ ((r >> 2) & 3)); }
 
 constexpr int kMaxImages = 48;
 struct PrepArgs {
@@ -638,13 +548,6 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     }
 }
 
-__device__ __forceinline__ int xcd_remap_split(int w, int G) {
-    const int q = G / 8, r = G % 8;
-    const int xcd = w % 8, local = w / 8;
-    const int start = xcd < r ? xcd * (q + 1) : r * (q + 1) + (xcd - r) * q;
-    return start + local;
-}
-
 // Large M: 128 x 128 tiles, 4 waves side by side along N, each 128 rows x 32 columns.
 constexpr int kLWM = 1, kLWN = 4, kLTM = 8, kLTN = 2;
 constexpr int kLBM = kLWM * kLTM * 16;
@@ -722,375 +625,6 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
         split_tile<kFmtQ8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else
         split_tile<kFmtF8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
-}
-
-// ---------------------------------------------------------------------------
-// Tiny M (1..16 rows, K a multiple of 256): one launch, one workgroup per
-// (projection, column block) over the whole K, no pre-pass and no K chunks.
-// The column block is 64 * tn columns with tn = 4, 2, 1 for K <= 512, 1024,
-// more, so every workgroup streams about the same number of weights.
-//  - x: the workgroup builds its 16-row x stages itself, one phase of 8 groups
-//    at a time into a double-buffered LDS area (rows >= M stay zero), with one
-//    barrier per phase. Thread (h, j, kp) = (tid >> 7, tid >> 4 & 7, tid & 15)
-//    takes k = 2kp, 2kp+1 of group j of the phase for the rows h, h + 2, ...
-//    below M, splits (or rounds) them, and sums each group over its 16 lanes.
-//  - weights: each wave loads its own rows into registers in blocks of 4
-//    groups, 16 bytes per lane and load, 16/tn groups ahead in a statically
-//    indexed ring; int4 codes reach MFMA operand order through a private LDS
-//    area of the wave, with no barrier.
-// The K loop is unrolled completely (K fixed per instantiation), so the
-// compiler tracks every load and waits only for the group it uses.
-// ---------------------------------------------------------------------------
-constexpr int kTinyMaxM = 16;
-constexpr int kTinyPG = 8;          // groups per x phase
-// Weight blocks (4 groups each) in flight per wave: 4 / tn, so every wave keeps
-// about the same number of weight bytes in flight whatever its width.
-__host__ __device__ constexpr int tiny_db(int TN) { return TN >= 4 ? 1 : 4 / TN; }
-constexpr int kTinyMaxInputs = 48;
-
-template <int NL>
-struct TinyLds {
-    static constexpr int XBUF = kTinyPG * NL * 1024;    // one phase of x limbs, 16 rows
-    static constexpr int XSUM = kTinyPG * 16 * 4;       // its group sums
-    static constexpr int XTOTAL = 2 * XBUF + 2 * XSUM;
-    // per-wave int4 staging: one area per tile, 16 rows of 4 x 16 bytes of
-    // codes and the 4 (scale, min) words
-    static constexpr int STG_ROW = 80;
-    static constexpr int STG_TILE = 16 * STG_ROW;
-    static constexpr int STG = 4 * STG_TILE;
-    static constexpr int TOTAL = XTOTAL + 4 * STG;
-};
-
-__host__ __device__ constexpr int tiny_tn(int K) { return K <= 512 ? 4 : K <= 1024 ? 2 : 1; }
-// K values the tiny kernel takes: whole phases, unrolled completely (NPH = K / 256)
-// so that the compiler tracks every load exactly and keeps the weight
-// prefetch in flight.
-__host__ __device__ constexpr bool tiny_k(int K) { return K == 256 || K == 512 || K == 1024 || K == 2048; }
-
-template <int FMT, int TN, int NL, int NPH>
-__device__ __forceinline__ void tiny_tile(const float* __restrict__ x, const void* payload_v, const void* scale_v,
-                                          float* __restrict__ y, int M, int N, int n0, unsigned char* smem) {
-    using L = TinyLds<NL>;
-    constexpr int G = NPH * kTinyPG;
-    constexpr int K = G * 32;
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int li = lane & 15, lc = lane >> 4;
-
-    // ---- x stages ----
-    const int xh_ = tid >> 7;                         // rows xh_, xh_ + 2, ... (uniform per wave)
-    const int xj = (tid >> 4) & 7;                    // group of the phase
-    const int kp = tid & 15;                          // k pair 2kp, 2kp+1
-    const int nrows = M > xh_ ? (M - xh_ + 1) / 2 : 0;   // rows this thread converts
-    const float* xcol = x + xh_ * static_cast<int64_t>(K) + xj * 32 + 2 * kp;
-    float2 xr[kTinyMaxM / 2];
-    auto x_load = [&](int ph) {
-#pragma unroll
-        for (int t = 0; t < kTinyMaxM / 2; ++t)
-            if (t < nrows) xr[t] = *reinterpret_cast<const float2*>(xcol + 2 * t * static_cast<int64_t>(K) + ph * (kTinyPG * 32));
-    };
-    auto x_convert = [&](int ph) {
-        unsigned char* buf = smem + (ph & 1) * L::XBUF + xj * (NL * 1024) + (kp & 3) * 4;
-        float* sums = reinterpret_cast<float*>(smem + 2 * L::XBUF + (ph & 1) * L::XSUM) + xj * 16;
-#pragma unroll
-        for (int t = 0; t < kTinyMaxM / 2; ++t) {
-            if (t >= nrows) break;
-            const int r = xh_ + 2 * t;
-            float v0 = xr[t].x, v1 = xr[t].y;
-            unsigned char* blk = buf + swz(r, kp >> 2) * 16;
-            if constexpr (NL == 3) {
-                uint32_t h, m, l;
-                split2(v0, v1, h, m, l);
-                *reinterpret_cast<uint32_t*>(blk) = h;
-                *reinterpret_cast<uint32_t*>(blk + 1024) = m;
-                *reinterpret_cast<uint32_t*>(blk + 2048) = l;
-            } else {
-                const uint32_t h = bf16x2_rne(v0, v1);
-                *reinterpret_cast<uint32_t*>(blk) = h;
-                v0 = bitsf(h << 16);                       // the sum is over the rounded values
-                v1 = bitsf(h & 0xffff0000u);
-            }
-            // sum over the 16 lanes of the (row, group) (one DPP row); lane kp = 0 holds it
-            float sum = v0 + v1;
-            sum += row_ror<8>(sum);
-            sum += row_ror<4>(sum);
-            sum += row_ror<2>(sum);
-            sum += row_ror<1>(sum);
-            if (kp == 0) sums[r] = sum;
-        }
-    };
-    auto lds_barrier = [&]() {
-        __builtin_amdgcn_s_waitcnt(0xc07f);            // this wave's LDS writes done (lgkmcnt(0))
-        __builtin_amdgcn_s_barrier();
-    };
-
-    // ---- weights: lane (li, lc) of tile tn holds column n0 + wave*TN*16 + tn*16 + li.
-    //      They are read in blocks of 4 groups (128 k), 16 bytes per lane and load:
-    //      int4: lane lc loads group 4b + lc of its row whole and the 4 lanes of a
-    //      row swap words through a private LDS area (word w of group j goes to
-    //      lane w, which feeds it to the MFMA of group j); lane lc also loads the
-    //      (scale, min) word of group 4b + lc, and the area hands all 4 words to
-    //      every lane of the row. The area of a tile is rewritten for the next
-    //      block only after this block's reads of it: one wave's LDS operations
-    //      run in order, so no barrier is needed. int8/FP8: lane lc loads bytes
-    //      16lc.. and 64 + 16lc.. of the block; the MFMAs contract k in that order
-    //      (x is read from the matching places), so no exchange is needed. ----
-    const unsigned char* payload = static_cast<const unsigned char*>(payload_v);
-    const unsigned char* wrow[TN];
-    const uint32_t* prow[TN];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        const int64_t col = min(n0 + wave * TN * 16 + tn * 16 + li, N - 1);
-        if constexpr (FMT == kFmtQ4) {
-            wrow[tn] = payload + col * (K / 2) + 16 * lc;
-            prow[tn] = static_cast<const uint32_t*>(scale_v) + col * G + lc;
-        } else {
-            wrow[tn] = payload + col * K + 16 * lc;
-            prow[tn] = nullptr;
-        }
-    }
-    constexpr int NB = G / 4;                                    // blocks of 4 groups
-    constexpr int CW = FMT == kFmtQ4 ? 4 : 8;                    // code words per lane and block
-    constexpr int PW = 1;                                        // pair words per lane and block
-    constexpr int DB = tiny_db(TN) < NB ? tiny_db(TN) : NB;     // blocks in flight
-    uint32_t bc[DB][TN][CW], bp[DB][TN][PW];
-    auto b_issue = [&](int b, uint32_t (&c)[TN][CW], uint32_t (&pr)[TN][PW]) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            if constexpr (FMT == kFmtQ4) {
-                const uint4 v = *reinterpret_cast<const uint4*>(wrow[tn] + b * 64);
-                c[tn][0] = v.x; c[tn][1] = v.y; c[tn][2] = v.z; c[tn][3] = v.w;
-                pr[tn][0] = prow[tn][4 * b];
-            } else {
-                const uint4 v0 = *reinterpret_cast<const uint4*>(wrow[tn] + b * 128);
-                const uint4 v1 = *reinterpret_cast<const uint4*>(wrow[tn] + b * 128 + 64);
-                c[tn][0] = v0.x; c[tn][1] = v0.y; c[tn][2] = v0.z; c[tn][3] = v0.w;
-                c[tn][4] = v1.x; c[tn][5] = v1.y; c[tn][6] = v1.z; c[tn][7] = v1.w;
-                pr[tn][0] = 0;
-            }
-        }
-    };
-    // operand words of the block's 4 MFMAs: wq[tn][j] for the MFMA j
-    unsigned char* stg = smem + L::XTOTAL + wave * L::STG + li * L::STG_ROW;
-    auto b_stage = [&](const uint32_t (&c)[TN][CW], const uint32_t (&pr)[TN][PW], uint32_t (&wq)[TN][4][2],
-                       uint32_t (&pq)[TN][4]) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            if constexpr (FMT == kFmtQ4) {
-                unsigned char* t = stg + tn * L::STG_TILE;
-#pragma unroll
-                for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(t + w * 16 + lc * 4) = c[tn][w];
-                *reinterpret_cast<uint32_t*>(t + 64 + lc * 4) = pr[tn][0];
-                const u32x4 r = *reinterpret_cast<const u32x4*>(t + lc * 16);
-                const u32x4 q = *reinterpret_cast<const u32x4*>(t + 64);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    wq[tn][j][0] = r[j];
-                    wq[tn][j][1] = 0;
-                    pq[tn][j] = q[j];
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    wq[tn][j][0] = c[tn][2 * j];
-                    wq[tn][j][1] = c[tn][2 * j + 1];
-                    pq[tn][j] = 0;
-                }
-            }
-        }
-    };
-
-    // int8/FP8 accumulate every group into the tile's accumulator; narrow waves
-    // spread the groups over NA accumulators so consecutive MFMAs do not wait
-    // on each other, and add them up at the end
-    constexpr int NA = FMT == kFmtQ4 ? 1 : 4 / TN;
-    floatx4 acc[TN][NA];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int a = 0; a < NA; ++a) acc[tn][a] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mreg[TN];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) mreg[tn] = 0.0f;
-    const int aoff = swz(li, lc) * 16;
-    // int8/FP8: the k of lane lc in the MFMA j of a block lie in group 2(j >> 1) + (lc >> 1)
-    // of the block, at lane place 2(lc & 1) + (j & 1)
-    int aoff8[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) aoff8[h] = (lc >> 1) * (NL * 1024) + swz(li, 2 * (lc & 1) + h) * 16;
-
-    // x limbs of group g (high, mid, low), read one group ahead of their use
-    auto x_read = [&](int g, u32x4 (&xv)[NL]) {
-        const int ph = g / kTinyPG;
-        const int jb = g & 3;
-        const unsigned char* blk;
-        if constexpr (FMT == kFmtQ4)
-            blk = smem + (ph & 1) * L::XBUF + (g % kTinyPG) * (NL * 1024) + aoff;
-        else
-            blk = smem + (ph & 1) * L::XBUF + ((g & ~3) % kTinyPG + 2 * (jb >> 1)) * (NL * 1024) + aoff8[jb & 1];
-#pragma unroll
-        for (int l = 0; l < NL; ++l) xv[l] = *reinterpret_cast<const u32x4*>(blk + l * 1024);
-    };
-    auto compute = [&](int g, const u32x4 (&xv)[NL], const uint32_t (&wq)[TN][4][2], const uint32_t (&bpr)[TN][4]) {
-        const int ph = g / kTinyPG;
-        const int jb = g & 3;
-        const u32x4 xh = xv[0];
-        u32x4 xm = {}, xl = {};
-        if constexpr (NL == 3) {
-            xm = xv[1];
-            xl = xv[2];
-        }
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn) {
-            u32x4 b;
-            if constexpr (FMT == kFmtQ4) b = codes4_to_bf16(wq[tn][jb][0]);
-            else if constexpr (FMT == kFmtF8) b = codes8f_to_bf16(wq[tn][jb][0], wq[tn][jb][1]);
-            else b = codes8_to_bf16(wq[tn][jb][0], wq[tn][jb][1]);
-            if constexpr (FMT == kFmtQ4) {
-                floatx4 p = floatx4{0.f, 0.f, 0.f, 0.f};
-                if constexpr (NL == 3) {
-                    p = mfma_bf16(xl, b, p);
-                    p = mfma_bf16(xm, b, p);
-                }
-                p = mfma_bf16(xh, b, p);
-                const float sc = half_bits_to_float(bpr[tn][jb] & 0xffffu);
-                const float mn = half_bits_to_float(bpr[tn][jb] >> 16);
-                mreg[tn] = lc == (g & 3) ? mn : mreg[tn];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) acc[tn][0][e] = fmaf(sc, p[e], acc[tn][0][e]);
-            } else {
-                floatx4& a = acc[tn][g % NA];
-                if constexpr (NL == 3) {
-                    a = mfma_bf16(xl, b, a);
-                    a = mfma_bf16(xm, b, a);
-                }
-                a = mfma_bf16(xh, b, a);
-            }
-        }
-        // int4 min term of the 4-group block that g closes: sum_g X_g[row] * min_g[col]
-        if constexpr (FMT == kFmtQ4) {
-            if ((g & 3) == 3) {
-                const float* sums = reinterpret_cast<const float*>(smem + 2 * L::XBUF + (ph & 1) * L::XSUM);
-                const float xs = sums[((g & ~3) % kTinyPG + lc) * 16 + li];
-#pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    acc[tn][0] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs, mreg[tn], acc[tn][0], 0, 0, 0);
-                    mreg[tn] = 0.0f;
-                }
-            }
-        }
-    };
-
-    // ---- prologue: zero both x areas (rows >= M stay zero), load phase 0 of x,
-    //      start the weights, stage x ----
-    {
-        uint4* z = reinterpret_cast<uint4*>(smem);
-        for (int t = tid; t < L::XTOTAL / 16; t += 256) z[t] = make_uint4(0u, 0u, 0u, 0u);
-    }
-    lds_barrier();
-    x_load(0);
-#pragma unroll
-    for (int b = 0; b < DB; ++b) b_issue(b, bc[b], bp[b]);
-    x_convert(0);
-    lds_barrier();
-    u32x4 xcur[NL];
-    x_read(0, xcur);
-
-    // ---- main loop, fully unrolled over blocks of 4 groups; block b sits in
-    //      ring slot b % DB, which is refilled with block b + DB once its codes
-    //      are in operand order. The x of phase p + 1 is loaded when phase p
-    //      starts and staged when it ends. ----
-    static_assert(kTinyPG % 4 == 0, "a phase holds whole blocks");
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-        const int ph = (4 * b) / kTinyPG;
-        if ((4 * b) % kTinyPG == 0 && ph + 1 < NPH) x_load(ph + 1);
-        uint32_t wq[TN][4][2], pq[TN][4];
-        b_stage(bc[b % DB], bp[b % DB], wq, pq);
-        if (b + DB < NB) b_issue(b + DB, bc[b % DB], bp[b % DB]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int g = 4 * b + j;
-            u32x4 xnext[NL];
-            if ((g + 1) % kTinyPG != 0) x_read(g + 1, xnext);      // same phase: read ahead
-            __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of this group's MFMAs
-            compute(g, xcur, wq, pq);
-#pragma unroll
-            for (int l = 0; l < NL; ++l) xcur[l] = xnext[l];
-        }
-        if ((4 * b + 4) % kTinyPG == 0) {
-            if (ph + 1 < NPH) x_convert(ph + 1);
-            lds_barrier();
-            if (ph + 1 < NPH) x_read(4 * b + 4, xcur);           // first group of the next phase
-        }
-    }
-
-    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile ----
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-        for (int a = 1; a < NA; ++a)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[tn][0][e] += acc[tn][a][e];
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        const int col = n0 + wave * TN * 16 + tn * 16 + li;
-        if (col >= N) continue;
-        float sc = 1.0f;
-        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(scale_v)[col];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = 4 * lc + e;
-            if (row < M) {
-                float v = acc[tn][0][e];
-                if constexpr (FMT == kFmtQ8) v *= sc;
-                y[static_cast<int64_t>(row) * N + col] = v;
-            }
-        }
-    }
-}
-
-struct TinyArgs {
-    int count;
-    int M;
-    int tile_begin[seg_begin_slots(kMaxSplitGrouped)];   // first workgroup of each projection
-    int tile_coarse[seg_coarse_slots(kMaxSplitGrouped)];
-    const float* xs[kTinyMaxInputs];
-    const void* payload[kMaxSplitGrouped];
-    const void* scale[kMaxSplitGrouped];
-    float* y[kMaxSplitGrouped];
-    int n[kMaxSplitGrouped];
-    uint16_t k[kMaxSplitGrouped];
-    uint8_t x_idx[kMaxSplitGrouped];
-    uint8_t fmt[kMaxSplitGrouped];
-};
-static_assert(sizeof(TinyArgs) <= 4096, "kernel arguments must stay within 4 KiB");
-
-template <int FMT, int NL>
-__device__ __forceinline__ void tiny_dispatch_k(int K, const float* x, const void* p, const void* s, float* y, int M,
-                                                int N, int n0, unsigned char* smem) {
-    if (K == 512) tiny_tile<FMT, tiny_tn(512), NL, 2>(x, p, s, y, M, N, n0, smem);
-    else if (K == 2048) tiny_tile<FMT, tiny_tn(2048), NL, 8>(x, p, s, y, M, N, n0, smem);
-    else if (K == 1024) tiny_tile<FMT, tiny_tn(1024), NL, 4>(x, p, s, y, M, N, n0, smem);
-    else tiny_tile<FMT, tiny_tn(256), NL, 1>(x, p, s, y, M, N, n0, smem);
-}
-
-template <int NL>
-__global__ __launch_bounds__(256) void tiny_kernel(TinyArgs g) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[TinyLds<NL>::TOTAL];
-    const int w = xcd_remap_split(blockIdx.x, gridDim.x);
-    const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
-    const int K = g.k[i];
-    const int tn = tiny_tn(K);
-    const int n0 = (w - g.tile_begin[i]) * tn * 64;
-    const float* x = g.xs[g.x_idx[i]];
-    if (g.fmt[i] == kFmtQ4)
-        tiny_dispatch_k<kFmtQ4, NL>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
-    else if (g.fmt[i] == kFmtQ8)
-        tiny_dispatch_k<kFmtQ8, NL>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
-    else
-        tiny_dispatch_k<kFmtF8, NL>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
 }
 
 // Finishes projections after their GEMM launch: sums the K-chunk partials in
@@ -1222,63 +756,13 @@ void launch_large(int fmt, int blocks, const SplitArgs& a, int tn, hipStream_t s
         split_gemm_kernel<kFmtF8, NL><<<blocks, 256, 0, stream>>>(a, tn);
 }
 
-// Tiny M: every projection in as few launches as the argument budget allows
-// (96 projections, 48 distinct inputs), then the biases in one finish pass.
-static hipError_t launch_tiny(const ProjTask* tasks, int count, int M, int NL, hipStream_t stream) {
-    int done = 0;
-    while (done < count) {
-        TinyArgs g{};
-        g.M = M;
-        int tiles = 0, n_in = 0;
-        while (done < count && g.count < kMaxSplitGrouped) {
-            const ProjTask& t = tasks[done];
-            const int cols = 64 * tiny_tn(t.K);
-            const int t_tiles = (t.N + cols - 1) / cols;
-            if (tiles + t_tiles > kMaxGroupedTiles) break;
-            int xi = -1;
-            for (int k = 0; k < n_in; ++k)
-                if (g.xs[k] == t.x) xi = k;
-            if (xi < 0) {
-                if (n_in == kTinyMaxInputs) break;
-                xi = n_in++;
-                g.xs[xi] = t.x;
-            }
-            const int c = g.count++;
-            g.payload[c] = t.payload;
-            g.scale[c] = t.scale;
-            g.y[c] = t.y;
-            g.n[c] = t.N;
-            g.k[c] = static_cast<uint16_t>(t.K);
-            g.x_idx[c] = static_cast<uint8_t>(xi);
-            g.fmt[c] = static_cast<uint8_t>(t.fmt);
-            g.tile_begin[c] = tiles;
-            tiles += t_tiles;
-            ++done;
-        }
-        seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
-        const int mark = timing_begin(stream);
-        if (NL == 1)
-            tiny_kernel<1><<<tiles, 256, 0, stream>>>(g);
-        else
-            tiny_kernel<3><<<tiles, 256, 0, stream>>>(g);
-        timing_end(mark, stream);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    return launch_bias_add(tasks, count, M, stream);
-}
-
 // All projections (sharing M) of this call: split every distinct input once into
 // a stream-ordered workspace, run the GEMMs, release the workspace. NL = 3:
 // exact three-limb split; NL = 1: x rounded to bf16.
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream) {
     if (NL != 1 && NL != 3) return hipErrorInvalidValue;
     const int M = static_cast<int>(M64);
-    if (M <= kTinyMaxM) {
-        bool fits = true;                 // whole K per workgroup, in phases of 8 groups
-        for (int i = 0; i < count; ++i) fits = fits && tiny_k(tasks[i].K);
-        if (fits) return launch_tiny(tasks, count, M, NL, stream);
-    }
+    if (direct_fits(tasks, count, M)) return launch_direct(tasks, count, M, NL, stream);
     const int tm_small = static_cast<int>((int64_t(M) + 15) / 16);
     // The grouped small-M launch addresses the limb images by 32-bit offsets;
     // a call whose images would not fit (enormous K) takes the tiled path.

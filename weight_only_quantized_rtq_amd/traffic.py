@@ -13,7 +13,8 @@ import os
 import re
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h")
+KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h",
+                  "split_device.h")
 
 # (workload, math) -> record; filled from the counter runs described in the
 # profiles folder.
