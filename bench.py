@@ -36,9 +36,9 @@ PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix
 PEAK_BF16_MFMA_TFLOPS = 2516.6     # MI355X dense bf16 matrix
 WEIGHT_SETS = 16
 KERNELS = {  # main GEMM kernel of each (math, workload), as rocprofv3 names it
-    ("split", "m80"): "direct_kernel<5, 3>",
+    ("split", "m80"): "split_grouped_kernel<5, 3>",
     ("split", "m65536"): "split_gemm_kernel<1|2, 3>",
-    ("bf16", "m80"): "direct_kernel<5, 1>",
+    ("bf16", "m80"): "split_grouped_kernel<5, 1>",
     ("bf16", "m65536"): "split_gemm_kernel<1|2, 1>",
     ("fp32", "m80"): "grouped_stream_kernel<5>",
     ("fp32", "m65536"): "gemm_kernel<1|2,2,2,4,4>",
