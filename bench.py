@@ -64,9 +64,9 @@ def parse():
                     help="skip the separately reported bf16-activation timing")
     ap.add_argument("--compare-fp32", action="store_true",
                     help="also time the fp32-MFMA path (few steps) and report it alongside")
-    ap.add_argument("--m-sweep", default="1,2,4,8,16,32,48,80",
-                    help="M values of the diagnostic sweep on the m80 weight sets, run with --workload both "
-                         "('' to skip)")
+    ap.add_argument("--m-sweep", default=None,
+                    help="M values of the diagnostic sweep on the m80 weight sets (default with --workload both: "
+                         "1,2,4,8,16,32,48,80; '' to skip; given explicitly it runs with any workload)")
     ap.add_argument("--bias", action="store_true",
                     help="give every projection an fp32 bias (y = x.W^T + b) to time the bias epilogue")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -371,7 +371,9 @@ def main():
             "note": "x rounded to the nearest bf16 (lower precision: 3e-3 bar, not 1e-5), one bf16 MFMA per "
                     "product; reported apart from the fp32-activation figures above",
             **bf16}
-    if args.m_sweep and args.workload == "both":
+    if args.m_sweep is None:
+        args.m_sweep = "1,2,4,8,16,32,48,80" if args.workload == "both" else ""
+    if args.m_sweep:
         line["m_sweep"] = {
             "note": f"diagnostic: the m80 weight sets at other M ({args.math} arithmetic); per-step and "
                     "in-kernel weight GB/s against the 8000 GB/s HBM peak",
