@@ -148,3 +148,47 @@ def test_direct_full_size_weight_sets_sampled(M):
                 ref_w = oracle.quantize(W[cols], fmt)
                 y = host(blocks[b][name].y[:, torch.as_tensor(cols, device=DEV)])
                 assert oracle.rel_fro(y, oracle.project(fmt, x, *ref_w)) <= 1e-5, (s, b, name)
+
+
+def test_direct_call_with_a_k_it_does_not_take_runs_grouped():
+    """A call is routed as a whole: with one K outside {256, 512, 1024, 2048}
+    (here 96) every projection takes the pre-pass + grouped path, at M <= 32."""
+    M = 8
+    shapes = {"wq": (100, 512), "wk": (64, 96), "w2": (70, 2048)}
+    blk, ref = {}, {}
+    for j, (name, (N, K)) in enumerate(shapes.items()):
+        fmt = ("q4", "q8", "f8")[j]
+        W = synth.weight(66, 0, j, "w1", N, K, heavy="rows")
+        x = synth.activation(66, j, "x_ffn", M, K)
+        blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), dev(x),
+                                   torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV))
+        ref[name] = (fmt, oracle.quantize(W, fmt), x)
+    rtq.block_project([blk], M)
+    for name, (fmt, r, x) in ref.items():
+        assert oracle.rel_fro(host(blk[name].y), oracle.project(fmt, x, *r)) <= 1e-5, name
+
+
+@pytest.mark.parametrize("M", [3, 20])
+def test_direct_call_split_over_launches(M):
+    """13 blocks of small projections: 104 projections reading 52 distinct
+    inputs, more than one launch's argument block holds (96 and 48), so the
+    call runs as several direct launches; every output checked."""
+    nb = 13
+    blocks, refs = [], []
+    for b in range(nb):
+        xs = {i: synth.activation(67, 4 * b + i, "x_ffn", M, 256 if i % 2 else 512) for i in range(4)}
+        dxs = {i: dev(v) for i, v in xs.items()}
+        blk, ref = {}, {}
+        for j, name in enumerate(("wq", "wk", "wv", "wg", "wo", "w1", "w3", "w2")):
+            N, K = 64 + 16 * (j % 3), (256 if j % 2 else 512)
+            fmt = ("q4", "q8", "f8")[(b + j) % 3]
+            W = synth.weight(67, b, j, "w1", N, K, heavy="rows")
+            blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), dxs[j % 4],
+                                       torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV))
+            ref[name] = (fmt, oracle.quantize(W, fmt), xs[j % 4])
+        blocks.append(blk)
+        refs.append(ref)
+    rtq.block_project(blocks, M)
+    for b in range(nb):
+        for name, (fmt, r, x) in refs[b].items():
+            assert oracle.rel_fro(host(blocks[b][name].y), oracle.project(fmt, x, *r)) <= 1e-5, (b, name)
