@@ -32,9 +32,11 @@
  *   - Every data pointer is a DEVICE pointer owned by the caller; the library
  *     never retains a caller's pointer past the call's work on its stream.
  *   - Memory and state of the library itself: a GEMM call on the split path
- *     takes one stream-ordered workspace (limb images of x, K-chunk partials)
- *     with hipMallocAsync on the caller's stream from the device's default
- *     memory pool and returns it with hipFreeAsync on the same stream; the
+ *     with M above 32 (or a K other than 256, 512, 1024, 2048) takes one
+ *     stream-ordered workspace (limb images of x, K-chunk partials) with
+ *     hipMallocAsync on the caller's stream from the device's default memory
+ *     pool and returns it with hipFreeAsync on the same stream (smaller calls
+ *     split x inside the GEMM kernel and allocate nothing); the
  *     pool's release threshold is raised once per device, so steady-state
  *     calls reuse pool memory. Process-wide state: the arithmetic mode
  *     (rtq_set_math) and the timing events (rtq_timing_enable); per thread:
