@@ -192,3 +192,24 @@ def test_direct_call_split_over_launches(M):
     for b in range(nb):
         for name, (fmt, r, x) in refs[b].items():
             assert oracle.rel_fro(host(blocks[b][name].y), oracle.project(fmt, x, *r)) <= 1e-5, (b, name)
+
+
+@pytest.mark.parametrize("fmt,K", [("q4", 512), ("q8", 2048), ("f8", 1024), ("q4", 256)])
+@pytest.mark.parametrize("M", [1, 30])
+def test_direct_guard_bands_and_determinism(fmt, K, M, mode):
+    """Outputs land only inside y (canaries around it survive, also past the
+    ragged last column block) and a rerun is bitwise identical: the direct
+    kernel has no atomics and a fixed summation order."""
+    N = 130
+    W = synth.weight(68, 0, 0, "w1", N, K, heavy="rows")
+    x = dev(synth.activation(68, 0, "x_ffn", M, K))
+    w = rtq.quantize(dev(W), fmt)
+    guard = 4096
+    buf = torch.full((guard + M * N + guard,), 1234.5, dtype=torch.float32, device=DEV)
+    y = buf[guard:guard + M * N].view(M, N)
+    rtq.gemm(x, w, y=y)
+    y1 = host(y).copy()
+    b = host(buf)
+    assert np.all(b[:guard] == 1234.5) and np.all(b[guard + M * N:] == 1234.5)
+    rtq.gemm(x, w, y=y)
+    assert np.array_equal(host(y).view(np.uint32), y1.view(np.uint32))
