@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--bias", action="store_true",
                     help="give every projection an fp32 bias (y = x.W^T + b) to time the bias epilogue")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-attainable", action="store_true",
+                    help="skip the measured streaming-read ceiling (hbm_attainable)")
     return ap.parse_args()
 
 
@@ -212,6 +214,26 @@ def m_sweep(torch, rtq, synth, Ms, steps=200, warmup=20, recipe="mixed"):
     del weights
     torch.cuda.empty_cache()
     return out
+
+
+def attainable_hbm_gbs(torch, gib=4, reps=10):
+    """Read bandwidth a plain device-wide streaming reduction (torch.sum over a
+    `gib` GiB fp32 buffer) attains on this GPU: the measured ceiling the weight
+    stream is compared with, beside the 8 TB/s published peak."""
+    buf = torch.ones(gib * (1 << 28), dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        buf.sum()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        buf.sum()
+    t1.record()
+    t1.synchronize()
+    gbs = buf.numel() * 4 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return gbs
 
 
 def load_traffic(workload, math, recipe="mixed"):
@@ -371,6 +393,11 @@ def main():
             "note": "x rounded to the nearest bf16 (lower precision: 3e-3 bar, not 1e-5), one bf16 MFMA per "
                     "product; reported apart from the fp32-activation figures above",
             **bf16}
+    if not args.no_attainable:
+        hbm = attainable_hbm_gbs(torch)
+        line["hbm_attainable"] = {"gbs": round(hbm, 1), "frac_of_peak": round(hbm / PEAK_HBM_GBS, 4),
+                                  "how": "torch.sum over a 4 GiB fp32 buffer, 10 passes (HIP events)",
+                                  "weight_frac_of_attainable": round(prim["weight_gbs"] / hbm, 5)}
     if args.m_sweep is None:
         args.m_sweep = "1,2,4,8,16,32,48,80" if args.workload == "both" else ""
     if args.m_sweep:
@@ -378,6 +405,10 @@ def main():
             "note": f"diagnostic: the m80 weight sets at other M ({args.math} arithmetic); per-step and "
                     "in-kernel weight GB/s against the 8000 GB/s HBM peak",
             "points": m_sweep(torch, rtq, synth, [int(v) for v in args.m_sweep.split(",")], recipe=args.recipe)}
+        if "hbm_attainable" in line:
+            for pt in line["m_sweep"]["points"]:
+                pt["weight_frac_of_attainable_in_kernel"] = round(
+                    pt["weight_gbs_in_kernel"] / line["hbm_attainable"]["gbs"], 4)
     if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
     print(json.dumps(line), flush=True)
