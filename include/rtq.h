@@ -160,6 +160,20 @@ rtq_status rtq_quantize_q8(const float* w, int8_t* q, float* scale,
  * infinities and NaN become NaN (0x7F with the input's sign). */
 rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K, void* stream);
 
+/* Host quantizers, for writing quantized checkpoints on a machine without a
+ * GPU (the RT-J cards' offline quantizing tool, "rt_quantize --type q4 / q8"):
+ * the same formats and the same arithmetic as rtq_quantize_q4 / _q8 / _f8
+ * above, which they match bit for bit. Every pointer is a HOST pointer owned
+ * by the caller; the call runs synchronously on the calling thread plus up to
+ * threads - 1 worker threads (threads <= 0: one per hardware thread, at most
+ * 1024), makes no HIP call and needs no GPU. Layouts, validation and
+ * alignment as for the GPU quantizers; the arrays must not overlap. */
+rtq_status rtq_quantize_q4_host(const float* w, uint8_t* payload, uint16_t* pairs,
+                                int64_t N, int64_t K, int32_t threads);
+rtq_status rtq_quantize_q8_host(const float* w, int8_t* q, float* scale,
+                                int64_t N, int64_t K, int32_t threads);
+rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int32_t threads);
+
 /* Arithmetic of the GEMM entry points, process-wide (default RTQ_MATH_SPLIT_BF16).
  *
  * RTQ_MATH_SPLIT_BF16: each fp32 activation is split exactly into three bf16

@@ -152,3 +152,34 @@ def test_quantize_file_matches_oracle(tmp_path, qtype):
     for name, (fmt, ref, xin, bias) in refs.items():
         err = oracle.rel_fro(dys[name].cpu().numpy(), oracle.project_bias(fmt, xs[xin], *ref, bias))
         assert err <= 1e-5, (name, err)
+
+
+@pytest.mark.parametrize("qtype", ["q4", "q8", "fp8"])
+def test_host_quantize_cli_writes_the_oracle_bytes(tmp_path, qtype):
+    """`checkpoint quantize SRC DST --type T --device cpu` (host quantizers, no
+    GPU) writes exactly the oracle's bytes, keeps the other tensors, and the
+    file loads back with the right formats."""
+    src = {}
+    shapes = {"wq": (64, 128), "wo": (48, 96), "w1": (32, 64), "w2": (40, 256)}
+    for j, (name, (N, K)) in enumerate(shapes.items()):
+        key = f"blocks.1.{'ffn.' if name in ('w1', 'w2', 'w3') else 'attn.'}{name}.weight"
+        src[key] = torch.from_numpy(synth.weight(24, 0, j, name, N, K, heavy="cols"))
+    src["decoder.weight"] = torch.ones(4, 8)
+    spath, dpath = os.path.join(tmp_path, "src.safetensors"), os.path.join(tmp_path, "dst.safetensors")
+    save_file(src, spath)
+    assert ck.main(["quantize", spath, dpath, "--type", qtype, "--device", "cpu"]) == 0
+    raw = load_file(dpath)
+    assert torch.equal(raw["decoder.weight"], src["decoder.weight"])
+    w = ck.load(dpath, device="cpu")
+    recipe = ck.TYPES[qtype]
+    for key, W in src.items():
+        name = ck.projection_of(key)
+        if name is None:
+            continue
+        fmt = recipe[name]
+        ref = oracle.quantize(W.numpy(), fmt)
+        got = w[key]
+        assert type(got).__name__ == {"q4": "Q4Weight", "q8": "Q8Weight", "f8": "F8Weight"}[fmt], key
+        assert np.array_equal(got.payload.numpy(), ref[0]), key
+        if fmt != "f8":
+            assert np.array_equal(got.scale_tensor.numpy().view(np.uint8), ref[1].view(np.uint8)), key

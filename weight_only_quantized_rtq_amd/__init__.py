@@ -41,7 +41,7 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 # Every symbol include/rtq.h declares.
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
            "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
-           "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
+           "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 MATH_SPLIT_BF16, MATH_FP32_MFMA, MATH_BF16 = 0, 1, 2
@@ -91,6 +91,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f = getattr(lib, name)
         f.argtypes = [vp, vp, vp, i64, i64, vp]
         f.restype = ctypes.c_int
+    for name in ("rtq_quantize_q4_host", "rtq_quantize_q8_host"):
+        f = getattr(lib, name)
+        f.argtypes = [vp, vp, vp, i64, i64, i32]
+        f.restype = ctypes.c_int
+    lib.rtq_quantize_f8_host.argtypes = [vp, vp, i64, i64, i32]
+    lib.rtq_quantize_f8_host.restype = ctypes.c_int
     lib.rtq_set_math.argtypes = [i32]
     lib.rtq_set_math.restype = ctypes.c_int
     lib.rtq_get_math.argtypes = []
@@ -349,6 +355,32 @@ def quantize_f8(W: torch.Tensor, stream=None) -> F8Weight:
     codes = torch.empty((N, K), dtype=torch.uint8, device=W.device)
     _check(lib.rtq_quantize_f8(_ptr(W), _ptr(codes), N, K, _stream(stream)))
     return F8Weight(codes)
+
+
+def quantize_host(W: torch.Tensor, fmt: str, threads: int = 0):
+    """The quantizers on the host (rtq_quantize_q4_host / _q8_host / _f8_host):
+    W is a CPU float32 [N, K] tensor; the result holds CPU tensors, bit-identical
+    to what quantize() gives on the GPU. Needs no GPU."""
+    lib = load_library()
+    if W.device.type != "cpu" or W.dtype != torch.float32 or W.dim() != 2:
+        raise ValueError(f"W must be a CPU float32 [N, K] tensor, got {W.dtype} {tuple(W.shape)} on {W.device}")
+    W = W.contiguous()
+    N, K = W.shape
+    if fmt == "q4":
+        payload = torch.empty((N, K // 2), dtype=torch.uint8)
+        pairs = torch.empty((N, K // Q4_GROUP, 2), dtype=torch.float16)
+        _check(lib.rtq_quantize_q4_host(_ptr(W), _ptr(payload), _ptr(pairs), N, K, threads))
+        return Q4Weight(payload, pairs)
+    if fmt == "q8":
+        q = torch.empty((N, K), dtype=torch.int8)
+        scale = torch.empty((N,), dtype=torch.float32)
+        _check(lib.rtq_quantize_q8_host(_ptr(W), _ptr(q), _ptr(scale), N, K, threads))
+        return Q8Weight(q, scale)
+    if fmt == "f8":
+        codes = torch.empty((N, K), dtype=torch.uint8)
+        _check(lib.rtq_quantize_f8_host(_ptr(W), _ptr(codes), N, K, threads))
+        return F8Weight(codes)
+    raise ValueError(f"unknown format {fmt!r}")
 
 
 def quantize(W: torch.Tensor, fmt: str, stream=None):

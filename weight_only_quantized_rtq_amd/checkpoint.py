@@ -14,12 +14,14 @@ Every other tensor (encoders, head, norms, biases, mask embeddings) stays as
 it is in the source checkpoint. The format of each tensor is read off its
 dtype, as the engine's loader does (int4 card, "Usage").
 
-    python -m weight_only_quantized_rtq_amd.checkpoint quantize SRC DST --type q4|q8|fp8
+    python -m weight_only_quantized_rtq_amd.checkpoint quantize SRC DST --type q4|q8|fp8 [--device cpu]
     python -m weight_only_quantized_rtq_amd.checkpoint info FILE
 
 `quantize` is the counterpart of the cards' rt_quantize step: it runs the
 library's GPU quantizers (rtq_quantize_q4 / _q8 / _f8) on the block
-projections. Loading never executes anything from the file (safetensors).
+projections, or with --device cpu its host quantizers (rtq_quantize_*_host,
+the same bytes, no GPU needed). Loading never executes anything from the file
+(safetensors).
 """
 from __future__ import annotations
 
@@ -28,7 +30,7 @@ import sys
 
 import torch
 
-from . import F8Weight, PROJ_NAMES, Projection, Q4Weight, Q8Weight, quantize
+from . import F8Weight, PROJ_NAMES, Projection, Q4Weight, Q8Weight, quantize, quantize_host
 
 Q4_SCALE = ".q4_scale"
 Q8_SCALE = ".q_scale"
@@ -162,8 +164,9 @@ def storage(name: str, w) -> dict[str, torch.Tensor]:
 
 
 def quantize_tensors(tensors: dict[str, torch.Tensor], qtype: str, device: str = "cuda:0"):
-    """Quantizes the 2-D block projections of a float checkpoint (GPU
-    quantizers); returns the entries of the quantized file."""
+    """Quantizes the 2-D block projections of a float checkpoint with the GPU
+    quantizers on `device`, or with the host quantizers (same bytes, no GPU)
+    when device is "cpu"; returns the entries of the quantized file."""
     if qtype not in TYPES:
         raise ValueError(f"--type must be one of {sorted(TYPES)}, got {qtype!r}")
     recipe = TYPES[qtype]
@@ -177,8 +180,9 @@ def quantize_tensors(tensors: dict[str, torch.Tensor], qtype: str, device: str =
         W = t.to(device=device, dtype=torch.float32).contiguous()
         if fmt == "q4" and W.shape[1] % 32:
             raise ValueError(f"{name}: K={W.shape[1]} is not a multiple of the int4 group size 32")
-        out.update(storage(name, quantize(W, fmt)))
-    torch.cuda.synchronize()
+        out.update(storage(name, quantize_host(W, fmt) if W.device.type == "cpu" else quantize(W, fmt)))
+    if torch.device(device).type != "cpu":
+        torch.cuda.synchronize()
     return out
 
 
@@ -202,7 +206,8 @@ def info(path: str) -> str:
 def main(argv: list[str]) -> int:
     if len(argv) >= 3 and argv[0] == "quantize":
         qtype = argv[argv.index("--type") + 1] if "--type" in argv else "q4"
-        quantize_file(argv[1], argv[2], qtype)
+        device = argv[argv.index("--device") + 1] if "--device" in argv else "cuda:0"
+        quantize_file(argv[1], argv[2], qtype, device)
         return 0
     if len(argv) == 2 and argv[0] == "info":
         print(info(argv[1]))

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <thread>
 #include <vector>
 
 #include "rtq_internal.h"
@@ -358,6 +359,53 @@ rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K,
         return fail(RTQ_ERR_OVERLAP, "rtq_quantize_f8: output overlaps the weights");
     return hip_status(rtq::launch_quantize_f8(w, codes, N, K, static_cast<hipStream_t>(stream)),
                       "rtq_quantize_f8 launch");
+}
+
+// ---- host quantizers: host pointers, no HIP call ----
+static int host_threads(int32_t threads) {
+    if (threads > 0) return threads < 1024 ? threads : 1024;
+    const unsigned hw = std::thread::hardware_concurrency();
+    return hw ? static_cast<int>(hw < 1024 ? hw : 1024) : 1;
+}
+
+rtq_status rtq_quantize_q4_host(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N, int64_t K,
+                                int32_t threads) {
+    clear_error();
+    rtq_status s = check_nk("rtq_quantize_q4_host", rtq::kFmtQ4, payload, pairs, w, N, K);
+    if (s != RTQ_OK || N == 0) return s;
+    if (overlaps(range_of(w, N * K * 4), range_of(payload, N * (K / 2))) ||
+        overlaps(range_of(w, N * K * 4), range_of(pairs, N * (K / RTQ_Q4_GROUP) * 4)) ||
+        overlaps(range_of(payload, N * (K / 2)), range_of(pairs, N * (K / RTQ_Q4_GROUP) * 4)))
+        return fail(RTQ_ERR_OVERLAP, "rtq_quantize_q4_host: arrays overlap");
+    rtq::quantize_q4_host(w, payload, pairs, N, K, host_threads(threads));
+    return RTQ_OK;
+}
+
+rtq_status rtq_quantize_q8_host(const float* w, int8_t* q, float* scale, int64_t N, int64_t K, int32_t threads) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
+        return fail(RTQ_ERR_SHAPE, "rtq_quantize_q8_host: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!w || !q || !scale) return fail(RTQ_ERR_NULL, "rtq_quantize_q8_host: a pointer argument is NULL");
+    if (!aligned(w, 4) || !aligned(scale, 4)) return fail(RTQ_ERR_ALIGN, "rtq_quantize_q8_host: misaligned pointer");
+    if (overlaps(range_of(w, N * K * 4), range_of(q, N * K)) || overlaps(range_of(w, N * K * 4), range_of(scale, N * 4)) ||
+        overlaps(range_of(q, N * K), range_of(scale, N * 4)))
+        return fail(RTQ_ERR_OVERLAP, "rtq_quantize_q8_host: arrays overlap");
+    rtq::quantize_q8_host(w, q, scale, N, K, host_threads(threads));
+    return RTQ_OK;
+}
+
+rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int32_t threads) {
+    clear_error();
+    if (N < 0 || N > kMaxDim || K < 1 || K > kMaxDim || N * K > kMaxElems)
+        return fail(RTQ_ERR_SHAPE, "rtq_quantize_f8_host: N=%lld K=%lld out of range", (long long)N, (long long)K);
+    if (N == 0) return RTQ_OK;
+    if (!w || !codes) return fail(RTQ_ERR_NULL, "rtq_quantize_f8_host: a pointer argument is NULL");
+    if (!aligned(w, 4)) return fail(RTQ_ERR_ALIGN, "rtq_quantize_f8_host: misaligned pointer");
+    if (overlaps(range_of(w, N * K * 4), range_of(codes, N * K)))
+        return fail(RTQ_ERR_OVERLAP, "rtq_quantize_f8_host: output overlaps the weights");
+    rtq::quantize_f8_host(w, codes, N, K, host_threads(threads));
+    return RTQ_OK;
 }
 
 }  // extern "C"

@@ -6,6 +6,11 @@
 // min-MSE clip search over the shrink factors 1.00 .. 0.80.
 // int8 (RT-J int8 model card, "Quantization format"): one symmetric fp32
 // scale per output row, scale = max|row| / 127, W = q * scale.
+#include <algorithm>
+#include <cmath>
+#include <thread>
+#include <vector>
+
 #include "rtq_device.h"
 #include "rtq_internal.h"
 
@@ -16,11 +21,12 @@ namespace {
 constexpr int kGroup = 32;
 
 // ---------------------------------------------------------------------------
-// int4 quantizer: one thread per 32-group. All decisions in fp64 with every
-// operation rounded on its own (no contraction), so the codes and pairs are a
-// deterministic function of the fp32 input.
+// int4 quantizer: one thread per 32-group (on the GPU; the host quantizer runs
+// the same function per group). All decisions in fp64 with every operation
+// rounded on its own (no contraction), so the codes and pairs are a
+// deterministic function of the fp32 input, the same on both sides.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void quantize_q4_group(const float* __restrict__ w, uint8_t* __restrict__ payload,
+__host__ __device__ inline void quantize_q4_group(const float* __restrict__ w, uint8_t* __restrict__ payload,
                                                   uint32_t* __restrict__ pairs, int64_t gid,
                                                   int64_t groups_per_row, int64_t K) {
 #pragma clang fp contract(off)
@@ -54,8 +60,8 @@ __device__ __forceinline__ void quantize_q4_group(const float* __restrict__ w, u
         const double hi = alphas[a] * wmax;
         const uint32_t s16 = double_to_half_bits((hi - lo) / 15.0);
         const uint32_t m16 = double_to_half_bits(lo);
-        const double s = half_bits_to_double(s16);
-        const double m = half_bits_to_double(m16);
+        const double s = half_bits_value(s16);
+        const double m = half_bits_value(m16);
         double err = 0.0;
         uint32_t codes[4] = {0, 0, 0, 0};
 #pragma unroll
@@ -98,8 +104,25 @@ __global__ __launch_bounds__(256) void quantize_q4_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------------------
-// int8 quantizer: one 256-thread workgroup per row.
+// int8 quantizer: one 256-thread workgroup per row (the host quantizer runs
+// the same per-element arithmetic).
 // ---------------------------------------------------------------------------
+// Row scale from the row's largest magnitude: max|row| / 127, rounded to fp32.
+__host__ __device__ inline float q8_scale_of(float amax) {
+    return static_cast<float>(static_cast<double>(amax) / 127.0);
+}
+
+// Code of one weight: rint(w / scale) in fp64, half to even, clamped to
+// -127..127; 0 for a zero scale.
+__host__ __device__ inline int8_t q8_code(float w, double scd) {
+    double r = 0.0;
+    if (scd > 0.0) {
+        r = __builtin_rint(static_cast<double>(w) / scd);
+        r = fmin(fmax(r, -127.0), 127.0);
+    }
+    return static_cast<int8_t>(r);
+}
+
 __global__ __launch_bounds__(256) void quantize_q8_kernel(const float* __restrict__ w,
                                                           int8_t* __restrict__ q,
                                                           float* __restrict__ scale, int64_t K) {
@@ -113,18 +136,11 @@ __global__ __launch_bounds__(256) void quantize_q8_kernel(const float* __restric
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = amax;
     __syncthreads();
     amax = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
-    const float sc = static_cast<float>(static_cast<double>(amax) / 127.0);
+    const float sc = q8_scale_of(amax);
     if (threadIdx.x == 0) scale[row] = sc;
     const double scd = sc;
     int8_t* dst = q + row * K;
-    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
-        double r = 0.0;
-        if (scd > 0.0) {
-            r = __builtin_rint(static_cast<double>(src[k]) / scd);
-            r = fmin(fmax(r, -127.0), 127.0);
-        }
-        dst[k] = static_cast<int8_t>(r);
-    }
+    for (int64_t k = threadIdx.x; k < K; k += blockDim.x) dst[k] = q8_code(src[k], scd);
 }
 
 // ---------------------------------------------------------------------------
@@ -175,22 +191,41 @@ inline unsigned blocks_for(int64_t n, int per) {
 // its rounding to an integer is the mantissa (plus 8 for normal values), so
 // code = 8 * (e + 6) + rint(|w| * 2^(3-e)), and a rounding up to 16 carries
 // into the exponent field by itself.
+__host__ __device__ inline uint8_t f8_code(float w) {
+    const uint32_t bits = __builtin_bit_cast(uint32_t, w);
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t mag = bits & 0x7fffffffu;
+    uint32_t code = 0x7fu;                                       // infinity or NaN
+    if (mag < 0x7f800000u) {
+        const int eb = static_cast<int>(mag >> 23) - 127;
+        const int e = eb > -6 ? eb : -6;
+        const int q = static_cast<int>(rintf(ldexpf(__builtin_bit_cast(float, mag), 3 - e)));
+        const int c = 8 * (e + 6) + q;
+        code = c > 0x7e ? 0x7fu : static_cast<uint32_t>(c);
+    }
+    return static_cast<uint8_t>(sign | code);
+}
+
 __global__ __launch_bounds__(256) void quantize_f8_kernel(const float* __restrict__ w,
                                                           uint8_t* __restrict__ codes, int64_t total) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
-         i += static_cast<int64_t>(gridDim.x) * 256) {
-        const uint32_t bits = __float_as_uint(w[i]);
-        const uint32_t sign = (bits >> 24) & 0x80u;
-        const uint32_t mag = bits & 0x7fffffffu;
-        uint32_t code = 0x7fu;                                   // infinity or NaN
-        if (mag < 0x7f800000u) {
-            const int e = max(static_cast<int>(mag >> 23) - 127, -6);
-            const int q = static_cast<int>(rintf(ldexpf(__uint_as_float(mag), 3 - e)));
-            const int c = 8 * (e + 6) + q;
-            code = c > 0x7e ? 0x7fu : static_cast<uint32_t>(c);
-        }
-        codes[i] = static_cast<uint8_t>(sign | code);
+         i += static_cast<int64_t>(gridDim.x) * 256)
+        codes[i] = f8_code(w[i]);
+}
+
+// Host: rows [0, N) split into contiguous ranges over `threads` threads (the
+// calling thread takes the first range).
+template <class F>
+void for_rows(int64_t N, int threads, F&& fn) {
+    const int64_t t = std::max<int64_t>(1, std::min<int64_t>(threads, N));
+    const int64_t per = (N + t - 1) / t;
+    std::vector<std::thread> pool;
+    for (int64_t i = 1; i < t; ++i) {
+        const int64_t b = i * per, e = std::min(N, b + per);
+        if (b < e) pool.emplace_back([&fn, b, e] { fn(b, e); });
     }
+    fn(0, std::min(N, per));
+    for (auto& th : pool) th.join();
 }
 
 __global__ __launch_bounds__(256) void dequant_f8_kernel(const uint8_t* __restrict__ codes,
@@ -215,6 +250,33 @@ hipError_t launch_quantize_q8(const float* w, int8_t* q, float* scale, int64_t N
                               hipStream_t stream) {
     quantize_q8_kernel<<<static_cast<unsigned>(N), 256, 0, stream>>>(w, q, scale, K);
     return hipGetLastError();
+}
+
+void quantize_q4_host(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N, int64_t K, int threads) {
+    const int64_t G = K / kGroup;
+    uint32_t* pr = reinterpret_cast<uint32_t*>(pairs);
+    for_rows(N, threads, [&](int64_t r0, int64_t r1) {
+        for (int64_t gid = r0 * G; gid < r1 * G; ++gid) quantize_q4_group(w, payload, pr, gid, G, K);
+    });
+}
+
+void quantize_q8_host(const float* w, int8_t* q, float* scale, int64_t N, int64_t K, int threads) {
+    for_rows(N, threads, [&](int64_t r0, int64_t r1) {
+        for (int64_t row = r0; row < r1; ++row) {
+            const float* src = w + row * K;
+            float amax = 0.0f;
+            for (int64_t k = 0; k < K; ++k) amax = std::fmax(amax, std::fabs(src[k]));
+            const float sc = q8_scale_of(amax);
+            scale[row] = sc;
+            for (int64_t k = 0; k < K; ++k) q[row * K + k] = q8_code(src[k], sc);
+        }
+    });
+}
+
+void quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int threads) {
+    for_rows(N, threads, [&](int64_t r0, int64_t r1) {
+        for (int64_t i = r0 * K; i < r1 * K; ++i) codes[i] = f8_code(w[i]);
+    });
 }
 
 hipError_t launch_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N,

@@ -13,14 +13,26 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
     return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits16)));
 }
 
-__device__ __forceinline__ double half_bits_to_double(uint32_t bits16) {
-    return static_cast<double>(half_bits_to_float(bits16));
+// fp16 bit pattern -> its exact fp64 value, from the bits alone (used by the
+// quantizers, which also run on the host): (1024 + f) * 2^(e - 25) for normal
+// codes, f * 2^-24 for subnormal ones.
+__host__ __device__ inline double half_bits_value(uint32_t h) {
+    const uint32_t e = (h >> 10) & 0x1fu, f = h & 0x3ffu;
+    double v;
+    if (e == 0x1fu) {
+        v = f ? __builtin_nan("") : __builtin_inf();
+    } else {
+        const uint32_t mant = e ? (f | 0x400u) : f;
+        const int pw = e ? static_cast<int>(e) - 25 : -24;        // in [-24, 5]: a normal fp64 power of two
+        v = static_cast<double>(mant) * __builtin_bit_cast(double, static_cast<uint64_t>(1023 + pw) << 52);
+    }
+    return (h & 0x8000u) ? -v : v;
 }
 
 // fp64 -> fp16 bit pattern, round to nearest, ties to even, directly from the
 // fp64 value (no intermediate fp32 rounding). Subnormal fp16 results are kept;
 // magnitudes that round above 65504 become infinity.
-__device__ __forceinline__ uint32_t double_to_half_bits(double d) {
+__host__ __device__ inline uint32_t double_to_half_bits(double d) {
     const uint64_t b = __builtin_bit_cast(uint64_t, d);
     const uint32_t sign = static_cast<uint32_t>(b >> 63) << 15;
     const int exp = static_cast<int>((b >> 52) & 0x7ff);

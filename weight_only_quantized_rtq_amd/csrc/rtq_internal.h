@@ -61,6 +61,12 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hip
 bool direct_fits(const ProjTask* tasks, int count, int64_t M);
 hipError_t launch_direct(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
 
+// Host quantizers (quant.hip): the GPU quantizers' per-group / per-element
+// arithmetic run on host memory over `threads` threads; bit-identical results.
+void quantize_q4_host(const float* w, uint8_t* payload, uint16_t* pairs, int64_t N, int64_t K, int threads);
+void quantize_q8_host(const float* w, int8_t* q, float* scale, int64_t N, int64_t K, int threads);
+void quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int threads);
+
 // y += bias (broadcast over the M rows) for every task that has a bias, in
 // place, after the GEMM kernels that wrote y (same stream).
 hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
