@@ -20,21 +20,21 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 3>, 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split"): {"fetch_kib": 38380.081, "write_kib": 33901.695,
+    ("m80", "split"): {"fetch_kib": 38377.913, "write_kib": 33895.494,
                        "fetch_factor": 1.99987, "write_factor": 1.0,
                        "algorithmic_bytes": 80658432,
-                       "sources_sha256": "d4e4c3ee7deda1708edcdd93c92f7a048589969e47df9933052b776bee8e7073"},
+                       "sources_sha256": "e930273116f20d510b7a2f334c962e5cfab8b6f3e9da00e92e4be619a4ad0cc1"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27764.155, "write_kib": 34568.498,
+    ("m80", "bf16"): {"fetch_kib": 27759.439, "write_kib": 34626.949,
                       "fetch_factor": 1.99987, "write_factor": 1.0,
                       "algorithmic_bytes": 80658432,
-                      "sources_sha256": "d4e4c3ee7deda1708edcdd93c92f7a048589969e47df9933052b776bee8e7073"},
+                      "sources_sha256": "e930273116f20d510b7a2f334c962e5cfab8b6f3e9da00e92e4be619a4ad0cc1"},
     # split_gemm_kernel<1|2, 3>, 12 blocks at M = 65536: 288 dispatches per counter run
     # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split"): {"fetch_kib": 178341.904, "write_kib": 249551.096,
+    ("m65536", "split"): {"fetch_kib": 180120.565, "write_kib": 249533.311,
                           "fetch_factor": 1.99987, "write_factor": 1.0,
                           "algorithmic_bytes": 419840512,
-                          "sources_sha256": "d4e4c3ee7deda1708edcdd93c92f7a048589969e47df9933052b776bee8e7073"},
+                          "sources_sha256": "e930273116f20d510b7a2f334c962e5cfab8b6f3e9da00e92e4be619a4ad0cc1"},
 }
 
 
