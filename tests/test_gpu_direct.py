@@ -213,3 +213,21 @@ def test_direct_guard_bands_and_determinism(fmt, K, M, mode):
     assert np.all(b[:guard] == 1234.5) and np.all(b[guard + M * N:] == 1234.5)
     rtq.gemm(x, w, y=y)
     assert np.array_equal(host(y).view(np.uint32), y1.view(np.uint32))
+
+
+@pytest.mark.parametrize("M", [1, 20])
+def test_direct_int4_pairs_not_16_byte_aligned(M, mode):
+    """The direct kernel reads int4 (scale, min) words 16 bytes at a time, so a
+    pair array that is only 4-byte aligned (the ABI's minimum) sends the call
+    to the grouped path; the result is the same."""
+    N, K = 512, 512          # the bf16 mode's fp32-x bar is statistical: full-width outputs
+    W = synth.weight(69, 0, 0, "w1", N, K)
+    x = synth.activation(69, 0, "x_ffn", M, K)
+    ref = oracle.quantize(W, "q4")
+    payload = dev(ref[0])
+    buf = torch.empty(N * (K // 32) * 2 + 2, dtype=torch.float16, device=DEV)
+    pairs = buf[2:].view(N, K // 32, 2)                           # 4 bytes past a 16-byte boundary
+    pairs.copy_(dev(ref[1]))
+    assert pairs.data_ptr() % 16 == 4
+    y = host(rtq.gemm(dev(x), rtq.Q4Weight(payload, pairs)))
+    check(y, mode, "q4", x, ref)

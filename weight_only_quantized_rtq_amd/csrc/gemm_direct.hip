@@ -75,13 +75,17 @@ struct DirectLds {
     static constexpr int XBUF = PG * GBYTES;            // one phase
     static constexpr int SUMS = kSumSlots * 16 * TM * 4;
     static constexpr int XTOTAL = 2 * XBUF + SUMS;
-    // per-wave int4 staging: 16 rows of 4 x 16 bytes of codes and the 4
-    // (scale, min) words; two areas, used by alternate column tiles
+    // per-wave int4 staging: 16 rows of 4 x 16 bytes of codes (+ 16 bytes of
+    // padding); two areas, used by alternate column tiles
     static constexpr int STG_ROW = 80;
     static constexpr int STG_TILE = 16 * STG_ROW;
     static constexpr int STG_AREAS = 2;
     static constexpr int STG = STG_AREAS * STG_TILE;
-    static constexpr int TOTAL = XTOTAL + 4 * STG;
+    // per-wave int4 (scale, min) words of every column tile for the whole K,
+    // rows padded by 16 bytes: at most 4 tiles x 16 rows x (16 + 4) words
+    // (tn * K / 32 is at most 64 words per row)
+    static constexpr int PAIRS = 4 * 16 * 80;
+    static constexpr int TOTAL = XTOTAL + 4 * STG + 4 * PAIRS;
 };
 
 template <int FMT, int TN, int NL, int G, int TM>
@@ -153,17 +157,12 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
     // path takes weights below 2^32 bytes (N*K < 2^32).
     const unsigned char* payload = static_cast<const unsigned char*>(payload_v);
     const unsigned char* pairs = static_cast<const unsigned char*>(scale_v);
-    uint32_t woff[TN], poff[TN];
+    uint32_t woff[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const uint32_t col = static_cast<uint32_t>(min(n0 + wave * TN * 16 + tn * 16 + li, N - 1));
-        if constexpr (FMT == kFmtQ4) {
-            woff[tn] = col * (K / 2) + 16 * lc;
-            poff[tn] = (col * G + lc) * 4;
-        } else {
-            woff[tn] = col * K + 16 * lc;
-            poff[tn] = 0;
-        }
+        if constexpr (FMT == kFmtQ4) woff[tn] = col * (K / 2) + 16 * lc;
+        else woff[tn] = col * K + 16 * lc;
     }
     constexpr int NB = G / 4;                                    // blocks of 4 groups
     constexpr int CW = FMT == kFmtQ4 ? 4 : 8;                    // code words per lane and block
@@ -175,7 +174,7 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
             if constexpr (FMT == kFmtQ4) {
                 const uint4 v = *reinterpret_cast<const uint4*>(payload + woff[tn] + b * 64);
                 c[tn][0] = v.x; c[tn][1] = v.y; c[tn][2] = v.z; c[tn][3] = v.w;
-                pr[tn] = *reinterpret_cast<const uint32_t*>(pairs + poff[tn] + b * 16);
+                pr[tn] = 0;
             } else {
                 const uint4 v0 = *reinterpret_cast<const uint4*>(payload + woff[tn] + b * 128);
                 const uint4 v1 = *reinterpret_cast<const uint4*>(payload + woff[tn] + b * 128 + 64);
@@ -185,22 +184,62 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
             }
         }
     };
+    // int4 (scale, min) words: every column tile's rows for the whole K, read
+    // once in contiguous 16-byte pieces (a tile's rows are consecutive in the
+    // pair array) into this wave's area, row r of tile tn at
+    // tn * 16 * PROW + r * PROW (PROW = 4G + 16 bytes); b_stage reads the
+    // block's four words of its row from there.
+    constexpr int PROW = 4 * G + 16;
+    static_assert(TN * 16 * PROW <= L::PAIRS, "pair area");
+    unsigned char* pair_area = smem + L::XTOTAL + 4 * L::STG + wave * L::PAIRS;
+    const unsigned char* pair_row = pair_area + li * PROW;
+    constexpr int PTILE = 16 * 4 * G;                          // bytes of a tile's 16 rows of words
+    constexpr int PIECES = FMT == kFmtQ4 ? (PTILE + 1023) / 1024 : 0;   // 16-byte loads per lane and tile
+    uint4 pv[TN][PIECES > 0 ? PIECES : 1];
+    auto pairs_issue = [&]() {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int col0 = n0 + wave * TN * 16 + tn * 16;
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) {
+                const int o = i * 1024 + lane * 16;                       // byte of the tile's block
+                if (o < PTILE) {
+                    const int r = o / (4 * G), w = o - r * (4 * G);
+                    const uint32_t row = static_cast<uint32_t>(min(col0 + r, N - 1));
+                    pv[tn][i] = *reinterpret_cast<const uint4*>(pairs + row * (4u * G) + w);
+                }
+            }
+        }
+    };
+    auto pairs_store = [&]() {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int i = 0; i < PIECES; ++i) {
+                const int o = i * 1024 + lane * 16;
+                if (o < PTILE) {
+                    const int r = o / (4 * G), w = o - r * (4 * G);
+                    *reinterpret_cast<uint4*>(pair_area + tn * (16 * PROW) + r * PROW + w) = pv[tn][i];
+                }
+            }
+    };
+
     // Operand words of the block's 4 MFMAs (wq[tn][j] for group 4b + j) and, for
     // int4, its (scale, min) words. A staging area is rewritten (two tiles or a
     // block later) only after this wave's reads of it: one wave's LDS operations
     // run in order, so no barrier is needed.
     unsigned char* stg = smem + L::XTOTAL + wave * L::STG + li * L::STG_ROW;
-    auto b_stage = [&](const uint32_t (&c)[TN][CW], const uint32_t (&pr)[TN], uint32_t (&wq)[TN][4][2],
+    auto b_stage = [&](int b, const uint32_t (&c)[TN][CW], const uint32_t (&pr)[TN], uint32_t (&wq)[TN][4][2],
                        uint32_t (&pq)[TN][4]) {
+        (void)pr;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
                 unsigned char* t = stg + (tn % L::STG_AREAS) * L::STG_TILE;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) *reinterpret_cast<uint32_t*>(t + w * 16 + lc * 4) = c[tn][w];
-                *reinterpret_cast<uint32_t*>(t + 64 + lc * 4) = pr[tn];
                 const u32x4 r = *reinterpret_cast<const u32x4*>(t + lc * 16);
-                const u32x4 q = *reinterpret_cast<const u32x4*>(t + 64);
+                const u32x4 q = *reinterpret_cast<const u32x4*>(pair_row + tn * (16 * PROW) + b * 16);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     wq[tn][j][0] = r[j];
@@ -292,15 +331,17 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
     };
 
     // ---- prologue: zero both x areas and the sums (rows >= M stay zero), load
-    //      phase 0 of x, start the weights, stage x ----
+    //      phase 0 of x and the int4 pair words, start the weights, stage both ----
     {
         uint4* z = reinterpret_cast<uint4*>(smem);
         for (int t = tid; t < L::XTOTAL / 16; t += 256) z[t] = make_uint4(0u, 0u, 0u, 0u);
     }
     lds_barrier();
     x_load(0);
+    pairs_issue();
 #pragma unroll
     for (int b = 0; b < DB; ++b) b_issue(b, bc[b], bp[b]);
+    pairs_store();
     x_convert(0);
     lds_barrier();
     u32x4 xcur[NL];
@@ -319,7 +360,7 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
         if (g % PG == 0 && ph + 1 < NPH) x_load(ph + 1);
         if (jb == 0) {
             constexpr int b = g / 4;
-            b_stage(bc[b % DB], bp[b % DB], wq, pq);
+            b_stage(b, bc[b % DB], bp[b % DB], wq, pq);
             if (b + DB < NB) b_issue(b + DB, bc[b % DB], bp[b % DB]);
         }
         u32x4 bop[TN];
@@ -439,8 +480,11 @@ void launch_direct_tm(int tm, int tiles, const DirectArgs& g, hipStream_t stream
 
 bool direct_fits(const ProjTask* tasks, int count, int64_t M) {
     if (M < 1 || M > 16 * kDirectMaxTM) return false;
-    for (int i = 0; i < count; ++i)
+    for (int i = 0; i < count; ++i) {
         if (!direct_k(tasks[i].K)) return false;
+        // int4 (scale, min) words are read 16 bytes at a time
+        if (tasks[i].fmt == kFmtQ4 && (reinterpret_cast<uintptr_t>(tasks[i].scale) & 15) != 0) return false;
+    }
     return true;
 }
 

@@ -56,8 +56,9 @@ bool split_ok(const ProjTask& task);
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
 
 // Small-M path of the split arithmetic (gemm_direct.hip): one launch, whole K
-// per workgroup, x split in the kernel. direct_fits(): M in 1..32 and every K
-// in {256, 512, 1024, 2048}; the tasks must also satisfy split_ok().
+// per workgroup, x split in the kernel. direct_fits(): M in 1..32, every K in
+// {256, 512, 1024, 2048} and int4 pair arrays 16-byte aligned; the tasks must
+// also satisfy split_ok().
 bool direct_fits(const ProjTask* tasks, int count, int64_t M);
 hipError_t launch_direct(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
 
