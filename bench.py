@@ -36,6 +36,8 @@ PEAK_FP32_MFMA_TFLOPS = 157.3      # MI355X dense fp32 matrix
 PEAK_BF16_MFMA_TFLOPS = 2516.6     # MI355X dense bf16 matrix
 WEIGHT_SETS = 16
 KERNELS = {  # main GEMM kernel of each (math, workload), as rocprofv3 names it
+    ("split16", "m80"): "split_grouped_kernel<5, 2>",
+    ("split16", "m65536"): "split_gemm_kernel<1|2, 2>",
     ("split", "m80"): "split_grouped_kernel<5, 3>",
     ("split", "m65536"): "split_gemm_kernel<1|2, 3>",
     ("bf16", "m80"): "split_grouped_kernel<5, 1>",
@@ -57,11 +59,14 @@ def parse():
     ap.add_argument("--recipe", choices=["mixed", "all_q8", "all_f8"], default="mixed",
                     help="weight formats: the int4 card's mixed int4/int8 recipe (default), the int8 card's "
                          "all-int8 recipe, or the FP8 card's all-E4M3 weights")
-    ap.add_argument("--math", choices=["split", "fp32", "bf16"], default="split",
-                    help="GEMM arithmetic: exact bf16x3 split on the bf16 MFMA (default), fp32 MFMA, or "
-                         "activations rounded to bf16 (lower precision)")
+    ap.add_argument("--math", choices=["split16", "split", "fp32", "bf16"], default="split16",
+                    help="GEMM arithmetic: row-scaled activations in two fp16 limbs on the fp16 MFMA (default), "
+                         "the exact bf16x3 split on the bf16 MFMA, fp32 MFMA, or activations rounded to bf16 "
+                         "(lower precision)")
     ap.add_argument("--no-bf16-path", action="store_true",
                     help="skip the separately reported bf16-activation timing")
+    ap.add_argument("--no-exact-path", action="store_true",
+                    help="skip the separately reported exact bf16x3 timing (with --math split16)")
     ap.add_argument("--compare-fp32", action="store_true",
                     help="also time the fp32-MFMA path (few steps) and report it alongside")
     ap.add_argument("--m-sweep", default=None,
@@ -246,10 +251,13 @@ def load_traffic(workload, math, recipe="mixed"):
 def roofline(res, math, workload, recipe="mixed"):
     """Roofline of the main GEMM kernel: algorithmic flops per launch over the
     kernel's average launch duration, against the peak of the matrix unit it
-    runs on (split: bf16 MFMA, three limb products per algorithmic multiply-add)."""
+    runs on (split: bf16 MFMA, three limb products per algorithmic multiply-add;
+    split16: fp16 MFMA, two)."""
     ach = res["kernel_tflops"]
     if math == "split":
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
+    elif math == "split16":
+        peak, issued = PEAK_BF16_MFMA_TFLOPS, 2            # the dense fp16 matrix peak equals the bf16 one
     elif math == "bf16":
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 1
     else:
@@ -320,23 +328,35 @@ def main():
     BIAS = args.bias
     rtq.load_library()
     torch.cuda.init()
-    modes = {"split": rtq.MATH_SPLIT_BF16, "fp32": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16}
+    modes = {"split16": rtq.MATH_SPLIT_F16, "split": rtq.MATH_SPLIT_BF16, "fp32": rtq.MATH_FP32_MFMA,
+             "bf16": rtq.MATH_BF16}
     rtq.set_math(modes[args.math])
+    fp32_modes = ("split16", "split")
     out = {}
     if args.workload in ("m80", "both"):
         out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup, args.recipe)
     if args.workload in ("m65536", "both"):
         out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large, args.recipe)
     fp32 = {}
-    if args.compare_fp32 and args.math == "split":
+    if args.compare_fp32 and args.math in fp32_modes:
         rtq.set_math(rtq.MATH_FP32_MFMA)
         for wl in out:
             r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1, args.recipe)
             fp32[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                         "roofline": roofline(r, "fp32", wl, args.recipe)}
+        rtq.set_math(modes[args.math])
+    exact = {}
+    if not args.no_exact_path and args.math == "split16":
         rtq.set_math(rtq.MATH_SPLIT_BF16)
+        for wl in out:
+            st, wu = (args.steps, args.warmup) if wl == "m80" else (args.steps_large, args.warmup_large)
+            r = measure(torch, rtq, synth, wl, st, wu, args.recipe)
+            exact[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
+                         "weight_gbs": round(r["weight_gbs"], 2), "steps": r["steps"],
+                         "roofline": roofline(r, "split", wl, args.recipe)}
+        rtq.set_math(modes[args.math])
     bf16 = {}
-    if not args.no_bf16_path and args.math == "split":
+    if not args.no_bf16_path and args.math in fp32_modes:
         rtq.set_math(rtq.MATH_BF16)
         for wl in out:
             st, wu = (args.steps, args.warmup) if wl == "m80" else (args.steps_large, args.warmup_large)
@@ -345,7 +365,7 @@ def main():
                         "weight_gbs": round(r["weight_gbs"], 2),
                         "weight_hbm_frac": round(r["weight_gbs"] / PEAK_HBM_GBS, 5), "steps": r["steps"],
                         "roofline": roofline(r, "bf16", wl, args.recipe)}
-        rtq.set_math(rtq.MATH_SPLIT_BF16)
+        rtq.set_math(modes[args.math])
 
     prim_name = "m80" if "m80" in out else "m65536"
     prim = out[prim_name]
@@ -365,13 +385,16 @@ def main():
         "warmup": args.warmup if prim_name == "m80" else args.warmup_large,
         "ms_per_step": round(prim["ms_per_step"], 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"split": "bf16x3/f32", "fp32": "f32", "bf16": "bf16/f32"}[args.math],
+        "dtype": {"split16": "f16x2/f32", "split": "bf16x3/f32", "fp32": "f32", "bf16": "bf16/f32"}[args.math],
         "data": "synthetic",
         "config": {"workload": cfg, "M": prim["M"], "n_blocks": synth.NUM_BLOCKS,
                    "weight_sets": WEIGHT_SETS if prim_name == "m80" else 1, "recipe": {"mixed": "mixed int4/int8", "all_q8": "all int8",
                                                                                "all_f8": "all FP8 E4M3"}[args.recipe],
                    "d_model": synth.D_MODEL, "d_ff": synth.D_FF, "bias": bool(args.bias),
-                   "math": {"split": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation",
+                   "math": {"split16": "each activation row scaled by a power of two and split into 2 fp16 limbs "
+                                       "(22 significant bits), exact code products, fp32 accumulation; rows of "
+                                       "M <= 32 calls take the exact 3-limb direct kernel",
+                            "split": "activations split exactly into 3 bf16 limbs, exact products, fp32 accumulation",
                             "fp32": "fp32 MFMA on dequantized weights",
                             "bf16": "activations rounded to bf16 (lower precision), exact weight products, "
                                     "fp32 accumulation"}[args.math]},
@@ -388,6 +411,11 @@ def main():
                     "roofline": roofline(r, args.math, wl, args.recipe)}
     if fp32:
         line["fp32_mfma_path"] = fp32
+    if exact:
+        line["exact_bf16x3_path"] = {
+            "note": "activations split exactly into 3 bf16 limbs (the library's default arithmetic), same "
+                    "workloads; reported next to the headline two-limb fp16 figures",
+            **exact}
     if bf16:
         line["bf16_activation_path"] = {
             "note": "x rounded to the nearest bf16 (lower precision: 3e-3 bar, not 1e-5), one bf16 MFMA per "

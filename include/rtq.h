@@ -192,9 +192,20 @@ rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64
  *   relative per element), so it is a lower-precision mode. Shapes the split
  *   path does not take (int8/FP8 K not a multiple of 32, x or payload not
  *   16-byte aligned, N*K >= 2^32) run on the fp32 kernels in every mode.
+ * RTQ_MATH_SPLIT_F16: fp32 activations in two fp16 limbs. Each row of x is
+ *   scaled by the power of two 2^e that puts its largest magnitude in
+ *   [2^14, 2^15) (exact), and every scaled value v is split into
+ *   h = fp16(v) and l = fp16(v - h), both rounded to nearest: h + l carries 22
+ *   significant bits of v (relative error at most 2^-22 per element, plus
+ *   2^-25 * 2^-e absolute for elements far below the row's largest). The
+ *   fp16 matrix cores (v_mfma_f32_16x16x32_f16) run two limb products per
+ *   code instead of three; each output row is scaled back by 2^-e. Calls that
+ *   take the small-M direct kernel (M <= 32, every K in 256..2048) run the
+ *   exact three-limb split there, which needs no row scale. Meets the same
+ *   parity bar as RTQ_MATH_SPLIT_BF16 (relative Frobenius error 1e-5).
  * Calls already enqueued are not affected. Returns RTQ_ERR_FORMAT for an
  * unknown mode. */
-enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2 };
+enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2, RTQ_MATH_SPLIT_F16 = 3 };
 rtq_status rtq_set_math(int32_t mode);
 int32_t rtq_get_math(void);
 

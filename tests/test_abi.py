@@ -185,6 +185,8 @@ def test_math_mode_switch(lib):
     assert lib.rtq_set_math(7) == ERR_FORMAT
     assert lib.rtq_set_math(rtq.MATH_FP32_MFMA) == OK
     assert lib.rtq_get_math() == rtq.MATH_FP32_MFMA
+    assert lib.rtq_set_math(rtq.MATH_SPLIT_F16) == OK
+    assert lib.rtq_get_math() == rtq.MATH_SPLIT_F16
     assert lib.rtq_set_math(rtq.MATH_BF16) == OK
     assert lib.rtq_get_math() == rtq.MATH_BF16
     assert lib.rtq_set_math(-1) == ERR_FORMAT and lib.rtq_get_math() == rtq.MATH_BF16

@@ -35,9 +35,10 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-@pytest.fixture(params=[rtq.MATH_SPLIT_BF16, rtq.MATH_FP32_MFMA], ids=["split_bf16", "fp32_mfma"])
+@pytest.fixture(params=[rtq.MATH_SPLIT_BF16, rtq.MATH_FP32_MFMA, rtq.MATH_SPLIT_F16],
+                ids=["split_bf16", "fp32_mfma", "split_f16"])
 def math(request):
-    """Runs a test under both arithmetic modes of the GEMM entry points."""
+    """Runs a test under each fp32-activation arithmetic of the GEMM entry points."""
     rtq.set_math(request.param)
     yield request.param
     rtq.set_math(rtq.MATH_SPLIT_BF16)

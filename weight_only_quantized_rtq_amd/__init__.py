@@ -44,7 +44,7 @@ EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rt
            "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
-MATH_SPLIT_BF16, MATH_FP32_MFMA, MATH_BF16 = 0, 1, 2
+MATH_SPLIT_BF16, MATH_FP32_MFMA, MATH_BF16, MATH_SPLIT_F16 = 0, 1, 2, 3
 
 
 class RtqError(RuntimeError):
@@ -120,8 +120,10 @@ def version() -> str:
 
 
 def set_math(mode: int) -> None:
-    """MATH_SPLIT_BF16 (default, exact fp32 activations), MATH_FP32_MFMA, or
-    MATH_BF16 (activations rounded to bf16) for the GEMM entry points (rtq_set_math)."""
+    """MATH_SPLIT_BF16 (default, exact fp32 activations), MATH_FP32_MFMA,
+    MATH_BF16 (activations rounded to bf16) or MATH_SPLIT_F16 (row-scaled
+    activations in two fp16 limbs, 22 significant bits) for the GEMM entry
+    points (rtq_set_math)."""
     _check(load_library().rtq_set_math(mode))
 
 

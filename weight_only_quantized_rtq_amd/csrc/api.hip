@@ -147,7 +147,8 @@ extern "C" {
 
 rtq_status rtq_set_math(int32_t mode) {
     clear_error();
-    if (mode != RTQ_MATH_SPLIT_BF16 && mode != RTQ_MATH_FP32_MFMA && mode != RTQ_MATH_BF16)
+    if (mode != RTQ_MATH_SPLIT_BF16 && mode != RTQ_MATH_FP32_MFMA && mode != RTQ_MATH_BF16 &&
+        mode != RTQ_MATH_SPLIT_F16)
         return fail(RTQ_ERR_FORMAT, "rtq_set_math: unknown mode %d", mode);
     g_math.store(mode, std::memory_order_relaxed);
     return RTQ_OK;

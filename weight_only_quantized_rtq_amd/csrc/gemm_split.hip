@@ -27,6 +27,16 @@
 // tile instead of three, y = bf16(x) . W^T with the same exact weight side and
 // fp32 accumulation; the group sums X_g are those of the rounded values.
 //
+// Two fp16 limbs (NL = 2). Each row of x is scaled by a power of two 2^e so
+// that its largest magnitude lies in [2^14, 2^15), then split as h = fp16(v),
+// l = fp16(v - h) (v = x * 2^e, both roundings to nearest). h + l holds v to
+// 22 significant bits (relative error <= 2^-22 per element, plus an absolute
+// 2^-25 in the scaled units for elements far below the row's largest). Codes
+// are exact in fp16, products of code and limb exact in fp32, and
+// v_mfma_f32_16x16x32_f16 accumulates two limb products per group and tile
+// instead of three. X_g are the sums of the scaled values; every output is
+// scaled back by 2^-e of its row (exact) before the int8 scale and the bias.
+//
 // Data movement.
 //  1. A pre-pass (prep_kernel) splits every distinct activation once into a
 //     limb image in a device workspace: NL bf16 planes in MFMA operand order,
@@ -56,16 +66,21 @@ namespace {
 // Limb image of one activation x [M][K] with NL limbs (G = K/32 groups, RB row
 // blocks of 16, RB*16 >= M; rows >= M are zero):
 //   block (g, rb) of NL KB at byte ((g*RB + rb)*NL + limb) * 1024; with NL = 3
-//   limb 0 = x1 (high), 1 = x2, 2 = x3, with NL = 1 the bf16-rounded x; inside
-//   a limb, row r (0..15) and 16-byte chunk c (k = 8c..8c+7 of the group) sit
-//   at (r*4 + (c ^ ((r>>2)&3))) * 16;
-//   then the group sums X[g][row] (fp32, RB*16 rows per group).
+//   limb 0 = x1 (high), 1 = x2, 2 = x3, with NL = 1 the bf16-rounded x, with
+//   NL = 2 the fp16 limbs h, l of the scaled row; inside a limb, row r (0..15)
+//   and 16-byte chunk c (k = 8c..8c+7 of the group) sit at
+//   (r*4 + (c ^ ((r>>2)&3))) * 16;
+//   then the group sums X[g][row] (fp32, RB*16 rows per group);
+//   with NL = 2 then the row exponents e[row] (int32, RB*16 rows).
 // For a fixed group the RB blocks are contiguous, so a row block of BM rows is
 // one contiguous run of BM/16 * NL KB.
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int64_t image_plane_bytes(int G, int RB, int NL) { return int64_t(G) * RB * 1024 * NL; }
-__host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
+__host__ __device__ inline int64_t image_exp_offset(int G, int RB, int NL) {
     return image_plane_bytes(G, RB, NL) + int64_t(G) * RB * 16 * 4;
+}
+__host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
+    return image_exp_offset(G, RB, NL) + (NL == 2 ? int64_t(RB) * 16 * 4 : 0);
 }
 
 constexpr int kMaxImages = 48;
@@ -139,6 +154,89 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
         float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, NL));
         X[static_cast<int64_t>(g) * RB * 16 + row] = s;
     }
+}
+
+// Two fp16 limbs (NL = 2). One wave per row: the row's scale needs its largest
+// magnitude first. Lane L takes k = 512*j + 8L .. 8L+7 of every 512-wide piece
+// j (group 16j + L/4, chunk L%4); the row maximum is a wave reduction. With
+// max|x[row][:]| = f * 2^E, f in [0.5, 1), the exponent is e = 15 - E (e = 15
+// for a zero row). Rows of K <= 512*kPrepHold stay in registers between the
+// two passes; longer rows are read again. The group sums use the order of
+// prep_kernel.
+constexpr int kPrepHold = 4;
+__global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs p) {
+    const int b = blockIdx.x;
+    const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
+    const int M = p.M[i], K = p.K[i], RB = p.RB[i];
+    const int G = K / 32;
+    const int row = (b - p.block_begin[i]) * 4 + static_cast<int>(threadIdx.x >> 6);   // < RB * 16
+    const int lane = threadIdx.x & 63;
+    const int c = lane & 3;
+    const int r = row & 15, rb = row >> 4;
+    const bool live = row < M;
+    const float* src = p.x[i] + static_cast<int64_t>(live ? row : 0) * K + 8 * lane;
+    const int pieces = (K + 511) / 512;
+    auto load = [&](int j, float (&v)[8]) {
+        if (live && 512 * j + 8 * lane < K) {
+            const float4* q = reinterpret_cast<const float4*>(src + 512 * j);
+            const float4 a = q[0], bb = q[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = 0.0f;
+        }
+    };
+    float hold[kPrepHold][8];
+    float mx = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kPrepHold; ++j) {
+        load(j, hold[j]);                                        // past the row: zeros
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(hold[j][e]));
+    }
+    for (int j = kPrepHold; j < pieces; ++j) {
+        float v[8];
+        load(j, v);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    int E = 0;
+    (void)frexpf(mx, &E);
+    const int ex = 15 - E;
+
+    unsigned char* img = p.img[i];
+    float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, 2));
+    auto emit = [&](int j, float (&v)[8]) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = ldexpf(v[e], ex);
+        uint32_t h[4], l[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) split_f16x2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+        float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+        const float s1 = __shfl_xor(s, 1, 64);
+        s = (c & 1) ? s1 + s : s + s1;
+        const float s2 = __shfl_xor(s, 2, 64);
+        s = (c & 2) ? s2 + s : s + s2;
+        const int g = 16 * j + (lane >> 2);
+        if (g < G) {
+            unsigned char* blk = img + (static_cast<int64_t>(g) * RB + rb) * 2048 + swz(r, c) * 16;
+            *reinterpret_cast<uint4*>(blk) = make_uint4(h[0], h[1], h[2], h[3]);
+            *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(l[0], l[1], l[2], l[3]);
+            if (c == 0) X[static_cast<int64_t>(g) * RB * 16 + row] = s;
+        }
+    };
+#pragma unroll
+    for (int j = 0; j < kPrepHold; ++j)
+        if (j < pieces) emit(j, hold[j]);
+    for (int j = kPrepHold; j < pieces; ++j) {
+        float v[8];
+        load(j, v);
+        emit(j, v);
+    }
+    if (lane == 0) reinterpret_cast<int*>(img + image_exp_offset(G, RB, 2))[row] = ex;
 }
 
 // ---------------------------------------------------------------------------
@@ -226,7 +324,7 @@ template <int FMT, int WM, int WN, int TM, int TN, int XL, int WL, int NL>
 __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
     using L = Lds<BM, TN, XL, WL, NL>;
-    static_assert(NL == 1 || NL == 3, "limbs");
+    static_assert(NL >= 1 && NL <= 3, "limbs");
     static_assert(WM * WN == 4, "four waves");
     static_assert(WL == 0 || (XL >= 1 && XL <= 2 * WL && WL <= 3), "prefetch leads");
     const int tid = threadIdx.x;
@@ -396,45 +494,41 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
-                b[tn] = codes4_to_bf16(cq[tn][0]);
+                b[tn] = NL == 2 ? codes4_to_f16(cq[tn][0]) : codes4_to_bf16(cq[tn][0]);
                 s[tn] = half_bits_to_float(cp[tn] & 0xffffu);
                 const float mn = half_bits_to_float(cp[tn] >> 16);
                 mreg[tn] = lc == (i & 3) ? mn : mreg[tn];
+            } else if constexpr (FMT == kFmtF8) {
+                b[tn] = NL == 2 ? codes8f_to_f16(cq[tn][0], cq[tn][1]) : codes8f_to_bf16(cq[tn][0], cq[tn][1]);
             } else {
-                if constexpr (FMT == kFmtF8) b[tn] = codes8f_to_bf16(cq[tn][0], cq[tn][1]);
-                else b[tn] = codes8_to_bf16(cq[tn][0], cq[tn][1]);
+                b[tn] = NL == 2 ? codes8_to_f16(cq[tn][0], cq[tn][1]) : codes8_to_bf16(cq[tn][0], cq[tn][1]);
             }
         }
+        // the limb products, smallest limb first
+        auto mma = [](const u32x4& x, const u32x4& w, floatx4 c) {
+            if constexpr (NL == 2) return mfma_f16(x, w, c);
+            else return mfma_bf16(x, w, c);
+        };
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
             const unsigned char* blk = base + (wm * TM + tm) * (NL * 1024) + aoff;
-            const u32x4 xh = *reinterpret_cast<const u32x4*>(blk);
-            u32x4 xm = {}, xl = {};
-            if constexpr (NL == 3) {
-                xm = *reinterpret_cast<const u32x4*>(blk + 1024);
-                xl = *reinterpret_cast<const u32x4*>(blk + 2048);
-            }
+            u32x4 xl[NL];
+#pragma unroll
+            for (int l = 0; l < NL; ++l) xl[l] = *reinterpret_cast<const u32x4*>(blk + l * 1024);
             if constexpr (FMT == kFmtQ4) {
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn) {
                     floatx4 p = floatx4{0.f, 0.f, 0.f, 0.f};
-                    if constexpr (NL == 3) {
-                        p = mfma_bf16(xl, b[tn], p);
-                        p = mfma_bf16(xm, b[tn], p);
-                    }
-                    p = mfma_bf16(xh, b[tn], p);
+#pragma unroll
+                    for (int l = NL - 1; l >= 0; --l) p = mma(xl[l], b[tn], p);
 #pragma unroll
                     for (int e = 0; e < 4; ++e) acc[tm][tn][e] = fmaf(s[tn], p[e], acc[tm][tn][e]);
                 }
             } else {
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    if constexpr (NL == 3) {
-                        acc[tm][tn] = mfma_bf16(xl, b[tn], acc[tm][tn]);
-                        acc[tm][tn] = mfma_bf16(xm, b[tn], acc[tm][tn]);
-                    }
-                    acc[tm][tn] = mfma_bf16(xh, b[tn], acc[tm][tn]);
-                }
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int l = NL - 1; l >= 0; --l) acc[tm][tn] = mma(xl[l], b[tn], acc[tm][tn]);
             }
         }
     };
@@ -524,7 +618,16 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         min_flush(i);
     }
 
-    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile ----
+    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile. With two
+    //      fp16 limbs each row is first scaled back by 2^-e[row] (exact). ----
+    int rexp[TM][4];
+    if constexpr (NL == 2) {
+        const int* exps = reinterpret_cast<const int*>(a.img + image_exp_offset(G, RB, NL));
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rexp[tm][e] = -exps[min(m0 + wm * TM * 16 + tm * 16 + 4 * lc + e, RB * 16 - 1)];
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + wn * TN * 16 + tn * 16 + li;
@@ -539,6 +642,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                 const int row = m0 + wm * TM * 16 + tm * 16 + 4 * lc + e;
                 if (row < M) {
                     float v = acc[tm][tn][e];
+                    if constexpr (NL == 2) v = ldexpf(v, rexp[tm][e]);
                     if constexpr (FMT == kFmtQ8) v *= sc;
                     if (a.bias) v += bv;
                     a.y[static_cast<int64_t>(row) * N + col] = v;
@@ -552,13 +656,20 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 constexpr int kLWM = 1, kLWN = 4, kLTM = 8, kLTN = 2;
 constexpr int kLBM = kLWM * kLTM * 16;
 constexpr int kLBN = kLWN * kLTN * 16;
+// Prefetch leads of the large-M kernel per limb count. One or two limbs: the
+// x stages run a step ahead and the weights stream through a per-wave LDS ring
+// a chunk ahead, and three workgroups (four with one limb) still fit a CU.
+// Three limbs (24 KB stages) keep the registers-one-step-ahead schedule, which
+// fits three workgroups where the LDS ring would leave two.
+template <int NL> struct LargeLead { static constexpr int XL = NL == 3 ? 0 : 1, WL = NL == 3 ? 0 : 1; };
 
 template <int FMT, int NL>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, 1, 0, 0, NL>::TOTAL];
+    constexpr int XL = LargeLead<NL>::XL, WL = LargeLead<NL>::WL;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, WL ? kLTN : 1, XL, WL, NL>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int nt = w % tiles_n;
-    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, 0, 0, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
+    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, XL, WL, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
 // Small M (<= 80): one row block of TM*16 rows; 4 waves side by side along N,
@@ -698,13 +809,19 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
             p.K[c] = u.K;
             p.RB[c] = RB;
             p.block_begin[c] = blocks;
-            const int64_t threads = int64_t(RB) * 16 * (u.K / 32) * 4;
-            blocks += static_cast<int>((threads + 255) / 256);
+            if (NL == 2) {
+                blocks += RB * 4;                           // one wave per row
+            } else {
+                const int64_t threads = int64_t(RB) * 16 * (u.K / 32) * 4;
+                blocks += static_cast<int>((threads + 255) / 256);
+            }
         }
         p.block_begin[p.count] = blocks;
         seg_fill_coarse(p.block_begin, p.block_coarse, p.count);
         if (NL == 1)
             prep_kernel<1><<<blocks, 256, 0, stream>>>(p);
+        else if (NL == 2)
+            prep_f16_kernel<<<blocks, 256, 0, stream>>>(p);
         else
             prep_kernel<3><<<blocks, 256, 0, stream>>>(p);
         const hipError_t e = hipGetLastError();
@@ -758,11 +875,13 @@ void launch_large(int fmt, int blocks, const SplitArgs& a, int tn, hipStream_t s
 
 // All projections (sharing M) of this call: split every distinct input once into
 // a stream-ordered workspace, run the GEMMs, release the workspace. NL = 3:
-// exact three-limb split; NL = 1: x rounded to bf16.
+// exact three-limb split; NL = 2: two fp16 limbs of the row-scaled x; NL = 1:
+// x rounded to bf16. The direct small-M kernel splits x itself and has no
+// row scale: with NL = 2 it runs the exact three-limb split.
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream) {
-    if (NL != 1 && NL != 3) return hipErrorInvalidValue;
+    if (NL < 1 || NL > 3) return hipErrorInvalidValue;
     const int M = static_cast<int>(M64);
-    if (direct_fits(tasks, count, M)) return launch_direct(tasks, count, M, NL, stream);
+    if (direct_fits(tasks, count, M)) return launch_direct(tasks, count, M, NL == 2 ? 3 : NL, stream);
     const int tm_small = static_cast<int>((int64_t(M) + 15) / 16);
     // The grouped small-M launch addresses the limb images by 32-bit offsets;
     // a call whose images would not fit (enormous K) takes the tiled path.
@@ -856,6 +975,8 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             const int mark = timing_begin(stream);
             if (NL == 1)
                 launch_grouped_tm<1>(tm_small, tiles, g, stream);
+            else if (NL == 2)
+                launch_grouped_tm<2>(tm_small, tiles, g, stream);
             else
                 launch_grouped_tm<3>(tm_small, tiles, g, stream);
             timing_end(mark, stream);
@@ -877,6 +998,8 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             const int mark = timing_begin(stream);
             if (NL == 1)
                 launch_large<1>(t.fmt, tmb * tn, a, tn, stream);
+            else if (NL == 2)
+                launch_large<2>(t.fmt, tmb * tn, a, tn, stream);
             else
                 launch_large<3>(t.fmt, tmb * tn, a, tn, stream);
             timing_end(mark, stream);

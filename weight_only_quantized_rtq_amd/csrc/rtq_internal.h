@@ -36,10 +36,13 @@ int timing_begin(hipStream_t stream);
 void timing_end(int slot, hipStream_t stream);
 
 // Arithmetic of the GEMM kernels (process-wide, see rtq_set_math).
-enum Math : int { kMathSplitBf16 = 0, kMathFp32Mfma = 1, kMathBf16 = 2 };
+enum Math : int { kMathSplitBf16 = 0, kMathFp32Mfma = 1, kMathBf16 = 2, kMathSplitF16 = 3 };
 int math_mode();
-// Limbs of the split path for a math mode: 3 (exact split) or 1 (bf16 x); 0 = fp32 path.
-inline int split_limbs(int mode) { return mode == kMathSplitBf16 ? 3 : mode == kMathBf16 ? 1 : 0; }
+// Limbs of the split path for a math mode: 3 (exact bf16 split), 2 (fp16
+// split of the row-scaled x) or 1 (bf16 x); 0 = fp32 path.
+inline int split_limbs(int mode) {
+    return mode == kMathSplitBf16 ? 3 : mode == kMathSplitF16 ? 2 : mode == kMathBf16 ? 1 : 0;
+}
 
 // Single projection y[M][N] = x[M][K] . dequant(W)^T.
 hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
@@ -49,8 +52,9 @@ hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
 bool grouped_ok(const ProjTask& task);
 
-// bf16 split-limb path (gemm_split.hip): every projection of the call, sharing M,
-// with NL = 3 limbs (exact) or 1 (x rounded to bf16). Tasks must satisfy
+// Split-limb path (gemm_split.hip): every projection of the call, sharing M,
+// with NL = 3 bf16 limbs (exact), 2 fp16 limbs of the row-scaled x, or 1 (x
+// rounded to bf16). Tasks must satisfy
 // split_ok(). Uses a stream-ordered workspace (hipMallocAsync).
 bool split_ok(const ProjTask& task);
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);

@@ -1,7 +1,8 @@
 // Device helpers of the split-limb kernels (gemm_split.hip, gemm_direct.hip):
-// the exact three-limb split of fp32 activations into bf16, weight code to
-// bf16 conversions, the bf16 MFMA, the swizzled 16 x 32 operand layout in LDS
-// and the XCD-aware workgroup order.
+// the exact three-limb split of fp32 activations into bf16 and the two-limb
+// fp16 split, weight code to bf16 / fp16 conversions, the bf16 and fp16
+// MFMAs, the swizzled 16 x 32 operand layout in LDS and the XCD-aware
+// workgroup order.
 #pragma once
 
 #include "rtq_device.h"
@@ -84,6 +85,78 @@ __device__ __forceinline__ u32x4 codes8f_to_bf16(uint32_t w0, uint32_t w1) {
     r[2] = pack_hi(c[0], c[1]);
     r[3] = pack_hi(d[0], d[1]);
     return r;
+}
+
+// fp16 forms for the two-limb fp16 split (NL = 2). A word 0x64XX is the fp16
+// value 1024 + XX (the 10-bit mantissa holds XX exactly), so placing a code
+// byte under 0x64 and subtracting a constant in fp16 gives the code's value
+// exactly: the difference is a small integer, representable without rounding.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ uint32_t f16x2_sub(uint32_t w, _Float16 c) {
+    const f16x2 r = __builtin_bit_cast(f16x2, w) - f16x2{c, c};
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// 8 int4 codes (one payload word, low nibble first) -> 8 fp16 (exact integers).
+__device__ __forceinline__ u32x4 codes4_to_f16(uint32_t w) {
+    const uint32_t lo = w & 0x0f0f0f0fu;                           // codes 0,2,4,6
+    const uint32_t hi = (w >> 4) & 0x0f0f0f0fu;                    // codes 1,3,5,7
+    const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u); // bytes: codes 0,1,2,3
+    const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u); // codes 4,5,6,7
+    constexpr uint32_t k64 = 0x64646464u;
+    u32x4 r;
+    r[0] = f16x2_sub(__builtin_amdgcn_perm(k64, a, 0x04010400u), 1024.0f16);
+    r[1] = f16x2_sub(__builtin_amdgcn_perm(k64, a, 0x04030402u), 1024.0f16);
+    r[2] = f16x2_sub(__builtin_amdgcn_perm(k64, b, 0x04010400u), 1024.0f16);
+    r[3] = f16x2_sub(__builtin_amdgcn_perm(k64, b, 0x04030402u), 1024.0f16);
+    return r;
+}
+
+// 8 int8 codes (two words) -> 8 fp16 (exact integers): the byte b + 128 under
+// 0x64 is 1152 + b, less 1152.
+__device__ __forceinline__ u32x4 codes8_to_f16(uint32_t w0, uint32_t w1) {
+    const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
+    constexpr uint32_t k64 = 0x64646464u;
+    u32x4 r;
+    r[0] = f16x2_sub(__builtin_amdgcn_perm(k64, t0, 0x04010400u), 1152.0f16);
+    r[1] = f16x2_sub(__builtin_amdgcn_perm(k64, t0, 0x04030402u), 1152.0f16);
+    r[2] = f16x2_sub(__builtin_amdgcn_perm(k64, t1, 0x04010400u), 1152.0f16);
+    r[3] = f16x2_sub(__builtin_amdgcn_perm(k64, t1, 0x04030402u), 1152.0f16);
+    return r;
+}
+
+// 8 FP8 E4M3 codes -> 8 fp16, exactly: an E4M3 value has at most 4
+// significant bits and lies inside the fp16 range (subnormals included), so
+// the rounding of the fp32 -> fp16 conversion never acts.
+__device__ __forceinline__ u32x4 codes8f_to_f16(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], a[1]));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], b[1]));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(c[0], c[1]));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(d[0], d[1]));
+    return r;
+}
+
+__device__ __forceinline__ floatx4 mfma_f16(u32x4 a, u32x4 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
+                                                  0, 0, 0);
+}
+
+// Two-limb fp16 split of two fp32 values already scaled into the fp16 range:
+// h = nearest fp16 of v (ties to even), l = nearest fp16 of v - h (the
+// difference is exact in fp32). Packed words, a in the low half.
+__device__ __forceinline__ void split_f16x2(float a, float b, uint32_t& h, uint32_t& l) {
+    const _Float16 ha = static_cast<_Float16>(a), hb = static_cast<_Float16>(b);
+    const _Float16 la = static_cast<_Float16>(a - static_cast<float>(ha));
+    const _Float16 lb = static_cast<_Float16>(b - static_cast<float>(hb));
+    h = __builtin_bit_cast(uint32_t, f16x2{ha, hb});
+    l = __builtin_bit_cast(uint32_t, f16x2{la, lb});
 }
 
 __device__ __forceinline__ floatx4 mfma_bf16(u32x4 a, u32x4 b, floatx4 c) {
