@@ -18,7 +18,8 @@ import weight_only_quantized_rtq_amd as rtq  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda:0"
-MODES = {"split_bf16": rtq.MATH_SPLIT_BF16, "fp32_mfma": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16}
+MODES = {"split_bf16": rtq.MATH_SPLIT_BF16, "fp32_mfma": rtq.MATH_FP32_MFMA, "bf16": rtq.MATH_BF16,
+         "split_f16": rtq.MATH_SPLIT_F16}
 
 
 def say(*a):
