@@ -200,9 +200,11 @@ rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64
  *   2^-25 * 2^-e absolute for elements far below the row's largest). The
  *   fp16 matrix cores (v_mfma_f32_16x16x32_f16) run two limb products per
  *   code instead of three; each output row is scaled back by 2^-e. Calls that
- *   take the small-M direct kernel (M <= 32, every K in 256..2048) run the
- *   exact three-limb split there, which needs no row scale. Meets the same
- *   parity bar as RTQ_MATH_SPLIT_BF16 (relative Frobenius error 1e-5).
+ *   take the small-M direct kernel (M <= 32, every K one of 256, 512, 1024,
+ *   2048, int4 pair arrays 16-byte aligned) run the exact three-limb split
+ *   there, which needs no row scale; shapes the split path does not take run
+ *   on the fp32 kernels, as in the other modes. Meets the same parity bar as
+ *   RTQ_MATH_SPLIT_BF16 (relative Frobenius error 1e-5).
  * Calls already enqueued are not affected. Returns RTQ_ERR_FORMAT for an
  * unknown mode. */
 enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2, RTQ_MATH_SPLIT_F16 = 3 };
