@@ -262,7 +262,7 @@ constexpr int kChunk = 2;         // steps per weight chunk when the weights str
 // (one per row and group) plus 4-byte (scale, min) records, int8 as two
 // 16-byte halves per row and group (TN * 1024 bytes either way). With the
 // weights in LDS the x stages run XL steps ahead (XL + 1 stages).
-template <int BM, int TN = 1, int XL = 0, int WL = 0, int NL = 3>
+template <int BM, int TN = 1, int XL = 0, int WL = 0, int NL = 3, int NW = 4>
 struct Lds {
     static constexpr int NSTAGE = WL > 0 ? XL + 1 : kStages;      // x stages
     static constexpr int NWSLOT = WL + 1;                         // weight-chunk slots per wave
@@ -273,9 +273,9 @@ struct Lds {
     static constexpr int XSLOT = BM <= 96 ? 96 : 128;
     static constexpr int WRING = XRING + kRing * XSLOT * 4;
     static constexpr int WCHUNK = TN * 1024;
-    static constexpr int TOTAL = WRING + (WL > 0 ? NWSLOT * 4 * WCHUNK : 0);
+    static constexpr int TOTAL = WRING + (WL > 0 ? NWSLOT * NW * WCHUNK : 0);
     static constexpr int COPIES = (BM / 16) * NL;                  // 1 KB copies per stage
-    static constexpr int PER_WAVE = (COPIES + 3) / 4;
+    static constexpr int PER_WAVE = (COPIES + NW - 1) / NW;
     static_assert(BM <= XSLOT, "group-sum slot holds every row of the tile");
 };
 
@@ -307,8 +307,9 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
-// One BM x (WN*TN*16) tile (rows m0.., columns n0..) over the whole K. The 4
-// waves are laid out WM x WN; each owns TM x TN 16x16 output tiles.
+// One BM x (WN*TN*16) tile (rows m0.., columns n0..) over the whole K. The
+// workgroup's 4 or 8 waves are laid out WM x WN; each owns TM x TN 16x16 output
+// tiles.
 //
 // K order: the tile walks the groups starting at group `rot` (cyclically), so
 // the column tiles that share a row block (rot = their column-tile index) read
@@ -323,9 +324,10 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
 template <int FMT, int WM, int WN, int TM, int TN, int XL, int WL, int NL>
 __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
-    using L = Lds<BM, TN, XL, WL, NL>;
+    constexpr int NW = WM * WN;                                   // waves of the workgroup
+    using L = Lds<BM, TN, XL, WL, NL, NW>;
     static_assert(NL >= 1 && NL <= 3, "limbs");
-    static_assert(WM * WN == 4, "four waves");
+    static_assert(NW == 4 || NW == 8, "four or eight waves");
     static_assert(WL == 0 || (XL >= 1 && XL <= 2 * WL && WL <= 3), "prefetch leads");
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -435,7 +437,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     }
     auto w_chunk_issue = [&](int c) {
         if constexpr (WL > 0) {
-            unsigned char* slot = wring + (c % L::NWSLOT) * 4 * L::WCHUNK;
+            unsigned char* slot = wring + (c % L::NWSLOT) * NW * L::WCHUNK;
             const int s0 = kChunk * c;
             const int g0 = group_of(s0);                          // s0 < GS
             const int g1 = group_of(min(s0 + 1, GS - 1));
@@ -454,7 +456,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         }
     };
     auto w_read = [&](int i, uint32_t (&wq)[TN][2], uint32_t (&wp)[TN]) {
-        const unsigned char* slot = wring + ((i / kChunk) % L::NWSLOT) * 4 * L::WCHUNK;
+        const unsigned char* slot = wring + ((i / kChunk) % L::NWSLOT) * NW * L::WCHUNK;
         const int h = i % kChunk;
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
@@ -698,6 +700,11 @@ static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within
 // Small M: column tiles of 4 waves x 4 x 16 = 256 and K chunks of at most 16
 // groups (512 of K), so every workgroup does about the same work.
 constexpr int kSmallBN = 256;
+// The 256 columns are spread over kSmallWaves waves side by side, kSmallTN
+// column tiles each: eight waves halve each wave's work per K step, and a K
+// step's time is mostly the latency of one wave's instruction chain.
+constexpr int kSmallWaves = 8;
+constexpr int kSmallTN = kSmallBN / (16 * kSmallWaves);
 constexpr int kMaxGroupedTiles = 1 << 30;   // workgroups of one grouped launch
 // Prefetch leads of the small-M kernel: x stages XL steps ahead, weight chunks
 // (streamed from HBM) WL chunks ahead, per limb count.
@@ -709,9 +716,9 @@ __host__ __device__ inline int split_chunks(int K) {
 }
 
 template <int TM, int NL>
-__global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
+__global__ __launch_bounds__(64 * kSmallWaves) void split_grouped_kernel(SplitGroupArgs g) {
     constexpr int XL = SmallLead<NL>::XL, WL = SmallLead<NL>::WL;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, 4, XL, WL, NL>::TOTAL];
+    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, kSmallTN, XL, WL, NL, kSmallWaves>::TOTAL];
     // Find this workgroup's projection: tiles are numbered projection by
     // projection, (column block, K chunk) within one. Consecutive tiles go to
     // one XCD, so the column tiles that read the same activation image share
@@ -731,11 +738,11 @@ __global__ __launch_bounds__(256) void split_grouped_kernel(SplitGroupArgs g) {
                       nullptr};
     const int rot = cb % (g_hi - g_lo);
     if (g.fmt[i] == kFmtQ4)
-        split_tile<kFmtQ4, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ4, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else if (g.fmt[i] == kFmtQ8)
-        split_tile<kFmtQ8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtQ8, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else
-        split_tile<kFmtF8, 1, 4, TM, 4, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
+        split_tile<kFmtF8, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
 }
 
 // Finishes projections after their GEMM launch: sums the K-chunk partials in
@@ -855,11 +862,11 @@ bool split_ok(const ProjTask& t) {
 template <int NL>
 void launch_grouped_tm(int tm, int tiles, const SplitGroupArgs& g, hipStream_t stream) {
     switch (tm) {
-        case 1: split_grouped_kernel<1, NL><<<tiles, 256, 0, stream>>>(g); break;
-        case 2: split_grouped_kernel<2, NL><<<tiles, 256, 0, stream>>>(g); break;
-        case 3: split_grouped_kernel<3, NL><<<tiles, 256, 0, stream>>>(g); break;
-        case 4: split_grouped_kernel<4, NL><<<tiles, 256, 0, stream>>>(g); break;
-        default: split_grouped_kernel<5, NL><<<tiles, 256, 0, stream>>>(g); break;
+        case 1: split_grouped_kernel<1, NL><<<tiles, 64 * kSmallWaves, 0, stream>>>(g); break;
+        case 2: split_grouped_kernel<2, NL><<<tiles, 64 * kSmallWaves, 0, stream>>>(g); break;
+        case 3: split_grouped_kernel<3, NL><<<tiles, 64 * kSmallWaves, 0, stream>>>(g); break;
+        case 4: split_grouped_kernel<4, NL><<<tiles, 64 * kSmallWaves, 0, stream>>>(g); break;
+        default: split_grouped_kernel<5, NL><<<tiles, 64 * kSmallWaves, 0, stream>>>(g); break;
     }
 }
 
