@@ -19,35 +19,35 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # (workload, math) -> record; filled from the counter runs described in the
 # profiles folder.
 RECORDS: dict = {
-    # split_grouped_kernel<5, 2> (two fp16 limbs), 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33057.254, "write_kib": 34390.409,
+    # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 33 dispatches per counter run
+    ("m80", "split16"): {"fetch_kib": 33142.241, "write_kib": 36111.324,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38441.778, "write_kib": 33915.064,
+    ("m80", "split"): {"fetch_kib": 38750.915, "write_kib": 35585.369,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27766.792, "write_kib": 34568.506,
+    ("m80", "bf16"): {"fetch_kib": 27839.742, "write_kib": 36378.769,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 288 dispatches per counter run
     # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109500.498, "write_kib": 306669.662,
+    ("m65536", "split16"): {"fetch_kib": 109437.714, "write_kib": 307932.335,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
-    ("m65536", "split"): {"fetch_kib": 179451.648, "write_kib": 249557.126,
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+    ("m65536", "split"): {"fetch_kib": 180321.738, "write_kib": 249525.384,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
-    ("m65536", "bf16"): {"fetch_kib": 57598.29, "write_kib": 273858.697,
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+    ("m65536", "bf16"): {"fetch_kib": 57654.972, "write_kib": 273769.15,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "dc89097c55b01bb364fe5572ea935b5c0fd9256efe20abc0721c863530132fc5"},
+         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
 }
 
 
