@@ -268,8 +268,8 @@ struct Lds {
     static constexpr int NWSLOT = WL + 1;                         // weight-chunk slots per wave
     static constexpr int STAGE = (BM / 16) * NL * 1024;
     static constexpr int XRING = NSTAGE * STAGE;
-    // Group-sum slot: waves 0 and 2 copy rows 0..63, waves 1 and 3 rows
-    // XSLOT-64 .. XSLOT-1 (the same rows twice, identical bytes).
+    // Group-sum slot: even waves copy rows 0..63, odd waves rows
+    // XSLOT-64 .. XSLOT-1 (the same rows several times, identical bytes).
     static constexpr int XSLOT = BM <= 96 ? 96 : 128;
     static constexpr int WRING = XRING + kRing * XSLOT * 4;
     static constexpr int WCHUNK = TN * 1024;
@@ -674,9 +674,8 @@ __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_
     split_tile<FMT, kLWM, kLWN, kLTM, kLTN, XL, WL, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
-// Small M (<= 80): one row block of TM*16 rows; 4 waves side by side along N,
-// each with TN column tiles, TN chosen per projection so that TN*K is about
-// constant (long-K projections get narrower tiles and more workgroups).
+// Small M (<= 80): one row block of TM*16 rows and 256 columns per workgroup,
+// every projection of the call in one launch.
 constexpr int kMaxSplitGrouped = 96;
 
 struct SplitGroupArgs {
@@ -697,8 +696,8 @@ struct SplitGroupArgs {
 };
 static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
-// Small M: column tiles of 4 waves x 4 x 16 = 256 and K chunks of at most 16
-// groups (512 of K), so every workgroup does about the same work.
+// Small M: column tiles of 256 and K chunks of at most 16 groups (512 of K),
+// so every workgroup does about the same work.
 constexpr int kSmallBN = 256;
 // The 256 columns are spread over kSmallWaves waves side by side, kSmallTN
 // column tiles each: eight waves halve each wave's work per K step, and a K
