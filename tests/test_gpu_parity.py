@@ -174,10 +174,13 @@ def test_dequant_f8_bit_exact(N, K):
 # ----------------------------------------------------------------------------
 # GEMM parity.
 # ----------------------------------------------------------------------------
+# The grouped small-M workgroup covers 256 columns with eight waves of two
+# 16-column tiles: N = 16 leaves all but one wave without a live column,
+# N = 272 is one workgroup plus a single tile.
 Q4_SHAPES = [(80, 512, 512), (1, 64, 32), (17, 40, 96), (77, 130, 544), (81, 200, 256),
-             (300, 129, 64), (129, 128, 1024), (256, 256, 2048)]
+             (300, 129, 64), (129, 128, 1024), (256, 256, 2048), (40, 16, 512), (48, 272, 1024)]
 Q8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (100, 50, 100), (5, 3, 7),
-             (200, 130, 96), (257, 129, 2048)]
+             (200, 130, 96), (257, 129, 2048), (40, 16, 2048), (64, 272, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", Q4_SHAPES)
@@ -226,7 +229,8 @@ def test_gemm_identity_is_bit_exact(fmt, K, math):
     assert np.array_equal(y[nz].view(np.uint32), want[nz].view(np.uint32))
 
 
-F8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (5, 3, 7), (257, 129, 2048), (300, 129, 64)]
+F8_SHAPES = [(80, 512, 512), (80, 512, 2048), (33, 70, 33), (5, 3, 7), (257, 129, 2048), (300, 129, 64),
+             (40, 16, 512), (80, 272, 1024)]
 
 
 @pytest.mark.parametrize("M,N,K", F8_SHAPES)
