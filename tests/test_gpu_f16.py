@@ -60,7 +60,7 @@ def row_errors(y, want):
 @pytest.mark.parametrize("fmt,M,N,K", [("q4", 48, 96, 512), ("q8", 48, 64, 2048), ("f8", 40, 64, 512),
                                        ("q4", 200, 130, 512), ("q8", 160, 96, 1024)])
 def test_rows_of_any_magnitude_each_meet_the_bar(fmt, M, N, K):
-    """Magnitudes 1e-30 .. 1e30 side by side, zero rows, and rows whose
+    """Magnitudes 1e-37 .. 1e37 side by side, zero rows, and rows whose
     largest element dwarfs the rest: each row takes its own exponent."""
     say(f"magnitudes {fmt} M={M} N={N} K={K}")
     W = synth.weight(41, 0, 0, "wq", N, K, heavy="rows")
@@ -71,6 +71,8 @@ def test_rows_of_any_magnitude_each_meet_the_bar(fmt, M, N, K):
     x[3] = 0.0
     x[5] *= 1e-6
     x[5, 7] = 3.0e4                                 # one element far above the rest of its row
+    x[6] = x[1] / np.abs(x[1]).max() * 1e-37        # near the bottom of the normal fp32 range
+    x[7] = x[2] / np.abs(x[2]).max() * 1e37         # near the top (outputs stay finite)
     x[M - 1] = 0.0
     x = x.astype(np.float32)
     w = rtq.quantize(dev(W), fmt)
@@ -78,7 +80,7 @@ def test_rows_of_any_magnitude_each_meet_the_bar(fmt, M, N, K):
     want = oracle.project(fmt, x, *ref)
     nz = [i for i in range(M) if np.any(want[i] != 0)]
     errs = row_errors(y[nz], want[nz])
-    say(f"  worst row error {max(errs):.3e}")
+    say(f"  worst row error {max(errs):.3e} (row {nz[int(np.argmax(errs))]})")
     assert max(errs) <= TOL, max(errs)
     assert np.all(y[3] == 0) and np.all(y[M - 1] == 0)
 

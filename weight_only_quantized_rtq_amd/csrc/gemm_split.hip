@@ -35,7 +35,7 @@
 // are exact in fp16, products of code and limb exact in fp32, and
 // v_mfma_f32_16x16x32_f16 accumulates two limb products per group and tile
 // instead of three. X_g are the sums of the scaled values; every output is
-// scaled back by 2^-e of its row (exact) before the int8 scale and the bias.
+// scaled back by 2^-e of its row (exact) after the int8 scale, before the bias.
 //
 // Data movement.
 //  1. A pre-pass (prep_kernel) splits every distinct activation once into a
@@ -621,7 +621,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     }
 
     // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile. With two
-    //      fp16 limbs each row is first scaled back by 2^-e[row] (exact). ----
+    //      fp16 limbs each row is scaled back by 2^-e[row] (exact) after the
+    //      int8 scale and before the bias. ----
     int rexp[TM][4];
     if constexpr (NL == 2) {
         const int* exps = reinterpret_cast<const int*>(a.img + image_exp_offset(G, RB, NL));
@@ -644,8 +645,10 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                 const int row = m0 + wm * TM * 16 + tm * 16 + 4 * lc + e;
                 if (row < M) {
                     float v = acc[tm][tn][e];
-                    if constexpr (NL == 2) v = ldexpf(v, rexp[tm][e]);
+                    // the int8 scale first: the code sum of a row scaled far
+                    // down would overflow if scaled back before it
                     if constexpr (FMT == kFmtQ8) v *= sc;
+                    if constexpr (NL == 2) v = ldexpf(v, rexp[tm][e]);
                     if (a.bias) v += bv;
                     a.y[static_cast<int64_t>(row) * N + col] = v;
                 }
