@@ -20,34 +20,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33142.241, "write_kib": 36111.324,
+    ("m80", "split16"): {"fetch_kib": 33147.686, "write_kib": 36132.093,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38750.915, "write_kib": 35585.369,
+    ("m80", "split"): {"fetch_kib": 38736.65, "write_kib": 35586.195,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27839.742, "write_kib": 36378.769,
+    ("m80", "bf16"): {"fetch_kib": 27843.309, "write_kib": 36291.83,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 288 dispatches per counter run
     # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109437.714, "write_kib": 307932.335,
+    ("m65536", "split16"): {"fetch_kib": 109414.739, "write_kib": 307597.207,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
-    ("m65536", "split"): {"fetch_kib": 180321.738, "write_kib": 249525.384,
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+    ("m65536", "split"): {"fetch_kib": 176630.93, "write_kib": 249598.631,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
-    ("m65536", "bf16"): {"fetch_kib": 57654.972, "write_kib": 273769.15,
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+    ("m65536", "bf16"): {"fetch_kib": 57617.651, "write_kib": 273703.261,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "9233e613bc1d9809b9a448ffea65ab338f778a020cadafb3d56f7f37d5f7b104"},
+         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
 }
 
 
