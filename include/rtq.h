@@ -182,6 +182,10 @@ rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64
  *   cores (v_mfma_f32_16x16x32_bf16) accumulate them in fp32. Per 32-group:
  *   y += scale*sum(code*x) + min*sum(x) (int4), y = scale[o]*sum(q*x) (int8).
  *   Same accuracy class as an fp32 GEMM (fp32 accumulation of exact products).
+ *   Range: the code sums sum(code*x) are formed before the scale, so a row
+ *   whose |x| * 127 * K (int8) or |x| * 15 * 32 (int4) exceeds the fp32 range
+ *   overflows even where x . W^T would not (|x| above about 1e33 at K = 2048);
+ *   RTQ_MATH_SPLIT_F16 scales rows first and has no such limit.
  * RTQ_MATH_FP32_MFMA: the weights are dequantized to fp32 while staging and the
  *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction.
  * Both satisfy the same parity bar against the fp64 reference.
