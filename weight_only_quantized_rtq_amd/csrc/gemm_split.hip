@@ -709,8 +709,9 @@ constexpr int kSmallWaves = 8;
 constexpr int kSmallTN = kSmallBN / (16 * kSmallWaves);
 constexpr int kMaxGroupedTiles = 1 << 30;   // workgroups of one grouped launch
 // Prefetch leads of the small-M kernel: x stages XL steps ahead, weight chunks
-// (streamed from HBM) WL chunks ahead, per limb count.
-template <int NL> struct SmallLead { static constexpr int XL = 2, WL = 1; };
+// (streamed from HBM) WL chunks ahead, per limb count. With eight waves per
+// workgroup one step of x lead is enough (two measured 1-3 % slower).
+template <int NL> struct SmallLead { static constexpr int XL = 1, WL = 1; };
 constexpr int kChunkGroups = 16;
 __host__ __device__ inline int split_chunks(int K) {
     const int G = K / 32;

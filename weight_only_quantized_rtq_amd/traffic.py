@@ -20,34 +20,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33147.686, "write_kib": 36132.093,
+    ("m80", "split16"): {"fetch_kib": 33133.43, "write_kib": 36139.523,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38736.65, "write_kib": 35586.195,
+    ("m80", "split"): {"fetch_kib": 39100.777, "write_kib": 35746.831,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27843.309, "write_kib": 36291.83,
+    ("m80", "bf16"): {"fetch_kib": 27850.712, "write_kib": 36677.017,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 288 dispatches per counter run
     # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109414.739, "write_kib": 307597.207,
+    ("m65536", "split16"): {"fetch_kib": 109363.226, "write_kib": 306684.771,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
-    ("m65536", "split"): {"fetch_kib": 176630.93, "write_kib": 249598.631,
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+    ("m65536", "split"): {"fetch_kib": 177234.75, "write_kib": 249509.477,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
-    ("m65536", "bf16"): {"fetch_kib": 57617.651, "write_kib": 273703.261,
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+    ("m65536", "bf16"): {"fetch_kib": 57603.607, "write_kib": 274197.758,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "b239c5feba453bdb37cd6fe1b7dde9f976e53fff2b189f19aa8d1eb9cace2667"},
+         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
 }
 
 
