@@ -5,8 +5,7 @@
  * output y [M, N] (row-major) and weights W [N, K] that stay in their packed,
  * weight-only quantized form in device memory and are dequantized inside the
  * GEMM ("RT-J - int4 (Q4-style, mixed-precision) quantized checkpoints",
- * opening paragraph: the kernels dequantize inside the GEMM, so weight traffic
- * is the packed payload).
+ * opening paragraph): only the packed bytes cross the memory bus.
  *
  * Storage formats (the checkpoints' tensors, one payload plus one companion):
  *
@@ -90,7 +89,7 @@ rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale,
 /* FP8 E4M3 projection: y[M][N] = x[M][K] . W^T with W[o][i] the E4M3 ("fn":
  * bias 7, subnormals, no infinities, S.1111.111 = NaN) value of the byte
  * codes[o][i], row-major [N][K], no scale ("RT-J - FP8 E4M3 checkpoints",
- * section "FP8 Format": matrix weights stored directly as float8_e4m3fn).
+ * section "FP8 Format": 2-D weights kept in the float8_e4m3fn type, no scale).
  * Any K >= 1; codes must be 16-byte aligned. A NaN code makes its outputs NaN. */
 rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y,
                        int64_t M, int64_t N, int64_t K, void* stream);

@@ -19,8 +19,9 @@ What is computed, and where the pages define it:
 * The mixed recipe (int4 model card, same section): int4 for wq/wk/wv/wg and
   ffn.w1/w3, int8 for the residual-writing wo and ffn.w2.
 * FP8 E4M3 weights (FP8 model card "RT-J - FP8 E4M3 checkpoints", section
-  "FP8 Format"): every matrix weight stored directly as PyTorch
-  float8_e4m3fn, no scale; W[o,i] is the E4M3 value of its code.
+  "FP8 Format"): each 2-D weight matrix is kept as PyTorch's
+  float8_e4m3fn type with no companion scale, so W[o,i] is the E4M3 value of
+  its one-byte code.
 * The GEMM itself: y = x . W^T with the weights dequantized first (int4 model
   card, opening paragraph: the kernels dequantize inside the GEMM).
 * The projection bias: the checkpoints keep biases in fp32 next to the
@@ -227,8 +228,8 @@ def quantize_q8(W: np.ndarray):
 
 # ----------------------------------------------------------------------------
 # FP8 E4M3 weights (FP8 model card "RT-J - FP8 E4M3 checkpoints", section
-# "FP8 Format": every matrix weight is stored directly as PyTorch
-# float8_e4m3fn, with no scale). The E4M3 "fn" encoding: 1 sign bit, 4
+# "FP8 Format": 2-D weight matrices are kept in PyTorch's float8_e4m3fn type
+# and carry no scale). The E4M3 "fn" encoding: 1 sign bit, 4
 # exponent bits with bias 7, 3 mantissa bits; exponent 0 holds the subnormals
 # m * 2^-9; there are no infinities, and S.1111.111 is NaN, so the largest
 # finite magnitude is 1.75 * 2^8 = 448.

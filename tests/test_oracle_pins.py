@@ -403,10 +403,64 @@ def pin_project_bias(o):
 PINS_BIAS = [pin_project_bias]
 
 
+def _sqrt_fraction_close(value, square: Fraction, rel=1e-15):
+    """value ~ sqrt(square), checked as value**2 against the exact rational square."""
+    assert value >= 0.0 and math.isfinite(value), value
+    v = Fraction(value)
+    assert abs(v * v - square) <= rel * square, (value, float(square))
+
+
+def pin_rel_fro(o):
+    """The parity metric ||y - y_ref||_F / ||y_ref||_F (the 1e-5 bar of the
+    fp32-activation GEMM is stated as a relative Frobenius error), checked on
+    hand-computed cases whose exact values follow from the definition."""
+    # [[4, 4]] against [[3, 4]]: difference (1, 0), reference norm 5 -> 1/5.
+    # Normalising by ||y|| would give 1/sqrt(32), the max-abs ratio 1/4, the
+    # squared ratio 1/25.
+    assert o.rel_fro(np.array([[4.0, 4.0]]), np.array([[3.0, 4.0]])) == 0.2
+    # the argument order matters: [[3, 4]] against [[4, 4]] is 1/sqrt(32)
+    _sqrt_fraction_close(o.rel_fro(np.array([[3.0, 4.0]]), np.array([[4.0, 4.0]])), Fraction(1, 32))
+    # Frobenius over the whole tensor, not the worst row: rows (3, 4) and
+    # (6, 8), one unit off in the first row -> 1/sqrt(125) (the worst row
+    # alone would give 1/5)
+    _sqrt_fraction_close(o.rel_fro(np.array([[3.0, 5.0], [6.0, 8.0]]), np.array([[3.0, 4.0], [6.0, 8.0]])),
+                         Fraction(1, 125))
+    # not the spectral norm: identity reference, one diagonal entry off by 1
+    # -> 1/sqrt(2) (spectral norms would give 1)
+    _sqrt_fraction_close(o.rel_fro(np.array([[2.0, 0.0], [0.0, 1.0]]), np.eye(2)), Fraction(1, 2))
+    # a 3-D tensor is measured over all of its elements as well
+    ref3 = np.zeros((2, 2, 2))
+    ref3[0, 0, 0] = 3.0
+    ref3[1, 1, 1] = 4.0
+    got3 = ref3.copy()
+    got3[1, 0, 1] = 1.0
+    assert o.rel_fro(got3, ref3) == 0.2
+    # equal tensors -> 0; both zero -> 0; a nonzero result against a zero
+    # reference -> infinity (no finite relative error exists)
+    y = np.arange(12, dtype=np.float32).reshape(3, 4) - 5.5
+    assert o.rel_fro(y, y) == 0.0
+    assert o.rel_fro(np.zeros((2, 3)), np.zeros((2, 3))) == 0.0
+    assert o.rel_fro(np.array([[0.0, 1e-30]]), np.zeros((1, 2))) == float("inf")
+    # fp32 inputs are measured in fp64: a difference of one fp32 ulp at 1.0
+    # among 10^4 equal entries is 2^-23 / 100 relative, not rounded to zero
+    big = np.ones((100, 100), dtype=np.float32)
+    one_off = big.copy()
+    one_off[7, 9] = np.float32(1.0 + 2.0 ** -23)
+    _sqrt_fraction_close(o.rel_fro(one_off, big), Fraction(1, 2 ** 46 * 10 ** 4))
+    # scale invariance by a power of two, and a NaN in the result never passes the bar
+    yr = np.array([[1.5, -2.0, 0.25]])
+    yg = np.array([[1.5, -2.0, 0.5]])
+    assert o.rel_fro(yg * 2.0 ** 60, yr * 2.0 ** 60) == o.rel_fro(yg, yr) == o.rel_fro(yg * 2.0 ** -60, yr * 2.0 ** -60)
+    assert not (o.rel_fro(np.array([[np.nan, 1.0]]), np.array([[1.0, 1.0]])) <= 1e-5)
+
+
+PINS_METRIC = [pin_rel_fro]
+
+
 PINS = [pin_nibble_golden, pin_pack_roundtrip, pin_q4_dequant_golden, pin_q4_dequant_identity_probe,
         pin_q4_dequant_rational, pin_q8_dequant_rational, pin_q8_golden, pin_q8_closed_form,
         pin_q4_recon_bound, pin_q4_grid_roundtrip, pin_q4_clip_argmin, pin_q4_degenerate,
-        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8 + PINS_BF16 + PINS_BIAS
+        pin_gemm_triple_loop, pin_gemm_exact_integer] + PINS_F8 + PINS_BF16 + PINS_BIAS + PINS_METRIC
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -634,6 +688,58 @@ def _mut_quantize_f8_saturate(W):
     return np.where(((out & 0x7F) == 0x7F) & ~np.isnan(w), (out & 0x80) | 0x7E, out).astype(np.uint8)
 
 
+def _mut_rel_fro_by_result(y, y_ref):
+    y, y_ref = np.asarray(y, np.float64), np.asarray(y_ref, np.float64)
+    den = np.linalg.norm(y.ravel())
+    return 0.0 if den == 0.0 else float(np.linalg.norm((y - y_ref).ravel()) / den)
+
+
+def _mut_rel_fro_max_abs(y, y_ref):
+    y, y_ref = np.asarray(y, np.float64), np.asarray(y_ref, np.float64)
+    den = np.abs(y_ref).max()
+    num = np.abs(y - y_ref).max()
+    return (0.0 if num == 0.0 else float("inf")) if den == 0.0 else float(num / den)
+
+
+def _mut_rel_fro_squared(y, y_ref):
+    r = oracle.rel_fro(y, y_ref)
+    return r * r
+
+
+def _mut_rel_fro_zero(y, y_ref):
+    return 0.0
+
+
+def _mut_rel_fro_swapped(y, y_ref):
+    return oracle.rel_fro(y_ref, y)
+
+
+def _mut_rel_fro_worst_row(y, y_ref):
+    y, y_ref = np.atleast_2d(np.asarray(y, np.float64)), np.atleast_2d(np.asarray(y_ref, np.float64))
+    return max(oracle.rel_fro(a, b) for a, b in zip(y, y_ref))
+
+
+def _mut_rel_fro_spectral(y, y_ref):
+    y, y_ref = np.asarray(y, np.float64), np.asarray(y_ref, np.float64)
+    if y.ndim != 2:
+        return oracle.rel_fro(y, y_ref)
+    den = np.linalg.norm(y_ref, 2)
+    num = np.linalg.norm(y - y_ref, 2)
+    return (0.0 if num == 0.0 else float("inf")) if den == 0.0 else float(num / den)
+
+
+def _mut_rel_fro_fp32(y, y_ref):
+    y, y_ref = np.asarray(y, np.float32), np.asarray(y_ref, np.float32)
+    den = np.linalg.norm(y_ref)
+    num = np.linalg.norm(y - y_ref)
+    return (0.0 if num == 0.0 else float("inf")) if den == 0.0 else float(np.float32(num) / np.float32(den))
+
+
+def _mut_rel_fro_zero_ref_passes(y, y_ref):
+    y_ref = np.asarray(y_ref, np.float64)
+    return 0.0 if np.linalg.norm(y_ref) == 0.0 else oracle.rel_fro(y, y_ref)
+
+
 MUTANTS = {
     "project_bias_rows": {"project_bias": _mut_project_bias_rows},
     "project_bias_dropped": {"project_bias": _mut_project_bias_dropped},
@@ -659,6 +765,15 @@ MUTANTS = {
     "gemm_drop_last_k": {"gemm_ref": _mut_gemm_drop_last_k},
     "gemm_low_precision": {"gemm_ref": _mut_gemm_fp32},
     "project_q4_transposed": {"project_q4": _mut_project_q4_transposed},
+    "rel_fro_by_result": {"rel_fro": _mut_rel_fro_by_result},
+    "rel_fro_max_abs": {"rel_fro": _mut_rel_fro_max_abs},
+    "rel_fro_squared": {"rel_fro": _mut_rel_fro_squared},
+    "rel_fro_zero": {"rel_fro": _mut_rel_fro_zero},
+    "rel_fro_swapped": {"rel_fro": _mut_rel_fro_swapped},
+    "rel_fro_worst_row": {"rel_fro": _mut_rel_fro_worst_row},
+    "rel_fro_spectral": {"rel_fro": _mut_rel_fro_spectral},
+    "rel_fro_fp32": {"rel_fro": _mut_rel_fro_fp32},
+    "rel_fro_zero_ref_passes": {"rel_fro": _mut_rel_fro_zero_ref_passes},
 }
 
 
