@@ -142,19 +142,19 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, reci
     return sets
 
 
-def time_workload(torch, rtq, sets, M, steps, warmup):
+def time_workload(torch, rtq, sets, M, steps, warmup, math):
     """Times exactly `steps` steps (wall clock between synchronizations) and,
     through the library's event timing, the main GEMM kernel launches inside
     them (HIP events recorded on the launch stream)."""
     for i in range(warmup):
         blocks, packed = sets[i % len(sets)]
-        rtq.block_project(blocks, M, packed=packed)
+        rtq.block_project(blocks, M, packed=packed, math=math)
     torch.cuda.synchronize()
     rtq.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
         blocks, packed = sets[i % len(sets)]
-        rtq.block_project(blocks, M, packed=packed)
+        rtq.block_project(blocks, M, packed=packed, math=math)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kernel_ms, launches = rtq.timing_read()
@@ -162,7 +162,7 @@ def time_workload(torch, rtq, sets, M, steps, warmup):
     return wall, kernel_ms, launches
 
 
-def measure(torch, rtq, synth, workload, steps, warmup, recipe="mixed"):
+def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
     nb = synth.NUM_BLOCKS
     if workload == "m80":
         M = synth.M_GOLDEN
@@ -171,7 +171,7 @@ def measure(torch, rtq, synth, workload, steps, warmup, recipe="mixed"):
         M = synth.M_LARGE
         sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False, recipe=recipe)
     wb, fl = block_bytes_flops(M, recipe)
-    wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup)
+    wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup, math)
     del sets
     torch.cuda.empty_cache()
     flops_step, bytes_step = fl * nb, wb * nb
@@ -188,7 +188,7 @@ def measure(torch, rtq, synth, workload, steps, warmup, recipe="mixed"):
     }
 
 
-def m_sweep(torch, rtq, synth, Ms, steps=200, warmup=20, recipe="mixed"):
+def m_sweep(torch, rtq, synth, Ms, math, steps=200, warmup=20, recipe="mixed"):
     """Diagnostic: the m80 weight sets (12 blocks x 16 sets) at other M, to show
     where the weight stream stops being the only cost. Same timing as the main
     workload; the weights are quantized once and shared across M."""
@@ -207,7 +207,7 @@ def m_sweep(torch, rtq, synth, Ms, steps=200, warmup=20, recipe="mixed"):
             blocks = [{name: rtq.Projection(weights[s][b][name], xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name])
                        for name in synth.PROJ_ORDER} for b in range(nb)]
             sets.append((blocks, rtq.pack_blocks(blocks, M)))
-        wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup)
+        wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup, math)
         _, fl = block_bytes_flops(M, recipe)
         ms = wall / steps * 1e3
         per_launch = kernel_ms / launches
@@ -328,44 +328,39 @@ def main():
     BIAS = args.bias
     rtq.load_library()
     torch.cuda.init()
-    modes = {"split16": rtq.MATH_SPLIT_F16, "split": rtq.MATH_SPLIT_BF16, "fp32": rtq.MATH_FP32_MFMA,
-             "bf16": rtq.MATH_BF16}
-    rtq.set_math(modes[args.math])
+    modes = rtq.MATHS
+    main_math = modes[args.math]
     fp32_modes = ("split16", "split")
     out = {}
     if args.workload in ("m80", "both"):
-        out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup, args.recipe)
+        out["m80"] = measure(torch, rtq, synth, "m80", args.steps, args.warmup, main_math, args.recipe)
     if args.workload in ("m65536", "both"):
-        out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large, args.recipe)
+        out["m65536"] = measure(torch, rtq, synth, "m65536", args.steps_large, args.warmup_large, main_math,
+                                args.recipe)
     fp32 = {}
     if args.compare_fp32 and args.math in fp32_modes:
-        rtq.set_math(rtq.MATH_FP32_MFMA)
         for wl in out:
-            r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1, args.recipe)
+            r = measure(torch, rtq, synth, wl, 300 if wl == "m80" else 3, 10 if wl == "m80" else 1,
+                        rtq.MATH_FP32_MFMA, args.recipe)
             fp32[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                         "roofline": roofline(r, "fp32", wl, args.recipe)}
-        rtq.set_math(modes[args.math])
     exact = {}
     if not args.no_exact_path and args.math == "split16":
-        rtq.set_math(rtq.MATH_SPLIT_BF16)
         for wl in out:
             st, wu = (args.steps, args.warmup) if wl == "m80" else (args.steps_large, args.warmup_large)
-            r = measure(torch, rtq, synth, wl, st, wu, args.recipe)
+            r = measure(torch, rtq, synth, wl, st, wu, rtq.MATH_SPLIT_BF16, args.recipe)
             exact[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                          "weight_gbs": round(r["weight_gbs"], 2), "steps": r["steps"],
                          "roofline": roofline(r, "split", wl, args.recipe)}
-        rtq.set_math(modes[args.math])
     bf16 = {}
     if not args.no_bf16_path and args.math in fp32_modes:
-        rtq.set_math(rtq.MATH_BF16)
         for wl in out:
             st, wu = (args.steps, args.warmup) if wl == "m80" else (args.steps_large, args.warmup_large)
-            r = measure(torch, rtq, synth, wl, st, wu, args.recipe)
+            r = measure(torch, rtq, synth, wl, st, wu, rtq.MATH_BF16, args.recipe)
             bf16[wl] = {"ms_per_step": round(r["ms_per_step"], 5), "tflops": round(r["tflops"], 3),
                         "weight_gbs": round(r["weight_gbs"], 2),
                         "weight_hbm_frac": round(r["weight_gbs"] / PEAK_HBM_GBS, 5), "steps": r["steps"],
                         "roofline": roofline(r, "bf16", wl, args.recipe)}
-        rtq.set_math(modes[args.math])
 
     prim_name = "m80" if "m80" in out else "m65536"
     prim = out[prim_name]
@@ -432,7 +427,8 @@ def main():
         line["m_sweep"] = {
             "note": f"diagnostic: the m80 weight sets at other M ({args.math} arithmetic); per-step and "
                     "in-kernel weight GB/s against the 8000 GB/s HBM peak",
-            "points": m_sweep(torch, rtq, synth, [int(v) for v in args.m_sweep.split(",")], recipe=args.recipe)}
+            "points": m_sweep(torch, rtq, synth, [int(v) for v in args.m_sweep.split(",")], main_math,
+                              recipe=args.recipe)}
         if "hbm_attainable" in line:
             for pt in line["m_sweep"]["points"]:
                 pt["weight_frac_of_attainable_in_kernel"] = round(

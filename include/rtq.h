@@ -173,46 +173,57 @@ rtq_status rtq_quantize_q8_host(const float* w, int8_t* q, float* scale,
                                 int64_t N, int64_t K, int32_t threads);
 rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int32_t threads);
 
-/* Arithmetic of the GEMM entry points, process-wide (default RTQ_MATH_SPLIT_BF16).
+/* Arithmetic of a GEMM call, chosen per call (the `math` argument of
+ * rtq_gemm_ex and rtq_block_project_ex; rtq_gemm_q4 / _q8 / _f8 and
+ * rtq_block_project run RTQ_MATH_SPLIT_BF16). No arithmetic state is kept
+ * between calls. Every mode first scales each row of x by the power of two
+ * 2^e that puts its largest magnitude in [2^14, 2^15) (exact, as is the
+ * scaling back of each output row by 2^-e), so a row's magnitude does not
+ * limit the range: codes times scaled activations stay far inside fp32.
  *
- * RTQ_MATH_SPLIT_BF16: each fp32 activation is split exactly into three bf16
- *   limbs (x = x1 + x2 + x3, no rounding); the int4/int8 codes and the E4M3
- *   values are exact in bf16, so every code*limb product is exact in fp32 and the bf16 matrix
- *   cores (v_mfma_f32_16x16x32_bf16) accumulate them in fp32. Per 32-group:
- *   y += scale*sum(code*x) + min*sum(x) (int4), y = scale[o]*sum(q*x) (int8).
- *   Same accuracy class as an fp32 GEMM (fp32 accumulation of exact products).
- *   Range: the code sums sum(code*x) are formed before the scale, so a row
- *   whose |x| * 127 * K (int8) or |x| * 15 * 32 (int4) exceeds the fp32 range
- *   overflows even where x . W^T would not (|x| above about 1e33 at K = 2048);
- *   RTQ_MATH_SPLIT_F16 scales rows first and has no such limit.
+ * RTQ_MATH_SPLIT_BF16: each scaled activation is split exactly into three
+ *   bf16 limbs (v = v1 + v2 + v3, no rounding); the int4/int8 codes and the
+ *   E4M3 values are exact in bf16, so every code*limb product is exact in fp32
+ *   and the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) accumulate them in
+ *   fp32. Per 32-group: y += scale*sum(code*x) + min*sum(x) (int4),
+ *   y = scale[o]*sum(q*x) (int8). Same accuracy class as an fp32 GEMM (fp32
+ *   accumulation of exact products). The row scale is exact for every element
+ *   whose scaled value stays a normal fp32 number (above 2^-126, i.e. more
+ *   than 2^-140 of the row's largest magnitude); smaller ones lose low bits,
+ *   far below the fp32 accumulation error.
  * RTQ_MATH_FP32_MFMA: the weights are dequantized to fp32 while staging and the
- *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction.
+ *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction on the
+ *   unscaled x.
  * Both satisfy the same parity bar against the fp64 reference.
- * RTQ_MATH_BF16: bf16 activations. Each x is rounded once to the nearest bf16
- *   (ties to even) and takes the place of the three limbs: y = bf16(x) . W^T
- *   with the exact weight side and fp32 accumulation of the first mode, a third
- *   of its matrix work. The result carries the rounding of x (about 2^-9
- *   relative per element), so it is a lower-precision mode. Shapes the split
- *   path does not take (int8/FP8 K not a multiple of 32, x or payload not
- *   16-byte aligned, N*K >= 2^32) run on the fp32 kernels in every mode.
- * RTQ_MATH_SPLIT_F16: fp32 activations in two fp16 limbs. Each row of x is
- *   scaled by the power of two 2^e that puts its largest magnitude in
- *   [2^14, 2^15) (exact), and every scaled value v is split into
- *   h = fp16(v) and l = fp16(v - h), both rounded to nearest: h + l carries 22
- *   significant bits of v (relative error at most 2^-22 per element, plus
- *   2^-25 * 2^-e absolute for elements far below the row's largest). The
- *   fp16 matrix cores (v_mfma_f32_16x16x32_f16) run two limb products per
- *   code instead of three; each output row is scaled back by 2^-e. Calls that
- *   take the small-M direct kernel (M <= 32, every K one of 256, 512, 1024,
- *   2048, int4 pair arrays 16-byte aligned) run the exact three-limb split
- *   there, which needs no row scale; shapes the split path does not take run
- *   on the fp32 kernels, as in the other modes. Meets the same parity bar as
- *   RTQ_MATH_SPLIT_BF16 (relative Frobenius error 1e-5).
- * Calls already enqueued are not affected. Returns RTQ_ERR_FORMAT for an
- * unknown mode. */
+ * RTQ_MATH_BF16: bf16 activations. Each scaled x is rounded once to the
+ *   nearest bf16 (ties to even) and takes the place of the three limbs:
+ *   y = bf16(x) . W^T with the exact weight side and fp32 accumulation of the
+ *   first mode, a third of its matrix work (the power-of-two scale does not
+ *   change the rounding of a normal-range x). The result carries the rounding
+ *   of x (about 2^-9 relative per element), so it is a lower-precision mode.
+ * RTQ_MATH_SPLIT_F16: fp32 activations in two fp16 limbs: every scaled value v
+ *   is split into h = fp16(v) and l = fp16(v - h), both rounded to nearest:
+ *   h + l carries 22 significant bits of v (relative error at most 2^-22 per
+ *   element, plus 2^-25 * 2^-e absolute for elements far below the row's
+ *   largest). The fp16 matrix cores (v_mfma_f32_16x16x32_f16) run two limb
+ *   products per code instead of three. Meets the same parity bar as
+ *   RTQ_MATH_SPLIT_BF16 (relative Frobenius error 1e-5). Calls that take the
+ *   small-M direct kernel (M <= 32, every K one of 256, 512, 1024, 2048, int4
+ *   pair arrays 16-byte aligned) run the exact three-limb split there.
+ * Shapes the split path does not take (int8/FP8 K not a multiple of 32, x or
+ * payload not 16-byte aligned, N*K >= 2^32) run on the fp32 kernels in every
+ * mode. An unknown mode returns RTQ_ERR_FORMAT. */
 enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2, RTQ_MATH_SPLIT_F16 = 3 };
-rtq_status rtq_set_math(int32_t mode);
-int32_t rtq_get_math(void);
+
+/* rtq_gemm_q4 / _q8 / _f8 with the format as an argument (fmt = RTQ_FMT_Q4,
+ * RTQ_FMT_Q8 or RTQ_FMT_F8; `scale` is the int4 pairs, the int8 row scales,
+ * ignored for FP8) and the arithmetic chosen by `math`. */
+rtq_status rtq_gemm_ex(int32_t fmt, const float* x, const void* payload, const void* scale, float* y,
+                       int64_t M, int64_t N, int64_t K, int32_t math, void* stream);
+
+/* rtq_block_project with the arithmetic chosen by `math`. */
+rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
+                                void* stream);
 
 /* Kernel timing (profiling aid). While enabled, every main GEMM kernel launch
  * of the entry points above is bracketed by a pair of HIP events recorded on

@@ -180,17 +180,24 @@ def test_f8_validation(lib):
     assert lib.rtq_block_project((rtq._Block * 1)(blk), 1, 0, None) == OK
 
 
-def test_math_mode_switch(lib):
-    assert lib.rtq_get_math() == rtq.MATH_SPLIT_BF16
-    assert lib.rtq_set_math(7) == ERR_FORMAT
-    assert lib.rtq_set_math(rtq.MATH_FP32_MFMA) == OK
-    assert lib.rtq_get_math() == rtq.MATH_FP32_MFMA
-    assert lib.rtq_set_math(rtq.MATH_SPLIT_F16) == OK
-    assert lib.rtq_get_math() == rtq.MATH_SPLIT_F16
-    assert lib.rtq_set_math(rtq.MATH_BF16) == OK
-    assert lib.rtq_get_math() == rtq.MATH_BF16
-    assert lib.rtq_set_math(-1) == ERR_FORMAT and lib.rtq_get_math() == rtq.MATH_BF16
-    assert lib.rtq_set_math(rtq.MATH_SPLIT_BF16) == OK
+def test_math_is_an_argument_checked_per_call(lib):
+    """The arithmetic is a per-call argument: an unknown value is rejected
+    before anything runs, and no call changes what a later call computes
+    (there is no arithmetic state to set)."""
+    for name in ("rtq_set_math", "rtq_get_math"):
+        with pytest.raises(AttributeError):
+            getattr(lib, name)
+    for bad in (-1, 4, 7):
+        assert lib.rtq_gemm_ex(rtq.FMT_Q4, A, B, C, D, 80, 512, 512, bad, None) == ERR_FORMAT
+        assert b"arithmetic" in lib.rtq_last_error()
+        blk = _block()
+        assert lib.rtq_block_project_ex((rtq._Block * 1)(blk), 1, 80, bad, None) == ERR_FORMAT
+    assert lib.rtq_gemm_ex(9, A, B, C, D, 80, 512, 512, rtq.MATH_SPLIT_BF16, None) == ERR_FORMAT
+    for m in rtq.MATHS.values():
+        # M = 0 is a no-op in every arithmetic; shape errors are reported as before
+        assert lib.rtq_gemm_ex(rtq.FMT_Q8, None, B, C, None, 0, 512, 512, m, None) == OK
+        assert lib.rtq_gemm_ex(rtq.FMT_Q4, A, B, C, D, 80, 512, 500, m, None) == ERR_SHAPE
+        assert lib.rtq_block_project_ex((rtq._Block * 1)(_block(fmt=rtq.FMT_F8, s=None)), 1, 0, m, None) == OK
 
 
 def test_struct_layout_matches_header(tmp_path):

@@ -1,4 +1,4 @@
-"""GPU parity of the bf16-activation mode (rtq_set_math(RTQ_MATH_BF16)).
+"""GPU parity of the bf16-activation mode (RTQ_MATH_BF16, passed to every call).
 
 In this mode x is rounded once to the nearest bf16 and the kernels compute
 y = bf16(x) . W^T with exact weight-side products and fp32 accumulation. Two
@@ -22,6 +22,7 @@ import synth  # noqa: E402
 import weight_only_quantized_rtq_amd as rtq  # noqa: E402
 
 pytestmark = pytest.mark.gpu
+MATH = rtq.MATH_BF16          # the arithmetic every call below passes
 
 TIGHT = 1e-5
 BAR = 3e-3
@@ -41,12 +42,6 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-@pytest.fixture(autouse=True)
-def bf16_mode():
-    rtq.set_math(rtq.MATH_BF16)
-    assert rtq.get_math() == rtq.MATH_BF16
-    yield
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
 
 
 def check(y, fmt, x, ref):
@@ -73,7 +68,7 @@ def test_gemm_bf16_parity(fmt, M, N, K):
     x = synth.activation(31, 0, "x_ffn", M, K)
     ref = oracle.quantize(W, fmt)
     w = rtq.quantize(dev(W), fmt)
-    y = host(rtq.gemm(dev(x), w))
+    y = host(rtq.gemm(dev(x), w, math=MATH))
     tight, loose = check(y, fmt, x, ref)
     say(f"  rel err vs bf16(x) {tight:.2e}, vs fp32 x {loose:.2e}")
 
@@ -85,7 +80,7 @@ def test_bf16_mode_rounds_the_activations():
     x = synth.activation(32, 0, "x_attn", M, K)
     x_off = (x.view(np.uint32) | np.uint32(0x5555)).view(np.float32)      # low bits set everywhere
     ref = oracle.quantize(W, "q4")
-    y = host(rtq.gemm(dev(x_off), rtq.quantize(dev(W), "q4")))
+    y = host(rtq.gemm(dev(x_off), rtq.quantize(dev(W), "q4"), math=MATH))
     assert oracle.rel_fro(y, oracle.project_bf16("q4", x_off, *ref)) <= TIGHT
     assert oracle.rel_fro(y, oracle.project("q4", x_off, *ref)) > 1e-4
 
@@ -96,7 +91,7 @@ def test_bf16_identity_is_bit_exact(fmt, K):
     N = 72
     W = synth.weight(33, 0, 0, "wv", N, K, heavy="rows")
     ref = oracle.quantize(W, fmt)
-    y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), rtq.quantize(dev(W), fmt)))
+    y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), rtq.quantize(dev(W), fmt), math=MATH))
     want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T)
     assert np.array_equal(y, want)
     nz = want != 0
@@ -111,7 +106,7 @@ def test_bf16_exact_integer_arithmetic():
     pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
     pairs[..., 0] = 0.25
     pairs[..., 1] = -2.0
-    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs))))
+    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs)), math=MATH))
     assert np.array_equal(y.astype(np.float64), oracle.project_q4(x, payload, pairs))
 
 
@@ -121,7 +116,7 @@ def test_bf16_mode_fallback_shapes_stay_fp32(fmt, M, N, K):
     W = synth.weight(34, 0, 0, "wo", N, K)
     x = synth.activation(34, 0, "h", M, K)
     ref = oracle.quantize(W, fmt)
-    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt)))
+    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt), math=MATH))
     assert oracle.rel_fro(y, oracle.project(fmt, x, *ref)) <= TIGHT
 
 
@@ -139,7 +134,7 @@ def test_bf16_block_project_one_block(recipe_name):
         refs[name] = (fmt, oracle.quantize(W, fmt), xin)
         blk[name] = rtq.Projection(rtq.quantize(dev(W), fmt), dxs[xin],
                                    torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV))
-    rtq.block_project([blk], M)
+    rtq.block_project([blk], M, math=MATH)
     for name, (fmt, ref, xin) in refs.items():
         check(host(blk[name].y), fmt, xs[xin], ref)
 
@@ -166,7 +161,7 @@ def test_bf16_full_size_twelve_blocks_sampled(M):
             rw[name] = (fmt, W)
         blocks.append(blk)
         refs_w.append(rw)
-    rtq.block_project(blocks, M)
+    rtq.block_project(blocks, M, math=MATH)
     torch.cuda.synchronize()
     rng = np.random.default_rng(M + 1)
     worst = [0.0, 0.0]

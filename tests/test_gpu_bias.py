@@ -37,9 +37,8 @@ def host(t: torch.Tensor) -> np.ndarray:
 
 @pytest.fixture(params=list(MODES), ids=list(MODES))
 def mode(request):
-    rtq.set_math(MODES[request.param])
-    yield request.param
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
+    """Arithmetic of the calls (its name; MODES gives the value passed to each call)."""
+    return request.param
 
 
 def bias_of(seed, N):
@@ -80,7 +79,7 @@ def test_block_project_with_biases(M, mode):
             ref[name] = (fmt, oracle.quantize(W, fmt), xs[xin], bias)
         blocks.append(blk)
         refs.append(ref)
-    rtq.block_project(blocks, M)
+    rtq.block_project(blocks, M, math=MODES[mode])
     for b in range(2):
         for name, (fmt, r, x, bias) in refs[b].items():
             y = host(blocks[b][name].y)
@@ -95,7 +94,7 @@ def test_gemm_with_bias(fmt, M, N, K, mode):
     x = synth.activation(43, 0, "x_ffn", M, K)
     b = bias_of(44, N)
     ref = oracle.quantize(W, fmt)
-    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt), bias=dev(b)))
+    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt), bias=dev(b), math=MODES[mode]))
     check(y, mode, fmt, x, ref, b)
 
 
@@ -110,5 +109,5 @@ def test_zero_weights_give_the_bias_exactly(M, mode):
                rtq.Q8Weight(dev(np.zeros((N, K), np.int8)), dev(np.zeros(N, np.float32))),
                rtq.F8Weight(dev(np.zeros((N, K), np.uint8)))]
     for w in weights:
-        y = host(rtq.gemm(dev(x), w, bias=dev(b)))
+        y = host(rtq.gemm(dev(x), w, bias=dev(b), math=MODES[mode]))
         assert np.array_equal(y.view(np.uint32), np.broadcast_to(b, (M, N)).view(np.uint32)), type(w).__name__

@@ -38,9 +38,8 @@ def host(t):
 
 @pytest.fixture(params=list(MODES), ids=list(MODES))
 def mode(request):
-    rtq.set_math(MODES[request.param])
-    yield request.param
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
+    """Arithmetic of the calls (its name; MODES gives the value passed to each call)."""
+    return request.param
 
 
 def check(y, mode, fmt, x, ref, b=None):
@@ -68,7 +67,7 @@ def test_direct_gemm_parity(fmt, M, N, K, mode):
     W = synth.weight(61, 0, 0, "w1", N, K, heavy="rows")
     x = synth.activation(61, 0, "x_ffn", M, K)
     ref = oracle.quantize(W, fmt)
-    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt)))
+    y = host(rtq.gemm(dev(x), rtq.quantize(dev(W), fmt), math=MODES[mode]))
     check(y, mode, fmt, x, ref)
 
 
@@ -93,7 +92,7 @@ def test_direct_block_project_twelve_blocks_with_biases(M, mode):
             ref[name] = (fmt, oracle.quantize(W, fmt), xs[xin], bias)
         blocks.append(blk)
         refs.append(ref)
-    rtq.block_project(blocks, M)
+    rtq.block_project(blocks, M, math=MODES[mode])
     for b in range(synth.NUM_BLOCKS):
         for name, (fmt, r, x, bias) in refs[b].items():
             check(host(blocks[b][name].y), mode, fmt, x, r, bias)
@@ -208,11 +207,11 @@ def test_direct_guard_bands_and_determinism(fmt, K, M, mode):
     guard = 4096
     buf = torch.full((guard + M * N + guard,), 1234.5, dtype=torch.float32, device=DEV)
     y = buf[guard:guard + M * N].view(M, N)
-    rtq.gemm(x, w, y=y)
+    rtq.gemm(x, w, y=y, math=MODES[mode])
     y1 = host(y).copy()
     b = host(buf)
     assert np.all(b[:guard] == 1234.5) and np.all(b[guard + M * N:] == 1234.5)
-    rtq.gemm(x, w, y=y)
+    rtq.gemm(x, w, y=y, math=MODES[mode])
     assert np.array_equal(host(y).view(np.uint32), y1.view(np.uint32))
 
 
@@ -230,5 +229,5 @@ def test_direct_int4_pairs_not_16_byte_aligned(M, mode):
     pairs = buf[2:].view(N, K // 32, 2)                           # 4 bytes past a 16-byte boundary
     pairs.copy_(dev(ref[1]))
     assert pairs.data_ptr() % 16 == 4
-    y = host(rtq.gemm(dev(x), rtq.Q4Weight(payload, pairs)))
+    y = host(rtq.gemm(dev(x), rtq.Q4Weight(payload, pairs), math=MODES[mode]))
     check(y, mode, "q4", x, ref)

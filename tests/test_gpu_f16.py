@@ -1,4 +1,4 @@
-"""GPU parity of the two-limb fp16 mode (rtq_set_math(RTQ_MATH_SPLIT_F16)).
+"""GPU parity of the two-limb fp16 mode (RTQ_MATH_SPLIT_F16, passed to every call).
 
 Each activation row is scaled by the power of two that puts its largest
 magnitude in [2^14, 2^15) and split into two fp16 limbs, h = fp16(v) and
@@ -26,6 +26,7 @@ import synth  # noqa: E402
 import weight_only_quantized_rtq_amd as rtq  # noqa: E402
 
 pytestmark = pytest.mark.gpu
+MATH = rtq.MATH_SPLIT_F16          # the arithmetic every call below passes
 
 TOL = 1e-5
 TIGHT = 2e-6
@@ -45,12 +46,6 @@ def host(t: torch.Tensor) -> np.ndarray:
     return t.cpu().numpy()
 
 
-@pytest.fixture(autouse=True)
-def f16_mode():
-    rtq.set_math(rtq.MATH_SPLIT_F16)
-    assert rtq.get_math() == rtq.MATH_SPLIT_F16
-    yield
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
 
 
 def row_errors(y, want):
@@ -76,7 +71,7 @@ def test_rows_of_any_magnitude_each_meet_the_bar(fmt, M, N, K):
     x[M - 1] = 0.0
     x = x.astype(np.float32)
     w = rtq.quantize(dev(W), fmt)
-    y = host(rtq.gemm(dev(x), w))
+    y = host(rtq.gemm(dev(x), w, math=MATH))
     want = oracle.project(fmt, x, *ref)
     nz = [i for i in range(M) if np.any(want[i] != 0)]
     errs = row_errors(y[nz], want[nz])
@@ -95,7 +90,7 @@ def test_long_and_short_rows(fmt, M, N, K):
     ref = oracle.quantize(W, fmt)
     x = synth.activation(42, 0, "x_ffn", M, K)
     w = rtq.quantize(dev(W), fmt)
-    y = host(rtq.gemm(dev(x), w))
+    y = host(rtq.gemm(dev(x), w, math=MATH))
     err = oracle.rel_fro(y, oracle.project(fmt, x, *ref))
     assert err <= TOL, err
 
@@ -109,7 +104,7 @@ def test_nonfinite_row_stays_in_its_row(M):
     x[2, 100] = np.inf
     x[4, 9] = np.nan
     w = rtq.quantize(dev(W), "q4")
-    y = host(rtq.gemm(dev(x), w))
+    y = host(rtq.gemm(dev(x), w, math=MATH))
     assert not np.any(np.isfinite(y[2])) and np.all(np.isnan(y[4]))
     keep = [i for i in range(M) if i not in (2, 4)]
     err = oracle.rel_fro(y[keep], oracle.project("q4", x[keep], *ref))
@@ -125,9 +120,8 @@ def test_small_m_runs_the_exact_direct_split(fmt):
     W = synth.weight(44, 0, 0, "wv", N, K)
     x = dev(synth.activation(44, 0, "x_attn", M, K))
     w = rtq.quantize(dev(W), fmt)
-    y16 = host(rtq.gemm(x, w)).copy()
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
-    y3 = host(rtq.gemm(x, w))
+    y16 = host(rtq.gemm(x, w, math=MATH)).copy()
+    y3 = host(rtq.gemm(x, w, math=rtq.MATH_SPLIT_BF16))
     assert np.array_equal(y16.view(np.uint32), y3.view(np.uint32))
 
 
@@ -140,11 +134,10 @@ def test_random_data_error_is_near_fp32_accumulation(fmt, M, N, K):
     x = synth.activation(45, 0, "x_ffn", M, K)
     w = rtq.quantize(dev(W), fmt)
     xd = dev(x)
-    y16 = host(rtq.gemm(xd, w)).copy()
+    y16 = host(rtq.gemm(xd, w, math=MATH)).copy()
     want = oracle.project(fmt, x, *ref)
     e16 = oracle.rel_fro(y16, want)
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
-    e3 = oracle.rel_fro(host(rtq.gemm(xd, w)), want)
+    e3 = oracle.rel_fro(host(rtq.gemm(xd, w, math=rtq.MATH_SPLIT_BF16)), want)
     say(f"  split_f16 {e16:.3e}  split_bf16 {e3:.3e}")
     assert e16 <= TIGHT, e16
 
@@ -169,7 +162,7 @@ def test_block_project_twelve_blocks_m80():
                                        y=torch.empty(M, N, dtype=torch.float32, device=DEV))
             refs.append((b, name, fmt, x, oracle.quantize(W, fmt)))
         projs.append(blk)
-    rtq.block_project(projs, M)
+    rtq.block_project(projs, M, math=MATH)
     for b, name, fmt, x, packed in refs:
         err = oracle.rel_fro(host(projs[b][name].y), oracle.project(fmt, x, *packed))
         assert err <= TOL, (b, name, err)

@@ -38,10 +38,9 @@ def host(t: torch.Tensor) -> np.ndarray:
 @pytest.fixture(params=[rtq.MATH_SPLIT_BF16, rtq.MATH_FP32_MFMA, rtq.MATH_SPLIT_F16],
                 ids=["split_bf16", "fp32_mfma", "split_f16"])
 def math(request):
-    """Runs a test under each fp32-activation arithmetic of the GEMM entry points."""
-    rtq.set_math(request.param)
-    yield request.param
-    rtq.set_math(rtq.MATH_SPLIT_BF16)
+    """Runs a test under each fp32-activation arithmetic of the GEMM entry points
+    (passed to every call; the library keeps no arithmetic state)."""
+    return request.param
 
 
 def gpu_quantize(W: np.ndarray, fmt: str):
@@ -191,7 +190,7 @@ def test_gemm_q4_parity(M, N, K, math):
     ref = oracle.quantize_q4(W)
     w = gpu_quantize(W, "q4")
     assert_same_quant(w, ref, "q4")
-    y = host(rtq.gemm_q4(dev(x), w))
+    y = host(rtq.gemm_q4(dev(x), w, math=math))
     err = oracle.rel_fro(y, oracle.project_q4(x, *ref))
     assert err <= TOL, err
 
@@ -204,7 +203,7 @@ def test_gemm_q8_parity(M, N, K, math):
     ref = oracle.quantize_q8(W)
     w = gpu_quantize(W, "q8")
     assert_same_quant(w, ref, "q8")
-    y = host(rtq.gemm_q8(dev(x), w))
+    y = host(rtq.gemm_q8(dev(x), w, math=math))
     err = oracle.rel_fro(y, oracle.project_q8(x, *ref))
     assert err <= TOL, err
 
@@ -222,7 +221,7 @@ def test_gemm_identity_is_bit_exact(fmt, K, math):
     ref = oracle.quantize(W, fmt)
     w = gpu_quantize(W, fmt)
     assert_same_quant(w, ref, fmt)
-    y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), w))
+    y = host(rtq.gemm(dev(np.eye(K, dtype=np.float32)), w, math=math))
     want = np.ascontiguousarray(oracle.dequant(fmt, *ref).T)
     assert np.array_equal(y, want)
     nz = want != 0
@@ -241,7 +240,7 @@ def test_gemm_f8_parity(M, N, K, math):
     codes = oracle.quantize_f8(W)
     w = gpu_quantize(W, "f8")
     assert_same_quant(w, (codes, None), "f8")
-    y = host(rtq.gemm_f8(dev(x), w))
+    y = host(rtq.gemm_f8(dev(x), w, math=math))
     err = oracle.rel_fro(y, oracle.project_f8(x, codes))
     assert err <= TOL, err
 
@@ -255,12 +254,12 @@ def test_gemm_exact_integer_arithmetic(M, N, K, math):
     pairs = np.zeros((N, K // 32, 2), dtype=np.float16)
     pairs[..., 0] = 0.25
     pairs[..., 1] = -2.0
-    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs))))
+    y = host(rtq.gemm_q4(dev(x), rtq.Q4Weight(dev(payload), dev(pairs)), math=math))
     want = oracle.project_q4(x, payload, pairs)
     assert np.array_equal(y.astype(np.float64), want)
     q = synth.uniform_ints(N + 1, (N, K), -127, 127).astype(np.int8)
     scale = np.full(N, 0.5, dtype=np.float32)
-    y8 = host(rtq.gemm_q8(dev(x), rtq.Q8Weight(dev(q), dev(scale))))
+    y8 = host(rtq.gemm_q8(dev(x), rtq.Q8Weight(dev(q), dev(scale)), math=math))
     assert np.array_equal(y8.astype(np.float64), oracle.project_q8(x, q, scale))
 
 
@@ -274,11 +273,11 @@ def test_gemm_guard_bands_and_determinism(math):
     guard = 4096
     buf = torch.full((guard + M * N + guard,), 1234.5, dtype=torch.float32, device=DEV)
     y = buf[guard:guard + M * N].view(M, N)
-    rtq.gemm_q4(x, w, y=y)
+    rtq.gemm_q4(x, w, y=y, math=math)
     y1 = host(y).copy()
     b = host(buf)
     assert np.all(b[:guard] == 1234.5) and np.all(b[guard + M * N:] == 1234.5)
-    rtq.gemm_q4(x, w, y=y)
+    rtq.gemm_q4(x, w, y=y, math=math)
     assert np.array_equal(host(y).view(np.uint32), y1.view(np.uint32))
 
 
@@ -324,7 +323,7 @@ def test_block_project_one_block(recipe_name, math):
                       "all_f8": oracle.RECIPE_ALL_F8}[recipe_name]
     M = 80
     blk, refs, xs = make_block(3, 0, 0, M, recipe)
-    rtq.block_project([blk], M)
+    rtq.block_project([blk], M, math=math)
     for name, (fmt, ref, xin) in refs.items():
         assert_same_quant(blk[name].weight, ref, fmt)
         err = oracle.rel_fro(host(blk[name].y), oracle.project(fmt, xs[xin], *ref))
@@ -342,7 +341,7 @@ def test_block_project_skips_missing_gate_and_runs_multi_tile(math):
             blocks.append(blk)
             refss.append(refs)
             xss.append(xs)
-        rtq.block_project(blocks, M)
+        rtq.block_project(blocks, M, math=math)
         for b in range(2):
             assert ("wg" in blocks[b]) == (b == 0)
             for name, (fmt, ref, xin) in refss[b].items():
@@ -394,7 +393,7 @@ def test_full_size_twelve_blocks_sampled(M, heavy, math):
             rw[name] = (fmt, W)
         blocks.append(blk)
         refs_w.append(rw)
-    rtq.block_project(blocks, M)
+    rtq.block_project(blocks, M, math=math)
     torch.cuda.synchronize()
     worst = _sampled_check(blocks, refs_w, xs_all, M, np.random.default_rng(M))
     say(f"  worst sampled rel err {worst:.3e}")
@@ -446,7 +445,7 @@ def test_f8_nan_code_makes_its_column_nan(M, K, math):
     codes[5, K // 3] = 0x7F
     codes[31, K - 1] = 0xFF
     x = synth.activation(18, 0, "x_attn", M, K)
-    y = host(rtq.gemm_f8(dev(x), rtq.F8Weight(dev(codes))))
+    y = host(rtq.gemm_f8(dev(x), rtq.F8Weight(dev(codes)), math=math))
     nan_cols = np.zeros(N, dtype=bool)
     nan_cols[[5, 31]] = True
     assert np.isnan(y[:, nan_cols]).all()

@@ -41,10 +41,14 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 # Every symbol include/rtq.h declares.
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
            "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
-           "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_set_math", "rtq_get_math", "rtq_timing_enable",
+           "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_gemm_ex",
+           "rtq_block_project_ex", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
+# Arithmetic of a GEMM call (the `math` argument; None runs the library's
+# default, MATH_SPLIT_BF16, through the plain entry points).
 MATH_SPLIT_BF16, MATH_FP32_MFMA, MATH_BF16, MATH_SPLIT_F16 = 0, 1, 2, 3
+MATHS = {"split": MATH_SPLIT_BF16, "fp32": MATH_FP32_MFMA, "bf16": MATH_BF16, "split16": MATH_SPLIT_F16}
 
 
 class RtqError(RuntimeError):
@@ -97,10 +101,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         f.restype = ctypes.c_int
     lib.rtq_quantize_f8_host.argtypes = [vp, vp, i64, i64, i32]
     lib.rtq_quantize_f8_host.restype = ctypes.c_int
-    lib.rtq_set_math.argtypes = [i32]
-    lib.rtq_set_math.restype = ctypes.c_int
-    lib.rtq_get_math.argtypes = []
-    lib.rtq_get_math.restype = i32
+    lib.rtq_gemm_ex.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i32, vp]
+    lib.rtq_gemm_ex.restype = ctypes.c_int
+    lib.rtq_block_project_ex.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp]
+    lib.rtq_block_project_ex.restype = ctypes.c_int
     lib.rtq_timing_enable.argtypes = [i32]
     lib.rtq_timing_enable.restype = ctypes.c_int
     lib.rtq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -117,18 +121,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def version() -> str:
     return load_library().rtq_version().decode()
-
-
-def set_math(mode: int) -> None:
-    """MATH_SPLIT_BF16 (default, exact fp32 activations), MATH_FP32_MFMA,
-    MATH_BF16 (activations rounded to bf16) or MATH_SPLIT_F16 (row-scaled
-    activations in two fp16 limbs, 22 significant bits) for the GEMM entry
-    points (rtq_set_math)."""
-    _check(load_library().rtq_set_math(mode))
-
-
-def get_math() -> int:
-    return int(load_library().rtq_get_math())
 
 
 def timing_enable(on: bool = True) -> None:
@@ -262,7 +254,7 @@ def weight_from_tensors(payload: torch.Tensor, scale: torch.Tensor | None = None
     raise TypeError(f"payload dtype {payload.dtype} is not a quantized format")
 
 
-def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream) -> torch.Tensor:
+def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream, math: int | None = None) -> torch.Tensor:
     lib = load_library()
     w.validate()
     _need(x, torch.float32, "x")
@@ -275,6 +267,10 @@ def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream) -> torch.Tensor:
         _need(y, torch.float32, "y")
         if tuple(y.shape) != (M, w.N):
             raise ValueError(f"y must be [{M}, {w.N}], got {tuple(y.shape)}")
+    if math is not None:
+        _check(lib.rtq_gemm_ex(w.fmt, _ptr(x), _ptr(w.payload), _ptr(w.scale_tensor), _ptr(y), M, w.N, w.K,
+                               int(math), _stream(stream)))
+        return y
     if w.fmt == FMT_F8:
         _check(lib.rtq_gemm_f8(_ptr(x), _ptr(w.payload), _ptr(y), M, w.N, w.K, _stream(stream)))
         return y
@@ -283,34 +279,38 @@ def _gemm(x: torch.Tensor, w, y: torch.Tensor | None, stream) -> torch.Tensor:
     return y
 
 
-def gemm_q4(x: torch.Tensor, w: Q4Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def gemm_q4(x: torch.Tensor, w: Q4Weight, y: torch.Tensor | None = None, stream=None,
+            math: int | None = None) -> torch.Tensor:
     """y = x . dequant(w)^T for an int4 weight (rtq_gemm_q4)."""
     if not isinstance(w, Q4Weight):
         raise TypeError("gemm_q4 needs a Q4Weight")
-    return _gemm(x, w, y, stream)
+    return _gemm(x, w, y, stream, math)
 
 
-def gemm_q8(x: torch.Tensor, w: Q8Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def gemm_q8(x: torch.Tensor, w: Q8Weight, y: torch.Tensor | None = None, stream=None,
+            math: int | None = None) -> torch.Tensor:
     """y = x . dequant(w)^T for an int8 weight (rtq_gemm_q8)."""
     if not isinstance(w, Q8Weight):
         raise TypeError("gemm_q8 needs a Q8Weight")
-    return _gemm(x, w, y, stream)
+    return _gemm(x, w, y, stream, math)
 
 
-def gemm_f8(x: torch.Tensor, w: F8Weight, y: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+def gemm_f8(x: torch.Tensor, w: F8Weight, y: torch.Tensor | None = None, stream=None,
+            math: int | None = None) -> torch.Tensor:
     """y = x . W^T for an FP8 E4M3 weight (rtq_gemm_f8)."""
     if not isinstance(w, F8Weight):
         raise TypeError("gemm_f8 needs an F8Weight")
-    return _gemm(x, w, y, stream)
+    return _gemm(x, w, y, stream, math)
 
 
-def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None, bias=None) -> torch.Tensor:
+def gemm(x: torch.Tensor, w, y: torch.Tensor | None = None, stream=None, bias=None,
+         math: int | None = None) -> torch.Tensor:
     """y = x . W^T (+ bias, fp32 [N], through a one-projection rtq_block_project)."""
     if bias is None:
-        return _gemm(x, w, y, stream)
+        return _gemm(x, w, y, stream, math)
     if y is None:
         y = torch.empty((x.shape[0], w.N), dtype=torch.float32, device=x.device)
-    block_project([{"wq": Projection(w, x, y, bias)}], x.shape[0], stream)
+    block_project([{"wq": Projection(w, x, y, bias)}], x.shape[0], stream, math=math)
     return y
 
 
@@ -438,9 +438,14 @@ def pack_blocks(blocks: list[dict[str, Projection]], M: int):
     return arr, keep
 
 
-def block_project(blocks: list[dict[str, Projection]], M: int, stream=None, packed=None) -> None:
-    """Runs every projection of the given blocks (rtq_block_project).
-    `packed` may hold a pack_blocks() result to reuse across calls."""
+def block_project(blocks: list[dict[str, Projection]], M: int, stream=None, packed=None,
+                  math: int | None = None) -> None:
+    """Runs every projection of the given blocks (rtq_block_project, or
+    rtq_block_project_ex with the arithmetic `math`). `packed` may hold a
+    pack_blocks() result to reuse across calls."""
     lib = load_library()
     arr, _keep = packed if packed is not None else pack_blocks(blocks, M)
-    _check(lib.rtq_block_project(arr, len(arr), M, _stream(stream)))
+    if math is None:
+        _check(lib.rtq_block_project(arr, len(arr), M, _stream(stream)))
+    else:
+        _check(lib.rtq_block_project_ex(arr, len(arr), M, int(math), _stream(stream)))

@@ -4,7 +4,6 @@
 #include <rtq.h>
 
 #include <algorithm>
-#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -42,7 +41,9 @@ constexpr int64_t kMaxDim = (int64_t(1) << 30) - 1;
 // every kernel grid and tile count derived from a tensor fits 32 bits.
 constexpr int64_t kMaxElems = int64_t(1) << 38;
 
-std::atomic<int> g_math{rtq::kMathSplitBf16};
+bool math_ok(int32_t m) {
+    return m == RTQ_MATH_SPLIT_BF16 || m == RTQ_MATH_FP32_MFMA || m == RTQ_MATH_BF16 || m == RTQ_MATH_SPLIT_F16;
+}
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -117,8 +118,6 @@ struct Timing {
 Timing g_timing;
 
 namespace rtq {
-int math_mode() { return g_math.load(std::memory_order_relaxed); }
-
 int timing_begin(hipStream_t stream) {
     std::lock_guard<std::mutex> lock(g_timing.mu);
     if (!g_timing.on || g_timing.n >= kMaxTimed) return -1;
@@ -144,17 +143,6 @@ void timing_end(int slot, hipStream_t stream) {
 }  // namespace rtq
 
 extern "C" {
-
-rtq_status rtq_set_math(int32_t mode) {
-    clear_error();
-    if (mode != RTQ_MATH_SPLIT_BF16 && mode != RTQ_MATH_FP32_MFMA && mode != RTQ_MATH_BF16 &&
-        mode != RTQ_MATH_SPLIT_F16)
-        return fail(RTQ_ERR_FORMAT, "rtq_set_math: unknown mode %d", mode);
-    g_math.store(mode, std::memory_order_relaxed);
-    return RTQ_OK;
-}
-
-int32_t rtq_get_math(void) { return g_math.load(std::memory_order_relaxed); }
 
 const char* rtq_version(void) { return "rtq 0.1.0 gfx950"; }
 
@@ -199,35 +187,44 @@ const char* rtq_status_string(rtq_status s) {
     return "unknown status";
 }
 
+rtq_status rtq_gemm_ex(int32_t fmt, const float* x, const void* payload, const void* scale, float* y,
+                       int64_t M, int64_t N, int64_t K, int32_t math, void* stream) {
+    clear_error();
+    const char* name = fmt == RTQ_FMT_Q4 ? "rtq_gemm_q4" : fmt == RTQ_FMT_Q8 ? "rtq_gemm_q8" : "rtq_gemm_f8";
+    if (fmt != RTQ_FMT_Q4 && fmt != RTQ_FMT_Q8 && fmt != RTQ_FMT_F8)
+        return fail(RTQ_ERR_FORMAT, "rtq_gemm_ex: unknown fmt %d", fmt);
+    if (!math_ok(math)) return fail(RTQ_ERR_FORMAT, "%s: unknown arithmetic %d", name, math);
+    rtq_status s = check_proj(name, fmt, x, payload, fmt == RTQ_FMT_F8 ? nullptr : scale, y, M, N, K);
+    if (s != RTQ_OK || M == 0) return s;
+    const rtq::ProjTask t{fmt, static_cast<int>(N), static_cast<int>(K), payload,
+                          fmt == RTQ_FMT_F8 ? nullptr : scale, x, y};
+    char what[32];
+    std::snprintf(what, sizeof(what), "%s launch", name);
+    return hip_status(rtq::launch_gemm(t, M, math, static_cast<hipStream_t>(stream)), what);
+}
+
 rtq_status rtq_gemm_q4(const float* x, const uint8_t* payload, const uint16_t* pairs, float* y,
                        int64_t M, int64_t N, int64_t K, void* stream) {
-    clear_error();
-    rtq_status s = check_proj("rtq_gemm_q4", rtq::kFmtQ4, x, payload, pairs, y, M, N, K);
-    if (s != RTQ_OK || M == 0) return s;
-    const rtq::ProjTask t{rtq::kFmtQ4, static_cast<int>(N), static_cast<int>(K), payload, pairs, x, y};
-    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_q4 launch");
+    return rtq_gemm_ex(RTQ_FMT_Q4, x, payload, pairs, y, M, N, K, RTQ_MATH_SPLIT_BF16, stream);
 }
 
 rtq_status rtq_gemm_q8(const float* x, const int8_t* q, const float* scale, float* y, int64_t M,
                        int64_t N, int64_t K, void* stream) {
-    clear_error();
-    rtq_status s = check_proj("rtq_gemm_q8", rtq::kFmtQ8, x, q, scale, y, M, N, K);
-    if (s != RTQ_OK || M == 0) return s;
-    const rtq::ProjTask t{rtq::kFmtQ8, static_cast<int>(N), static_cast<int>(K), q, scale, x, y};
-    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_q8 launch");
+    return rtq_gemm_ex(RTQ_FMT_Q8, x, q, scale, y, M, N, K, RTQ_MATH_SPLIT_BF16, stream);
 }
 
 rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y, int64_t M, int64_t N, int64_t K,
                        void* stream) {
-    clear_error();
-    rtq_status s = check_proj("rtq_gemm_f8", rtq::kFmtF8, x, codes, nullptr, y, M, N, K);
-    if (s != RTQ_OK || M == 0) return s;
-    const rtq::ProjTask t{rtq::kFmtF8, static_cast<int>(N), static_cast<int>(K), codes, nullptr, x, y};
-    return hip_status(rtq::launch_gemm(t, M, static_cast<hipStream_t>(stream)), "rtq_gemm_f8 launch");
+    return rtq_gemm_ex(RTQ_FMT_F8, x, codes, nullptr, y, M, N, K, RTQ_MATH_SPLIT_BF16, stream);
 }
 
 rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
+    return rtq_block_project_ex(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream);
+}
+
+rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
     clear_error();
+    if (!math_ok(math)) return fail(RTQ_ERR_FORMAT, "rtq_block_project: unknown arithmetic %d", math);
     if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
     if (n_blocks < 1 || n_blocks > RTQ_MAX_BLOCKS)
         return fail(RTQ_ERR_SHAPE, "rtq_block_project: n_blocks=%d out of range [1, %d]", n_blocks, RTQ_MAX_BLOCKS);
@@ -286,11 +283,12 @@ rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t 
     if (M == 0) return RTQ_OK;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (n_grouped) {
-        const rtq_status s = hip_status(rtq::launch_grouped(grouped, n_grouped, M, st), "rtq_block_project launch");
+        const rtq_status s =
+            hip_status(rtq::launch_grouped(grouped, n_grouped, M, math, st), "rtq_block_project launch");
         if (s != RTQ_OK) return s;
     }
     for (int i = 0; i < n_single; ++i) {
-        const rtq_status s = hip_status(rtq::launch_gemm(single[i], M, st), "rtq_block_project launch");
+        const rtq_status s = hip_status(rtq::launch_gemm(single[i], M, math, st), "rtq_block_project launch");
         if (s != RTQ_OK) return s;
     }
     return RTQ_OK;

@@ -537,12 +537,12 @@ bool grouped_ok(const ProjTask& t) {
            (reinterpret_cast<uintptr_t>(t.payload) & 15) == 0;
 }
 
-hipError_t launch_gemm(const ProjTask& t, int64_t M, hipStream_t stream) {
+hipError_t launch_gemm(const ProjTask& t, int64_t M, int math, hipStream_t stream) {
     const TileArgs a{t.x, t.payload, t.scale, t.y, static_cast<int>(M), t.N, t.K};
     const bool safe = !grouped_ok(t);
-    const int nl = split_limbs(math_mode());
+    const int nl = split_limbs(math);
     if (!safe && nl && split_ok(t)) return launch_split(&t, 1, M, nl, stream);
-    if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, stream);
+    if (!safe && M <= kSmallMaxM) return launch_grouped(&t, 1, M, kMathFp32Mfma, stream);
     hipError_t e;
     if (t.fmt == kFmtQ4) e = launch_one<kFmtQ4, false>(a, stream);
     else if (t.fmt == kFmtQ8) e = safe ? launch_one<kFmtQ8, true>(a, stream) : launch_one<kFmtQ8, false>(a, stream);
@@ -561,7 +561,7 @@ hipError_t launch_grouped_fp32(const ProjTask* tasks, int count, int64_t M, hipS
         for (int i = 0; i < count; ++i) {
             ProjTask t = tasks[i];
             t.bias = nullptr;
-            const hipError_t e = launch_gemm(t, M, stream);
+            const hipError_t e = launch_gemm(t, M, kMathFp32Mfma, stream);
             if (e != hipSuccess) return e;
         }
         return hipSuccess;
@@ -634,8 +634,8 @@ hipError_t launch_grouped_fp32_bias(const ProjTask* tasks, int count, int64_t M,
     return e == hipSuccess ? launch_bias_add(tasks, count, M, stream) : e;
 }
 
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
-    const int nl = split_limbs(math_mode());
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream) {
+    const int nl = split_limbs(math);
     if (!nl) return launch_grouped_fp32_bias(tasks, count, M, stream);
     // Split path for every task it takes; the rest (weights past 32-bit
     // offsets) run on the fp32 kernels.

@@ -5,6 +5,13 @@
 // codes (RT-J FP8 card, section "FP8 Format"), dequantized inside the GEMM as
 // the cards' opening paragraphs describe.
 //
+// Row scale. Every row of x is first scaled by the power of two 2^e that puts
+// its largest magnitude in [2^14, 2^15) (exact for every value that stays a
+// normal fp32 number), and every output row is scaled back by 2^-e (exact)
+// after the int8 scale, before the bias. The code sums below therefore stay
+// far inside the fp32 range whatever the magnitude of the row. "x" below is
+// the scaled row.
+//
 // Arithmetic. Every fp32 activation is split, exactly, into three bf16 limbs:
 //   x1 = x with the low 16 bits of its encoding cleared  (top 8 significant bits)
 //   r  = x - x1                                           (exact, <= 16 bits)
@@ -27,20 +34,20 @@
 // tile instead of three, y = bf16(x) . W^T with the same exact weight side and
 // fp32 accumulation; the group sums X_g are those of the rounded values.
 //
-// Two fp16 limbs (NL = 2). Each row of x is scaled by a power of two 2^e so
-// that its largest magnitude lies in [2^14, 2^15), then split as h = fp16(v),
-// l = fp16(v - h) (v = x * 2^e, both roundings to nearest). h + l holds v to
+// Two fp16 limbs (NL = 2). Each scaled value v (largest magnitude of the row
+// in [2^14, 2^15), inside the fp16 range) is split as h = fp16(v),
+// l = fp16(v - h) (both roundings to nearest). h + l holds v to
 // 22 significant bits (relative error <= 2^-22 per element, plus an absolute
 // 2^-25 in the scaled units for elements far below the row's largest). Codes
 // are exact in fp16, products of code and limb exact in fp32, and
 // v_mfma_f32_16x16x32_f16 accumulates two limb products per group and tile
-// instead of three. X_g are the sums of the scaled values; every output is
-// scaled back by 2^-e of its row (exact) after the int8 scale, before the bias.
+// instead of three. X_g are the sums of the scaled values.
 //
 // Data movement.
-//  1. A pre-pass (prep_kernel) splits every distinct activation once into a
-//     limb image in a device workspace: NL bf16 planes in MFMA operand order,
-//     with an XOR swizzle that makes the LDS reads conflict-free, plus X_g.
+//  1. A pre-pass (prep_kernel) scales and splits every distinct activation
+//     once into a limb image in a device workspace: NL limb planes in MFMA
+//     operand order, with an XOR swizzle that makes the LDS reads
+//     conflict-free, plus X_g and the row exponents.
 //  2. The GEMM copies each 32-wide group of its row block from that image into
 //     an LDS ring with global_load_lds_dwordx4 (direct to LDS: no registers, no
 //     VALU), ahead of the compute, one barrier per group.
@@ -71,7 +78,8 @@ namespace {
 //   and 16-byte chunk c (k = 8c..8c+7 of the group) sit at
 //   (r*4 + (c ^ ((r>>2)&3))) * 16;
 //   then the group sums X[g][row] (fp32, RB*16 rows per group);
-//   with NL = 2 then the row exponents e[row] (int32, RB*16 rows).
+//   then the row exponents e[row] (int32, RB*16 rows): row `row` of x was
+//   scaled by 2^e[row] before the split.
 // For a fixed group the RB blocks are contiguous, so a row block of BM rows is
 // one contiguous run of BM/16 * NL KB.
 // ---------------------------------------------------------------------------
@@ -80,7 +88,7 @@ __host__ __device__ inline int64_t image_exp_offset(int G, int RB, int NL) {
     return image_plane_bytes(G, RB, NL) + int64_t(G) * RB * 16 * 4;
 }
 __host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
-    return image_exp_offset(G, RB, NL) + (NL == 2 ? int64_t(RB) * 16 * 4 : 0);
+    return image_exp_offset(G, RB, NL) + int64_t(RB) * 16 * 4;
 }
 
 constexpr int kMaxImages = 48;
@@ -97,74 +105,22 @@ struct PrepArgs {
 };
 static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
-// One thread per (row, 8-wide chunk). A wave covers one 16-row block of one
-// group (4 threads per row), so each limb it writes is one contiguous 1 KB run,
-// and the group sum of a row is two shuffles in a fixed order.
+// One wave per row: the row's scale needs its largest magnitude first. Lane L
+// takes k = 512*j + 8L .. 8L+7 of every 512-wide piece j (group 16j + L/4,
+// chunk L%4); the row maximum is a wave reduction. With max|x[row][:]| =
+// f * 2^E, f in [0.5, 1), the exponent is e = 15 - E (e = 15 for a zero row),
+// so the scaled row's largest magnitude lies in [2^14, 2^15). Every scaled
+// value v = x * 2^e (exact while v stays a normal fp32 number) is then
+//   NL = 3: split exactly into three bf16 limbs (split2);
+//   NL = 2: split into two fp16 limbs h = fp16(v), l = fp16(v - h);
+//   NL = 1: rounded to the nearest bf16;
+// and the group sums X_g are sums of the scaled values (of the rounded ones
+// with NL = 1), each formed as ((v0+v1)+(v2+v3))+((v4+v5)+(v6+v7)) per chunk,
+// then chunks (0+1)+(2+3). Rows of K <= 512*kPrepHold stay in registers
+// between the two passes; longer rows are read again.
+constexpr int kPrepHold = 4;
 template <int NL>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
-    const int b = blockIdx.x;
-    const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
-    const int M = p.M[i], K = p.K[i], RB = p.RB[i];
-    const int G = K / 32;
-    const int64_t t = static_cast<int64_t>(b - p.block_begin[i]) * 256 + threadIdx.x;
-    const int64_t total = int64_t(RB) * 16 * G * 4;
-    const bool live = t < total;
-    const int c = static_cast<int>(t & 3);
-    const int r = static_cast<int>((t >> 2) & 15);
-    const int64_t blk_id = t >> 6;                      // g * RB + rb
-    const int rb = static_cast<int>(blk_id % RB);
-    const int g = static_cast<int>(blk_id / RB);
-    const int row = rb * 16 + r;
-    float v[8];
-    if (live && row < M) {
-        const float4* src = reinterpret_cast<const float4*>(p.x[i] + static_cast<int64_t>(row) * K + g * 32 + c * 8);
-        const float4 a = src[0], bb = src[1];
-        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-        v[4] = bb.x; v[5] = bb.y; v[6] = bb.z; v[7] = bb.w;
-    } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-    }
-    uint32_t h[4], m[4], l[4];
-    if constexpr (NL == 3) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) split2(v[2 * j], v[2 * j + 1], h[j], m[j], l[j]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h[j] = bf16x2_rne(v[2 * j], v[2 * j + 1]);
-            v[2 * j] = bitsf(h[j] << 16);               // the group sum is over the rounded values
-            v[2 * j + 1] = bitsf(h[j] & 0xffff0000u);
-        }
-    }
-    float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-    const float s1 = __shfl_xor(s, 1, 64);
-    s = (c & 1) ? s1 + s : s + s1;                  // chunks (0+1), (2+3)
-    const float s2 = __shfl_xor(s, 2, 64);
-    s = (c & 2) ? s2 + s : s + s2;                  // (0+1) + (2+3)
-    if (!live) return;
-    unsigned char* img = p.img[i];
-    unsigned char* blk = img + blk_id * (NL * 1024) + swz(r, c) * 16;
-    *reinterpret_cast<uint4*>(blk + 0) = make_uint4(h[0], h[1], h[2], h[3]);
-    if constexpr (NL == 3) {
-        *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(m[0], m[1], m[2], m[3]);
-        *reinterpret_cast<uint4*>(blk + 2048) = make_uint4(l[0], l[1], l[2], l[3]);
-    }
-    if (c == 0) {
-        float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, NL));
-        X[static_cast<int64_t>(g) * RB * 16 + row] = s;
-    }
-}
-
-// Two fp16 limbs (NL = 2). One wave per row: the row's scale needs its largest
-// magnitude first. Lane L takes k = 512*j + 8L .. 8L+7 of every 512-wide piece
-// j (group 16j + L/4, chunk L%4); the row maximum is a wave reduction. With
-// max|x[row][:]| = f * 2^E, f in [0.5, 1), the exponent is e = 15 - E (e = 15
-// for a zero row). Rows of K <= 512*kPrepHold stay in registers between the
-// two passes; longer rows are read again. The group sums use the order of
-// prep_kernel.
-constexpr int kPrepHold = 4;
-__global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs p) {
     const int b = blockIdx.x;
     const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
     const int M = p.M[i], K = p.K[i], RB = p.RB[i];
@@ -208,13 +164,23 @@ __global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs p) {
     const int ex = 15 - E;
 
     unsigned char* img = p.img[i];
-    float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, 2));
+    float* X = reinterpret_cast<float*>(img + image_plane_bytes(G, RB, NL));
     auto emit = [&](int j, float (&v)[8]) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) v[e] = ldexpf(v[e], ex);
-        uint32_t h[4], l[4];
+        uint32_t h[4], m[4], l[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) split_f16x2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+        for (int q = 0; q < 4; ++q) {
+            if constexpr (NL == 3) {
+                split2(v[2 * q], v[2 * q + 1], h[q], m[q], l[q]);
+            } else if constexpr (NL == 2) {
+                split_f16x2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+            } else {
+                h[q] = bf16x2_rne(v[2 * q], v[2 * q + 1]);
+                v[2 * q] = bitsf(h[q] << 16);               // the group sum is over the rounded values
+                v[2 * q + 1] = bitsf(h[q] & 0xffff0000u);
+            }
+        }
         float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
         const float s1 = __shfl_xor(s, 1, 64);
         s = (c & 1) ? s1 + s : s + s1;
@@ -222,9 +188,14 @@ __global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs p) {
         s = (c & 2) ? s2 + s : s + s2;
         const int g = 16 * j + (lane >> 2);
         if (g < G) {
-            unsigned char* blk = img + (static_cast<int64_t>(g) * RB + rb) * 2048 + swz(r, c) * 16;
+            unsigned char* blk = img + (static_cast<int64_t>(g) * RB + rb) * (NL * 1024) + swz(r, c) * 16;
             *reinterpret_cast<uint4*>(blk) = make_uint4(h[0], h[1], h[2], h[3]);
-            *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(l[0], l[1], l[2], l[3]);
+            if constexpr (NL == 3) {
+                *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(m[0], m[1], m[2], m[3]);
+                *reinterpret_cast<uint4*>(blk + 2048) = make_uint4(l[0], l[1], l[2], l[3]);
+            } else if constexpr (NL == 2) {
+                *reinterpret_cast<uint4*>(blk + 1024) = make_uint4(l[0], l[1], l[2], l[3]);
+            }
             if (c == 0) X[static_cast<int64_t>(g) * RB * 16 + row] = s;
         }
     };
@@ -236,7 +207,7 @@ __global__ __launch_bounds__(256) void prep_f16_kernel(PrepArgs p) {
         load(j, v);
         emit(j, v);
     }
-    if (lane == 0) reinterpret_cast<int*>(img + image_exp_offset(G, RB, 2))[row] = ex;
+    if (lane == 0) reinterpret_cast<int*>(img + image_exp_offset(G, RB, NL))[row] = ex;
 }
 
 // ---------------------------------------------------------------------------
@@ -620,11 +591,11 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         min_flush(i);
     }
 
-    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile. With two
-    //      fp16 limbs each row is scaled back by 2^-e[row] (exact) after the
-    //      int8 scale and before the bias. ----
+    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile. Each row
+    //      is scaled back by 2^-e[row] (exact) after the int8 scale and before
+    //      the bias. ----
     int rexp[TM][4];
-    if constexpr (NL == 2) {
+    {
         const int* exps = reinterpret_cast<const int*>(a.img + image_exp_offset(G, RB, NL));
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm)
@@ -648,7 +619,7 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                     // the int8 scale first: the code sum of a row scaled far
                     // down would overflow if scaled back before it
                     if constexpr (FMT == kFmtQ8) v *= sc;
-                    if constexpr (NL == 2) v = ldexpf(v, rexp[tm][e]);
+                    v = ldexpf(v, rexp[tm][e]);
                     if (a.bias) v += bv;
                     a.y[static_cast<int64_t>(row) * N + col] = v;
                 }
@@ -819,19 +790,14 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
             p.K[c] = u.K;
             p.RB[c] = RB;
             p.block_begin[c] = blocks;
-            if (NL == 2) {
-                blocks += RB * 4;                           // one wave per row
-            } else {
-                const int64_t threads = int64_t(RB) * 16 * (u.K / 32) * 4;
-                blocks += static_cast<int>((threads + 255) / 256);
-            }
+            blocks += RB * 4;                               // one wave per row
         }
         p.block_begin[p.count] = blocks;
         seg_fill_coarse(p.block_begin, p.block_coarse, p.count);
         if (NL == 1)
             prep_kernel<1><<<blocks, 256, 0, stream>>>(p);
         else if (NL == 2)
-            prep_f16_kernel<<<blocks, 256, 0, stream>>>(p);
+            prep_kernel<2><<<blocks, 256, 0, stream>>>(p);
         else
             prep_kernel<3><<<blocks, 256, 0, stream>>>(p);
         const hipError_t e = hipGetLastError();
@@ -840,17 +806,34 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
     return hipSuccess;
 }
 
-void release_threshold_once(int device) {
+// The library's own stream-ordered memory pool of a device, created on first
+// use and kept for the process; it keeps freed memory (release threshold at
+// the maximum), so steady-state calls are served from the pool without a
+// driver allocation. The device's default pool is left as it is.
+hipError_t library_pool(int device, hipMemPool_t* out) {
     static std::mutex mu;
-    static bool done[64] = {};
+    static hipMemPool_t pools[64] = {};
+    if (device < 0 || device >= 64) return hipErrorInvalidDevice;
     std::lock_guard<std::mutex> lock(mu);
-    if (device < 0 || device >= 64 || done[device]) return;
-    hipMemPool_t pool;
-    if (hipDeviceGetDefaultMemPool(&pool, device) == hipSuccess) {
+    if (!pools[device]) {
+        hipMemPoolProps props{};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = device;
+        hipMemPool_t pool = nullptr;
+        hipError_t e = hipMemPoolCreate(&pool, &props);
+        if (e != hipSuccess) return e;
         uint64_t keep = ~0ull;
-        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        e = hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        if (e != hipSuccess) {
+            (void)hipMemPoolDestroy(pool);
+            return e;
+        }
+        pools[device] = pool;
     }
-    done[device] = true;
+    *out = pools[device];
+    return hipSuccess;
 }
 
 }  // namespace
@@ -930,10 +913,11 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
         }
     }
     int device = 0;
-    (void)hipGetDevice(&device);
-    release_threshold_once(device);
+    hipError_t e = hipGetDevice(&device);
+    hipMemPool_t pool = nullptr;
+    if (e == hipSuccess) e = library_pool(device, &pool);
     void* ws = nullptr;
-    hipError_t e = hipMallocAsync(&ws, static_cast<size_t>(ws_bytes), stream);
+    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(ws_bytes), pool, stream);
     if (e != hipSuccess) return e;
     unsigned char* wsb = static_cast<unsigned char*>(ws);
     e = run_prep(inputs, n_in, wsb, M, RB, NL, stream);

@@ -35,21 +35,20 @@ struct ProjTask {
 int timing_begin(hipStream_t stream);
 void timing_end(int slot, hipStream_t stream);
 
-// Arithmetic of the GEMM kernels (process-wide, see rtq_set_math).
+// Arithmetic of a GEMM call (the rtq_gemm_ex / rtq_block_project_ex argument).
 enum Math : int { kMathSplitBf16 = 0, kMathFp32Mfma = 1, kMathBf16 = 2, kMathSplitF16 = 3 };
-int math_mode();
 // Limbs of the split path for a math mode: 3 (exact bf16 split), 2 (fp16
 // split of the row-scaled x) or 1 (bf16 x); 0 = fp32 path.
 inline int split_limbs(int mode) {
     return mode == kMathSplitBf16 ? 3 : mode == kMathSplitF16 ? 2 : mode == kMathBf16 ? 1 : 0;
 }
 
-// Single projection y[M][N] = x[M][K] . dequant(W)^T.
-hipError_t launch_gemm(const ProjTask& task, int64_t M, hipStream_t stream);
+// Single projection y[M][N] = x[M][K] . dequant(W)^T in arithmetic `math`.
+hipError_t launch_gemm(const ProjTask& task, int64_t M, int math, hipStream_t stream);
 
 // Several projections sharing M, in grouped launches. Every task must satisfy
 // grouped_ok().
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream);
 bool grouped_ok(const ProjTask& task);
 
 // Split-limb path (gemm_split.hip): every projection of the call, sharing M,
