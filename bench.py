@@ -76,7 +76,9 @@ def parse():
                     help="give every projection an fp32 bias (y = x.W^T + b) to time the bias epilogue")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-attainable", action="store_true",
-                    help="skip the measured streaming-read ceiling (hbm_attainable)")
+                    help="skip the measured ceilings (streaming read, matrix-instruction loop)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the single-GEMM and one-block configurations (config_cases)")
     return ap.parse_args()
 
 
@@ -175,6 +177,10 @@ def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
     del sets
     torch.cuda.empty_cache()
     flops_step, bytes_step = fl * nb, wb * nb
+    act_bytes = sum(M * k * 4 for k in synth.INPUT_WIDTH.values())    # the four inputs of a block
+    out_bytes = sum(M * synth.BLOCK_SHAPES[n][0] * 4 for n in synth.PROJ_ORDER)
+    alg_step = bytes_step + nb * (out_bytes + (act_bytes if workload == "m80" else 0)) + \
+        (act_bytes if workload != "m80" else 0)
     ms_step = wall / steps * 1e3
     per_step = launches / steps
     launch_ms = kernel_ms / launches
@@ -185,6 +191,7 @@ def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
         "kernel_tflops": flops_step / per_step / (launch_ms * 1e-3) / 1e12,
         "kernel_weight_gbs": bytes_step / per_step / (launch_ms * 1e-3) / 1e9,
         "flops_per_step": flops_step, "weight_bytes_per_step": bytes_step, "steps": steps,
+        "algorithmic_bytes_per_step": alg_step,
     }
 
 
@@ -221,24 +228,97 @@ def m_sweep(torch, rtq, synth, Ms, math, steps=200, warmup=20, recipe="mixed"):
     return out
 
 
-def attainable_hbm_gbs(torch, gib=4, reps=10):
-    """Read bandwidth a plain device-wide streaming reduction (torch.sum over a
-    `gib` GiB fp32 buffer) attains on this GPU: the measured ceiling the weight
-    stream is compared with, beside the 8 TB/s published peak."""
-    buf = torch.ones(gib * (1 << 28), dtype=torch.float32, device="cuda:0")
-    for _ in range(2):
-        buf.sum()
-    torch.cuda.synchronize()
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        buf.sum()
-    t1.record()
-    t1.synchronize()
-    gbs = buf.numel() * 4 * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+def measured_ceilings(torch, rtq, gib=4, reps=5):
+    """The chip's measured ceilings beside the published peaks: the library's
+    streaming-read kernel (rtq_diag_stream_read) over a `gib` GiB buffer, best
+    of a small sweep of loads in flight and grid sizes, and its back-to-back
+    matrix-instruction loop (rtq_diag_mfma_loop) for fp16, bf16 and fp32.
+    Timed with events on the stream the kernels run on."""
+    dev = "cuda:0"
+    buf = torch.ones(gib * (1 << 28), dtype=torch.float32, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    best = None
+    sweep = []
+    for unroll in (4, 8, 16):
+        for blocks in (2048, 4096, 8192):
+            rtq.diag_stream_read(buf, unroll, blocks, sink)
+            ev0.record()
+            for _ in range(reps):
+                rtq.diag_stream_read(buf, unroll, blocks, sink)
+            ev1.record()
+            ev1.synchronize()
+            gbs = buf.numel() * 4 * reps / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+            sweep.append({"unroll": unroll, "blocks": blocks, "gbs": round(gbs, 1)})
+            if best is None or gbs > best["gbs"]:
+                best = sweep[-1]
     del buf
     torch.cuda.empty_cache()
-    return gbs
+    fsink = torch.zeros(1, dtype=torch.float32, device=dev)
+    mfma = {}
+    for kind, name, peak in ((0, "fp16", PEAK_BF16_MFMA_TFLOPS), (1, "bf16", PEAK_BF16_MFMA_TFLOPS),
+                             (2, "fp32", PEAK_FP32_MFMA_TFLOPS)):
+        iters = 20000 if kind < 2 else 5000
+        rtq.diag_mfma_loop(kind, 100, 2048, fsink)
+        ev0.record()
+        flops = rtq.diag_mfma_loop(kind, iters, 2048, fsink)
+        ev1.record()
+        ev1.synchronize()
+        tf = flops / (ev0.elapsed_time(ev1) * 1e-3) / 1e12
+        mfma[name] = {"tflops": round(tf, 1), "frac_of_peak": round(tf / peak, 4),
+                      "instruction": ["v_mfma_f32_16x16x32_f16", "v_mfma_f32_16x16x32_bf16",
+                                      "v_mfma_f32_16x16x4_f32"][kind]}
+    return {"hbm_read_gbs": best["gbs"], "hbm_frac_of_peak": round(best["gbs"] / PEAK_HBM_GBS, 4),
+            "hbm_how": f"rtq_diag_stream_read over a {gib} GiB buffer (16-byte loads, best of the sweep), "
+                       f"{reps} passes timed with HIP events",
+            "hbm_sweep": sweep, "mfma": mfma,
+            "mfma_how": "rtq_diag_mfma_loop: 2048 workgroups x 4 waves, 8 independent accumulators per wave"}
+
+
+def config_cases(torch, rtq, synth, math, reps=2000, warmup=100):
+    """The small single-GEMM and one-block configurations at M = 80 (weights
+    resident, one seeded weight set): time per call, TFLOP/s, weight GB/s."""
+    dev = "cuda:0"
+    M = synth.M_GOLDEN
+    out = {}
+    cases = [("cfg1_q4_wq_512x512", "q4", "wq", 512, 512, "x_attn"),
+             ("cfg2_q8_wo_512x512", "q8", "wo", 512, 512, "x_o"),
+             ("cfg2_q8_w2_512x2048", "q8", "w2", 512, 2048, "h")]
+    for name, fmt, proj, N, K, xin in cases:
+        w = rtq.quantize(torch.from_numpy(synth.weight(1, 0, 0, proj, N, K)).to(dev), fmt)
+        x = torch.from_numpy(synth.activation(1, 0, xin, M, K)).to(dev)
+        y = torch.empty((M, N), dtype=torch.float32, device=dev)
+        for _ in range(warmup):
+            rtq.gemm(x, w, y=y, math=math)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            rtq.gemm(x, w, y=y, math=math)
+        torch.cuda.synchronize()
+        t = (time.perf_counter() - t0) / reps
+        wb = N * K // 2 + N * (K // 32) * 4 if fmt == "q4" else N * K + N * 4
+        out[name] = {"us_per_call": round(t * 1e6, 3), "tflops": round(2 * M * N * K / t / 1e12, 3),
+                     "weight_gbs": round(wb / t / 1e9, 2), "M": M, "N": N, "K": K, "fmt": fmt}
+    # one RT-J block (8 projections, 4 inputs)
+    xs = {n: torch.from_numpy(synth.activation(3, 0, n, M)).to(dev) for n in synth.INPUT_WIDTH}
+    blk = {}
+    for name in synth.PROJ_ORDER:
+        N, K, xin = synth.BLOCK_SHAPES[name]
+        w = rtq.quantize(torch.from_numpy(synth.weight(3, 0, 0, name)).to(dev), rtq.RECIPE_MIXED[name])
+        blk[name] = rtq.Projection(w, xs[xin], torch.empty((M, N), dtype=torch.float32, device=dev))
+    packed = rtq.pack_blocks([blk], M)
+    for _ in range(warmup):
+        rtq.block_project([blk], M, packed=packed, math=math)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        rtq.block_project([blk], M, packed=packed, math=math)
+    torch.cuda.synchronize()
+    t = (time.perf_counter() - t0) / reps
+    wb, fl = block_bytes_flops(M)
+    out["cfg3_one_block"] = {"us_per_call": round(t * 1e6, 3), "tflops": round(fl / t / 1e12, 3),
+                             "weight_gbs": round(wb / t / 1e9, 2), "M": M}
+    return out
 
 
 def load_traffic(workload, math, recipe="mixed"):
@@ -249,10 +329,14 @@ def load_traffic(workload, math, recipe="mixed"):
 
 
 def roofline(res, math, workload, recipe="mixed"):
-    """Roofline of the main GEMM kernel: algorithmic flops per launch over the
-    kernel's average launch duration, against the peak of the matrix unit it
-    runs on (split: bf16 MFMA, three limb products per algorithmic multiply-add;
-    split16: fp16 MFMA, two)."""
+    """Roofline of the main GEMM kernel from its average launch time (HIP
+    events on the launch stream). At M = 80 the binding roof is HBM: the
+    achieved figure is the packed weight bytes one launch streams over the
+    launch time, against 8 TB/s (the matrix-unit figures ride along under
+    "mfma"). At M = 65536 it is the matrix unit: algorithmic flops over the
+    launch time, against the peak of the unit the arithmetic runs on (split:
+    bf16 MFMA, three limb products per multiply-add; split16: fp16 MFMA, two;
+    bf16: one; fp32: the fp32 matrix peak)."""
     ach = res["kernel_tflops"]
     if math == "split":
         peak, issued = PEAK_BF16_MFMA_TFLOPS, 3
@@ -263,17 +347,24 @@ def roofline(res, math, workload, recipe="mixed"):
     else:
         peak, issued = PEAK_FP32_MFMA_TFLOPS, 1
     tr = load_traffic(workload, math, recipe)
-    out = {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
-           "frac": round(ach / peak, 5), "traffic": tr["bytes_per_launch"] if tr else None,
-           "traffic_detail": tr,
-           "kernel": KERNELS[(math, workload)],
-           "kernel_ms_per_launch": round(res["kernel_ms_per_launch"], 6),
+    mfma = {"achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s", "frac": round(ach / peak, 5),
+            "mfma_flops_per_algorithmic_flop": issued, "matrix_unit_frac": round(ach * issued / peak, 5)}
+    out = {"kernel": KERNELS[(math, workload)], "kernel_ms_per_launch": round(res["kernel_ms_per_launch"], 6),
            "launches_per_step": res["kernel_launches_per_step"],
-           "mfma_flops_per_algorithmic_flop": issued,
-           "matrix_unit_frac": round(ach * issued / peak, 5),
-           "weight_gbs_in_kernel": round(res["kernel_weight_gbs"], 2),
-           "weight_hbm_frac_in_kernel": round(res["kernel_weight_gbs"] / PEAK_HBM_GBS, 5)}
-    return out
+           "traffic": tr["bytes_per_launch"] if tr else None, "traffic_detail": tr}
+    if workload == "m80":
+        gbs = res["kernel_weight_gbs"]
+        per_launch_s = res["kernel_ms_per_launch"] * 1e-3
+        all_bytes = res["algorithmic_bytes_per_step"] / res["kernel_launches_per_step"]
+        return {"bound": "hbm", "achieved": round(gbs, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 5), **out,
+                "basis": "packed weight bytes per launch / average launch time",
+                "all_algorithmic_bytes_gbs": round(all_bytes / per_launch_s / 1e9, 2),
+                "all_algorithmic_bytes_frac": round(all_bytes / per_launch_s / 1e9 / PEAK_HBM_GBS, 5),
+                "mfma": mfma}
+    return {"bound": "mfma", **mfma, **out,
+            "weight_gbs_in_kernel": round(res["kernel_weight_gbs"], 2),
+            "weight_hbm_frac_in_kernel": round(res["kernel_weight_gbs"] / PEAK_HBM_GBS, 5)}
 
 
 def cpu_baseline(cfg, M, seconds, rows=None, recipe="mixed"):
@@ -313,6 +404,41 @@ def cpu_baseline(cfg, M, seconds, rows=None, recipe="mixed"):
             "kind": "oracle",
             "sample": f"{done} RT-J block passes (8 projections, M={Ms}, numpy dequant + fp64 matmul) "
                       f"in {el:.1f} s, cycling 2 oracle-quantized blocks"}
+
+
+def cpu_baseline_extra(seconds):
+    """Beside the all-thread baseline: the same oracle on one thread (bounded
+    sample at M = 80), and one whole RT-J block at M = 65536 timed once and
+    reported x 12 as the 12-block pass (an explicit extrapolation)."""
+    import oracle
+    import synth
+    out = {}
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:                                                   # noqa: BLE001
+        threadpool_limits = None
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            r = cpu_baseline(4, synth.M_GOLDEN, seconds)
+        r["cores"] = 1
+        out["single_core_m80"] = r
+    blk = []
+    for name in synth.PROJ_ORDER:
+        fmt = oracle.RECIPE_MIXED[name]
+        N, K, xin = synth.BLOCK_SHAPES[name]
+        blk.append((fmt, oracle.quantize(synth.weight(5, 0, 0, name), fmt), xin))
+    xs = {n: synth.activation(5, synth.SHARED_BLOCK, n, synth.M_LARGE) for n in synth.INPUT_WIDTH}
+    _, fl = block_bytes_flops(synth.M_LARGE)
+    t0 = time.perf_counter()
+    for fmt, packed, xin in blk:
+        oracle.project(fmt, xs[xin], *packed)
+    el = time.perf_counter() - t0
+    out["m65536_one_block_x12"] = {
+        "value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "s_per_block": round(el, 3),
+        "s_per_12_block_pass_extrapolated": round(12 * el, 3),
+        "sample": "one RT-J block (8 projections) at M=65536 in full, timed once; the 12-block pass is 12x that "
+                  "(extrapolated, not run)"}
+    return out
 
 
 def main():
@@ -417,10 +543,25 @@ def main():
                     "product; reported apart from the fp32-activation figures above",
             **bf16}
     if not args.no_attainable:
-        hbm = attainable_hbm_gbs(torch)
-        line["hbm_attainable"] = {"gbs": round(hbm, 1), "frac_of_peak": round(hbm / PEAK_HBM_GBS, 4),
-                                  "how": "torch.sum over a 4 GiB fp32 buffer, 10 passes (HIP events)",
-                                  "weight_frac_of_attainable": round(prim["weight_gbs"] / hbm, 5)}
+        ceil = measured_ceilings(torch, rtq)
+        line["measured_ceilings"] = ceil
+        hbm = ceil["hbm_read_gbs"]
+        rl = line["roofline"]
+        if rl["bound"] == "hbm":
+            rl["frac_of_measured_ceiling"] = round(rl["achieved"] / hbm, 5)
+        unit = {"split16": "fp16", "split": "bf16", "bf16": "bf16", "fp32": "fp32"}[args.math]
+        line["weight_frac_of_measured_hbm"] = round(prim["weight_gbs"] / hbm, 5)
+        for wl in out:
+            tgt = rl if wl == prim_name else line[wl]["roofline"]
+            if tgt["bound"] == "mfma":
+                tgt["frac_of_measured_ceiling"] = round(tgt["achieved"] / ceil["mfma"][unit]["tflops"], 5)
+            else:
+                tgt["mfma"]["frac_of_measured_ceiling"] = round(
+                    tgt["mfma"]["achieved"] / ceil["mfma"][unit]["tflops"], 5)
+    if not args.no_configs and args.workload in ("m80", "both"):
+        line["config_cases"] = {
+            "note": "single GEMMs and one block at M = 80, one resident weight set, per call (dispatch included)",
+            **config_cases(torch, rtq, synth, main_math)}
     if args.m_sweep is None:
         args.m_sweep = "1,2,4,8,16,32,48,80" if args.workload == "both" else ""
     if args.m_sweep:
@@ -429,12 +570,14 @@ def main():
                     "in-kernel weight GB/s against the 8000 GB/s HBM peak",
             "points": m_sweep(torch, rtq, synth, [int(v) for v in args.m_sweep.split(",")], main_math,
                               recipe=args.recipe)}
-        if "hbm_attainable" in line:
+        if "measured_ceilings" in line:
             for pt in line["m_sweep"]["points"]:
-                pt["weight_frac_of_attainable_in_kernel"] = round(
-                    pt["weight_gbs_in_kernel"] / line["hbm_attainable"]["gbs"], 4)
+                pt["weight_frac_of_measured_hbm_in_kernel"] = round(
+                    pt["weight_gbs_in_kernel"] / line["measured_ceilings"]["hbm_read_gbs"], 4)
     if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
+        if args.recipe == "mixed":
+            line["cpu_baseline"].update(cpu_baseline_extra(args.cpu_seconds / 2))
     print(json.dumps(line), flush=True)
 
 

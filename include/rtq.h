@@ -32,14 +32,15 @@
  *     never retains a caller's pointer past the call's work on its stream.
  *   - Memory and state of the library itself: a GEMM call on the split path
  *     with M above 32 (or a K other than 256, 512, 1024, 2048) takes one
- *     stream-ordered workspace (limb images of x, K-chunk partials) with
- *     hipMallocAsync on the caller's stream from the device's default memory
- *     pool and returns it with hipFreeAsync on the same stream (smaller calls
- *     split x inside the GEMM kernel and allocate nothing); the
- *     pool's release threshold is raised once per device, so steady-state
- *     calls reuse pool memory. Process-wide state: the arithmetic mode
- *     (rtq_set_math) and the timing events (rtq_timing_enable); per thread:
- *     the last error message.
+ *     stream-ordered workspace (limb images of x, K-chunk partials) from a
+ *     memory pool of the library's own (one per device, created on first
+ *     use, kept for the process, releasing nothing back to the device), with
+ *     hipMallocFromPoolAsync / hipFreeAsync on the caller's stream, so
+ *     steady-state calls reuse pool memory without a driver allocation;
+ *     smaller calls split x inside the GEMM kernel and allocate nothing. The
+ *     device's default pool is not touched. The arithmetic is an argument of
+ *     each call. Process-wide state: those pools and the timing events
+ *     (rtq_timing_enable, a profiling aid); per thread: the last error message.
  *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*; NULL
  *     selects the null stream). Nothing is synchronized. Faults during
  *     execution surface at the caller's next synchronization.
@@ -176,33 +177,45 @@ rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64
 /* Arithmetic of a GEMM call, chosen per call (the `math` argument of
  * rtq_gemm_ex and rtq_block_project_ex; rtq_gemm_q4 / _q8 / _f8 and
  * rtq_block_project run RTQ_MATH_SPLIT_BF16). No arithmetic state is kept
- * between calls. Every mode first scales each row of x by the power of two
- * 2^e that puts its largest magnitude in [2^14, 2^15) (exact, as is the
- * scaling back of each output row by 2^-e), so a row's magnitude does not
- * limit the range: codes times scaled activations stay far inside fp32.
+ * between calls.
  *
- * RTQ_MATH_SPLIT_BF16: each scaled activation is split exactly into three
+ * Range. The three split arithmetics form code sums (sum of code*x) before
+ * the scale. Calls that take the pre-pass (M > 32, or any K other than 256,
+ * 512, 1024, 2048) first scale each row of x by the power of two 2^e that puts
+ * its largest magnitude in [2^14, 2^15) (exact, as is the scaling back of each
+ * output row by 2^-e), so rows of any finite magnitude stay far inside fp32.
+ * Calls that take the small-M direct kernel (M <= 32, every K one of 256, 512,
+ * 1024, 2048, int4 pair arrays 16-byte aligned) split x unscaled: results meet
+ * the parity bar for rows whose elements lie in [2^-100, 2^100] in magnitude;
+ * far above that a row's code sums can overflow, and its outputs are then not
+ * finite (never finite and wrong; other rows are unaffected). The fp32-MFMA
+ * arithmetic multiplies the dequantized fp32 weights by x: an fp32 GEMM's
+ * range on every route.
+ *
+ * RTQ_MATH_SPLIT_BF16: each activation (row-scaled where the route scales)
+ *   is split exactly into three
  *   bf16 limbs (v = v1 + v2 + v3, no rounding); the int4/int8 codes and the
  *   E4M3 values are exact in bf16, so every code*limb product is exact in fp32
  *   and the bf16 matrix cores (v_mfma_f32_16x16x32_bf16) accumulate them in
  *   fp32. Per 32-group: y += scale*sum(code*x) + min*sum(x) (int4),
  *   y = scale[o]*sum(q*x) (int8). Same accuracy class as an fp32 GEMM (fp32
- *   accumulation of exact products). The row scale is exact for every element
- *   whose scaled value stays a normal fp32 number (above 2^-126, i.e. more
- *   than 2^-140 of the row's largest magnitude); smaller ones lose low bits,
- *   far below the fp32 accumulation error.
+ *   accumulation of exact products). Where rows are scaled, the scale is
+ *   exact for every element whose scaled value stays a normal fp32 number
+ *   (above 2^-126, i.e. more than 2^-140 of the row's largest magnitude);
+ *   smaller ones lose low bits, far below the fp32 accumulation error.
  * RTQ_MATH_FP32_MFMA: the weights are dequantized to fp32 while staging and the
  *   fp32 matrix cores (v_mfma_f32_16x16x4_f32) run the contraction on the
  *   unscaled x.
  * Both satisfy the same parity bar against the fp64 reference.
- * RTQ_MATH_BF16: bf16 activations. Each scaled x is rounded once to the
+ * RTQ_MATH_BF16: bf16 activations. Each x (row-scaled where the route
+ *   scales) is rounded once to the
  *   nearest bf16 (ties to even) and takes the place of the three limbs:
  *   y = bf16(x) . W^T with the exact weight side and fp32 accumulation of the
  *   first mode, a third of its matrix work (the power-of-two scale does not
  *   change the rounding of a normal-range x). The result carries the rounding
  *   of x (about 2^-9 relative per element), so it is a lower-precision mode.
- * RTQ_MATH_SPLIT_F16: fp32 activations in two fp16 limbs: every scaled value v
- *   is split into h = fp16(v) and l = fp16(v - h), both rounded to nearest:
+ * RTQ_MATH_SPLIT_F16: fp32 activations in two fp16 limbs: every row-scaled
+ *   value v is split into h = fp16(v) and l = fp16(v - h), both rounded to nearest:
  *   h + l carries 22 significant bits of v (relative error at most 2^-22 per
  *   element, plus 2^-25 * 2^-e absolute for elements far below the row's
  *   largest). The fp16 matrix cores (v_mfma_f32_16x16x32_f16) run two limb
@@ -234,6 +247,27 @@ rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64
  * window; later ones are not timed. */
 rtq_status rtq_timing_enable(int32_t on);
 rtq_status rtq_timing_read(double* total_ms, int64_t* launches);
+
+/* Diagnostics: the measured ceilings the kernels are compared with, beside
+ * the published peaks. Both launch on `stream` and are timed by the caller
+ * (events around the call). Neither writes anything the caller reads.
+ *
+ * rtq_diag_stream_read: reads `bytes` (a positive multiple of 16) of the
+ * device buffer `buf` (16-byte aligned) with coalesced 16-byte loads, `unroll`
+ * (4, 8 or 16) loads in flight per lane, over `blocks` workgroups of 256
+ * threads striding over the buffer. `sink` is a device word the kernel writes
+ * only in a case that does not arise (it keeps the loads live).
+ *
+ * rtq_diag_mfma_loop: `blocks` workgroups of four waves, each wave issuing
+ * iters x 8 independent matrix instructions back to back: kind 0
+ * v_mfma_f32_16x16x32_f16, 1 v_mfma_f32_16x16x32_bf16, 2
+ * v_mfma_f32_16x16x4_f32. *flops (if not NULL) receives the floating-point
+ * operations of the launch (2*16*16*32 or 2*16*16*4 per instruction). `sink`
+ * as above. */
+rtq_status rtq_diag_stream_read(const void* buf, int64_t bytes, int32_t unroll, int32_t blocks, uint32_t* sink,
+                                void* stream);
+rtq_status rtq_diag_mfma_loop(int32_t kind, int64_t iters, int32_t blocks, float* sink, double* flops,
+                              void* stream);
 
 const char* rtq_status_string(rtq_status status);
 const char* rtq_last_error(void);   /* thread-local; valid until the next call on this thread */

@@ -42,7 +42,7 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
            "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
            "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_gemm_ex",
-           "rtq_block_project_ex", "rtq_timing_enable",
+           "rtq_block_project_ex", "rtq_diag_stream_read", "rtq_diag_mfma_loop", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 # Arithmetic of a GEMM call (the `math` argument; None runs the library's
@@ -105,6 +105,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtq_gemm_ex.restype = ctypes.c_int
     lib.rtq_block_project_ex.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp]
     lib.rtq_block_project_ex.restype = ctypes.c_int
+    lib.rtq_diag_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
+    lib.rtq_diag_stream_read.restype = ctypes.c_int
+    lib.rtq_diag_mfma_loop.argtypes = [i32, i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.rtq_diag_mfma_loop.restype = ctypes.c_int
     lib.rtq_timing_enable.argtypes = [i32]
     lib.rtq_timing_enable.restype = ctypes.c_int
     lib.rtq_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
@@ -121,6 +125,24 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
 
 def version() -> str:
     return load_library().rtq_version().decode()
+
+
+def diag_stream_read(buf: torch.Tensor, unroll: int = 8, blocks: int = 4096, sink=None, stream=None) -> None:
+    """Streaming read of a whole device tensor (rtq_diag_stream_read)."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.int32, device=buf.device)
+    _check(load_library().rtq_diag_stream_read(_ptr(buf), buf.numel() * buf.element_size(), unroll, blocks,
+                                                _ptr(sink), _stream(stream)))
+
+
+def diag_mfma_loop(kind: int, iters: int, blocks: int = 1024, sink=None, stream=None) -> float:
+    """Back-to-back matrix instructions (rtq_diag_mfma_loop): kind 0 fp16,
+    1 bf16, 2 fp32. Returns the launch's floating-point operations."""
+    if sink is None:
+        sink = torch.zeros(1, dtype=torch.float32, device="cuda")
+    flops = ctypes.c_double(0.0)
+    _check(load_library().rtq_diag_mfma_loop(kind, iters, blocks, _ptr(sink), ctypes.byref(flops), _stream(stream)))
+    return flops.value
 
 
 def timing_enable(on: bool = True) -> None:

@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librtq.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_split.hip", "gemm_direct.hip"]
+SOURCES = ["api.hip", "quant.hip", "gemm.hip", "gemm_split.hip", "gemm_direct.hip", "diag.hip"]
 OBJDIR = os.path.join(PKG, "_build")
 
 FLAGS = [

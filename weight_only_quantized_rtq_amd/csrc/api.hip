@@ -218,11 +218,11 @@ rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y, int64_t M
     return rtq_gemm_ex(RTQ_FMT_F8, x, codes, nullptr, y, M, N, K, RTQ_MATH_SPLIT_BF16, stream);
 }
 
-rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
-    return rtq_block_project_ex(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream);
-}
+namespace {
 
-rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
+// rtq_block_project / _ex: validation, then the grouped launch and the
+// projections the grouped kernels do not take.
+rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
     clear_error();
     if (!math_ok(math)) return fail(RTQ_ERR_FORMAT, "rtq_block_project: unknown arithmetic %d", math);
     if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
@@ -294,6 +294,16 @@ rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64
     return RTQ_OK;
 }
 
+}  // namespace
+
+rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
+    return block_project_impl(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream);
+}
+
+rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
+    return block_project_impl(blocks, n_blocks, M, math, stream);
+}
+
 rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N, int64_t K,
                           void* stream) {
     clear_error();
@@ -358,6 +368,33 @@ rtq_status rtq_quantize_f8(const float* w, uint8_t* codes, int64_t N, int64_t K,
         return fail(RTQ_ERR_OVERLAP, "rtq_quantize_f8: output overlaps the weights");
     return hip_status(rtq::launch_quantize_f8(w, codes, N, K, static_cast<hipStream_t>(stream)),
                       "rtq_quantize_f8 launch");
+}
+
+// ---- diagnostics: measured ceilings ----
+rtq_status rtq_diag_stream_read(const void* buf, int64_t bytes, int32_t unroll, int32_t blocks, uint32_t* sink,
+                                void* stream) {
+    clear_error();
+    if (!buf || !sink) return fail(RTQ_ERR_NULL, "rtq_diag_stream_read: a pointer argument is NULL");
+    if (bytes < 16 || bytes % 16 != 0 || bytes > (kMaxElems << 2))
+        return fail(RTQ_ERR_SHAPE, "rtq_diag_stream_read: bytes=%lld is not a positive multiple of 16", (long long)bytes);
+    if (unroll != 4 && unroll != 8 && unroll != 16)
+        return fail(RTQ_ERR_SHAPE, "rtq_diag_stream_read: unroll=%d is not 4, 8 or 16", unroll);
+    if (blocks < 1 || blocks > (1 << 20)) return fail(RTQ_ERR_SHAPE, "rtq_diag_stream_read: blocks=%d out of range", blocks);
+    if (!aligned(buf, 16) || !aligned(sink, 4)) return fail(RTQ_ERR_ALIGN, "rtq_diag_stream_read: misaligned pointer");
+    return hip_status(rtq::launch_stream_read(buf, bytes, unroll, blocks, sink, static_cast<hipStream_t>(stream)),
+                      "rtq_diag_stream_read launch");
+}
+
+rtq_status rtq_diag_mfma_loop(int32_t kind, int64_t iters, int32_t blocks, float* sink, double* flops, void* stream) {
+    clear_error();
+    if (kind < 0 || kind > 2) return fail(RTQ_ERR_FORMAT, "rtq_diag_mfma_loop: unknown kind %d", kind);
+    if (!sink) return fail(RTQ_ERR_NULL, "rtq_diag_mfma_loop: sink is NULL");
+    if (iters < 1 || iters > (int64_t(1) << 31)) return fail(RTQ_ERR_SHAPE, "rtq_diag_mfma_loop: iters out of range");
+    if (blocks < 1 || blocks > (1 << 20)) return fail(RTQ_ERR_SHAPE, "rtq_diag_mfma_loop: blocks=%d out of range", blocks);
+    if (!aligned(sink, 4)) return fail(RTQ_ERR_ALIGN, "rtq_diag_mfma_loop: misaligned sink");
+    if (flops) *flops = double(blocks) * 4.0 * double(iters) * 8.0 * (kind == 2 ? 2.0 * 16 * 16 * 4 : 2.0 * 16 * 16 * 32);
+    return hip_status(rtq::launch_mfma_loop(kind, iters, blocks, sink, static_cast<hipStream_t>(stream)),
+                      "rtq_diag_mfma_loop launch");
 }
 
 // ---- host quantizers: host pointers, no HIP call ----

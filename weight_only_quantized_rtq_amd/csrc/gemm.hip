@@ -2,9 +2,9 @@
 //
 // The packed weights are streamed once per output tile, unpacked and
 // dequantized in registers while the tile is staged into LDS (int4: code*s+m
-// with the group's fp16 pair; int8: the integer itself, the row scale being
-// applied once in the epilogue since it factors out of the K sum; FP8: the
-// E4M3 value), and the contraction runs on the fp32 MFMA
+// with the group's fp16 pair; int8: code*scale[row], the single-rounded fp32
+// product, so no sum is formed before the scale and the range is that of an
+// fp32 GEMM; FP8: the E4M3 value), and the contraction runs on the fp32 MFMA
 // (v_mfma_f32_16x16x4_f32) with fp32 accumulators. The formats are those of
 // the RT-J int4 / int8 model cards, section "Quantization format", and of the
 // FP8 card, section "FP8 Format"; the dequantize-inside-the-GEMM design is the
@@ -74,6 +74,8 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, flo
     const int wr = tid >> 1;        // W tile row staged by this thread
     const int wh = tid & 1;         // which 16 of the 32 k
     const int wrow = n0 + wr;
+    // int8 row scale of the staged W row (multiplied into every code)
+    const float wscale = FMT == kFmtQ8 && wrow < N ? static_cast<const float*>(a.scale)[wrow] : 1.0f;
     uint2 q4bits = make_uint2(0, 0);
     uint32_t q4pair = 0;
     uint4 q8bits = make_uint4(0, 0, 0, 0);
@@ -149,12 +151,14 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, flo
             }
         } else if constexpr (SAFE) {
 #pragma unroll
-            for (int j = 0; j < 16; ++j) wv[j] = wsafe[j];
+            for (int j = 0; j < 16; ++j) wv[j] = FMT == kFmtQ8 ? wsafe[j] * wscale : wsafe[j];
         } else {
             const uint32_t words[4] = {q8bits.x, q8bits.y, q8bits.z, q8bits.w};
 #pragma unroll
-            for (int j = 0; j < 16; ++j)
-                wv[j] = code8_value<FMT>(words[j >> 2] >> (8 * (j & 3)));
+            for (int j = 0; j < 16; ++j) {
+                const float c = code8_value<FMT>(words[j >> 2] >> (8 * (j & 3)));
+                wv[j] = FMT == kFmtQ8 ? c * wscale : c;
+            }
         }
         float* wd = ws[buf] + wr * kLD + wh * 16;
 #pragma unroll
@@ -219,17 +223,13 @@ __device__ __forceinline__ void gemm_tile(const TileArgs& a, int mt, int nt, flo
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + wn * TN * 16 + tn * 16 + li;
         if (col >= N) continue;
-        float sc = 1.0f;
-        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = m0 + wm * TM * 16 + tm * 16 + 4 * (lane >> 4) + r;
                 if (row < M) {
-                    float v = acc[tm][tn][r];
-                    if constexpr (FMT == kFmtQ8) v *= sc;
-                    a.y[static_cast<int64_t>(row) * N + col] = v;
+                    a.y[static_cast<int64_t>(row) * N + col] = acc[tm][tn][r];
                 }
             }
         }
@@ -295,9 +295,11 @@ __device__ __forceinline__ void stream_tile(const TileArgs& a, int slice, int n_
         }
         const uint8_t* wp[TN];
         const uint32_t* pp[TN];
+        float qsc[TN];                          // int8 row scale of the lane's W row
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             const int col = min(n0 + tn * 16 + li, N - 1);
+            qsc[tn] = FMT == kFmtQ8 ? static_cast<const float*>(a.scale)[col] : 1.0f;
             if constexpr (FMT == kFmtQ4) {
                 wp[tn] = static_cast<const uint8_t*>(a.payload) + static_cast<int64_t>(col) * (K / 2);
                 pp[tn] = static_cast<const uint32_t*>(a.scale) + static_cast<int64_t>(col) * G;
@@ -364,6 +366,8 @@ __device__ __forceinline__ void stream_tile(const TileArgs& a, int slice, int n_
                 for (int tn = 0; tn < TN; ++tn) {
                     if constexpr (FMT == kFmtQ4) {
                         b[tn] = fmaf(static_cast<float>(nibble(wd[tn][step >> 3], step & 7)), s[tn], m[tn]);
+                    } else if constexpr (FMT == kFmtQ8) {
+                        b[tn] = code8_value<FMT>(wd[tn][step >> 2] >> (8 * (step & 3))) * qsc[tn];
                     } else {
                         b[tn] = code8_value<FMT>(wd[tn][step >> 2] >> (8 * (step & 3)));
                     }
@@ -428,17 +432,13 @@ __device__ __forceinline__ void stream_tile(const TileArgs& a, int slice, int n_
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + tn * 16 + li;
         if (col >= N) continue;
-        float sc = 1.0f;
-        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int row = tm * 16 + 4 * lc + r;
                 if (row < M) {
-                    float v = acc[tm][tn][r];
-                    if constexpr (FMT == kFmtQ8) v *= sc;
-                    a.y[static_cast<int64_t>(row) * N + col] = v;
+                    a.y[static_cast<int64_t>(row) * N + col] = acc[tm][tn][r];
                 }
             }
         }

@@ -27,11 +27,6 @@
 //    16lc.. and 64 + 16lc.. of the block and the MFMAs contract k in that
 //    order; x is read from the matching places, so no exchange is needed.
 //  - the codes of a group are converted to bf16 once and serve all TM row tiles.
-//  - row scale: before the first phase the workgroup reads its rows of x once
-//    for their largest magnitudes and scales row r by the power of two 2^e_r
-//    that puts that magnitude in [2^14, 2^15) while staging; every output row
-//    is scaled back by 2^-e_r (exact) after the int8 scale, so the code sums
-//    stay inside the fp32 range whatever the magnitude of the row.
 // The K loop is unrolled completely (K fixed per instantiation), so the
 // compiler tracks every load and waits only for the group it uses; the x reads
 // of the next row tile or group are issued before the MFMAs of the current one.
@@ -79,8 +74,7 @@ struct DirectLds {
     static constexpr int GBYTES = TM * NL * 1024;       // one group: TM row tiles x NL limbs of 1 KB
     static constexpr int XBUF = PG * GBYTES;            // one phase
     static constexpr int SUMS = kSumSlots * 16 * TM * 4;
-    static constexpr int RMAX = 2 * XBUF + SUMS;         // largest magnitude of each row (fp32 bits)
-    static constexpr int XTOTAL = RMAX + 16 * TM * 4;
+    static constexpr int XTOTAL = 2 * XBUF + SUMS;
     // per-wave int4 staging: 16 rows of 4 x 16 bytes of codes (+ 16 bytes of
     // padding); two areas, used by alternate column tiles
     static constexpr int STG_ROW = 80;
@@ -123,9 +117,6 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
             if (t < nrows)
                 xr[t] = *reinterpret_cast<const float2*>(xcol + static_cast<int64_t>(RS * t) * K + ph * (PG * 32));
     };
-    // Row scale: row r is multiplied by 2^rexp[t] (r = xh + RS*t), which puts
-    // its largest magnitude in [2^14, 2^15); the outputs are scaled back.
-    int rexp[NR];
     auto x_convert = [&](int ph) {
         unsigned char* buf = smem + (ph & 1) * L::XBUF + xj * L::GBYTES + (kp & 3) * 4;
         float* sums = reinterpret_cast<float*>(smem + 2 * L::XBUF) + ((ph * PG + xj) % kSumSlots) * (16 * TM);
@@ -133,7 +124,7 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
         for (int t = 0; t < NR; ++t) {
             if (t >= nrows) break;
             const int r = xh + RS * t;
-            float v0 = ldexpf(xr[t].x, rexp[t]), v1 = ldexpf(xr[t].y, rexp[t]);
+            float v0 = xr[t].x, v1 = xr[t].y;
             unsigned char* blk = buf + (r >> 4) * (NL * 1024) + swz(r & 15, kp >> 2) * 16;
             if constexpr (NL == 3) {
                 uint32_t h, m, l;
@@ -346,43 +337,6 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
         for (int t = tid; t < L::XTOTAL / 16; t += 256) z[t] = make_uint4(0u, 0u, 0u, 0u);
     }
     lds_barrier();
-    // ---- row maxima over the whole K: every phase of this thread's rows,
-    //      reduced over the 16 lanes of a DPP row, then across the phase's
-    //      groups with an LDS max on the fp32 bits (non-negative floats order
-    //      like their bit patterns) ----
-    {
-        float mx[NR];
-#pragma unroll
-        for (int t = 0; t < NR; ++t) mx[t] = 0.0f;
-        static_for<0, NPH>([&](auto pc) {
-            constexpr int ph = decltype(pc)::value;
-#pragma unroll
-            for (int t = 0; t < NR; ++t)
-                if (t < nrows) {
-                    const float2 v = *reinterpret_cast<const float2*>(xcol + static_cast<int64_t>(RS * t) * K + ph * (PG * 32));
-                    mx[t] = fmaxf(mx[t], fmaxf(fabsf(v.x), fabsf(v.y)));
-                }
-        });
-        unsigned int* rmax = reinterpret_cast<unsigned int*>(smem + L::RMAX);
-#pragma unroll
-        for (int t = 0; t < NR; ++t) {
-            if (t >= nrows) break;
-            float m = mx[t];
-            m = fmaxf(m, row_ror<8>(m));
-            m = fmaxf(m, row_ror<4>(m));
-            m = fmaxf(m, row_ror<2>(m));
-            m = fmaxf(m, row_ror<1>(m));
-            if (kp == 0) atomicMax(rmax + xh + RS * t, fbits(m));
-        }
-    }
-    lds_barrier();
-#pragma unroll
-    for (int t = 0; t < NR; ++t) {
-        int E = 0;
-        const int r = min(xh + RS * t, 16 * TM - 1);
-        (void)frexpf(bitsf(reinterpret_cast<const unsigned int*>(smem + L::RMAX)[r]), &E);
-        rexp[t] = 15 - E;
-    }
     x_load(0);
     pairs_issue();
 #pragma unroll
@@ -447,17 +401,7 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
         }
     });
 
-    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile; each row
-    //      is scaled back by 2^-e (exact) after the int8 scale ----
-    int oexp[TM][4];
-#pragma unroll
-    for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            int E = 0;
-            (void)frexpf(bitsf(reinterpret_cast<const unsigned int*>(smem + L::RMAX)[16 * tm + 4 * lc + e]), &E);
-            oexp[tm][e] = E - 15;
-        }
+    // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile ----
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + wave * TN * 16 + tn * 16 + li;
@@ -476,7 +420,7 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
                 if (row < M) {
                     float v = acc[tm][tn][0][e];
                     if constexpr (FMT == kFmtQ8) v *= s;
-                    y[static_cast<int64_t>(row) * N + col] = ldexpf(v, oexp[tm][e]);
+                    y[static_cast<int64_t>(row) * N + col] = v;
                 }
             }
         }

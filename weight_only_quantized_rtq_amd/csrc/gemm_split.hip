@@ -866,61 +866,99 @@ void launch_large(int fmt, int blocks, const SplitArgs& a, int tn, hipStream_t s
         split_gemm_kernel<kFmtF8, NL><<<blocks, 256, 0, stream>>>(a, tn);
 }
 
+namespace {
+
+// Workspace layout of a split call (no direct kernel): one limb image per
+// distinct (x, K), then the K-chunk partials of the grouped launch.
+struct SplitPlan {
+    bool small = false;     // grouped small-M launch (else one tiled launch per projection)
+    int RB = 0;             // 16-row blocks of every image
+    int n_in = 0;
+    Input inputs[8 * 64];
+    int img_of[8 * 64];
+    int64_t part_off[8 * 64];
+    int64_t ws_bytes = 0;
+};
+
+void plan_split(const ProjTask* tasks, int count, int M, int NL, SplitPlan& p) {
+    const int tm_small = static_cast<int>((int64_t(M) + 15) / 16);
+    // The grouped small-M launch addresses the limb images by 32-bit offsets;
+    // a call whose images would not fit (enormous K) takes the tiled path.
+    p.small = M <= 80;
+    for (;;) {
+        p.RB = p.small ? tm_small : static_cast<int>((int64_t(M) + kLBM - 1) / kLBM) * (kLBM / 16);
+        // Distinct inputs (pointer, K).
+        p.n_in = 0;
+        p.ws_bytes = 0;
+        for (int i = 0; i < count; ++i) {
+            int found = -1;
+            for (int j = 0; j < p.n_in; ++j)
+                if (p.inputs[j].x == tasks[i].x && p.inputs[j].K == tasks[i].K) found = j;
+            if (found < 0) {
+                found = p.n_in++;
+                p.inputs[found] = Input{tasks[i].x, tasks[i].K, p.ws_bytes};
+                p.ws_bytes += (image_bytes(tasks[i].K / 32, p.RB, NL) + 255) / 256 * 256;
+            }
+            p.img_of[i] = found;
+        }
+        if (!p.small || p.ws_bytes <= int64_t(UINT32_MAX)) break;
+        p.small = false;
+    }
+    for (int i = 0; i < count; ++i) {
+        p.part_off[i] = -1;
+        const int ks = split_chunks(tasks[i].K);
+        if (p.small && ks > 1) {
+            p.part_off[i] = p.ws_bytes;
+            p.ws_bytes += (int64_t(ks) * M * tasks[i].N * 4 + 255) / 256 * 256;
+        }
+    }
+}
+
+}  // namespace
+
+int64_t split_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int NL) {
+    if (count == 0 || direct_fits(tasks, count, M)) return 0;
+    thread_local SplitPlan plan;
+    plan_split(tasks, count, static_cast<int>(M), NL, plan);
+    return plan.ws_bytes;
+}
+
+namespace {
+
 // All projections (sharing M) of this call: split every distinct input once into
-// a stream-ordered workspace, run the GEMMs, release the workspace. NL = 3:
-// exact three-limb split; NL = 2: two fp16 limbs of the row-scaled x; NL = 1:
-// x rounded to bf16. The direct small-M kernel splits x itself and has no
-// row scale: with NL = 2 it runs the exact three-limb split.
-hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream) {
+// a workspace, run the GEMMs. The workspace is ext_ws (ext_cap bytes) when
+// given, else a stream-ordered allocation from the library's pool, returned
+// at the end. NL = 3: exact three-limb split; NL = 2: two fp16 limbs of the
+// row-scaled x; NL = 1: x rounded to bf16. The direct small-M kernel splits x
+// itself and has no row scale: with NL = 2 it runs the exact three-limb split.
+hipError_t split_impl(const ProjTask* tasks, int count, int64_t M64, int NL, hipStream_t stream,
+                      unsigned char* ext_ws, int64_t ext_cap) {
     if (NL < 1 || NL > 3) return hipErrorInvalidValue;
     const int M = static_cast<int>(M64);
     if (direct_fits(tasks, count, M)) return launch_direct(tasks, count, M, NL == 2 ? 3 : NL, stream);
     const int tm_small = static_cast<int>((int64_t(M) + 15) / 16);
-    // The grouped small-M launch addresses the limb images by 32-bit offsets;
-    // a call whose images would not fit (enormous K) takes the tiled path.
-    bool small = M <= 80;
-    int RB = 0;
-    Input inputs[8 * 64];
-    int img_of[8 * 64];
-    int n_in = 0;
-    int64_t ws_bytes = 0;
-    for (;;) {
-        RB = small ? tm_small : static_cast<int>((int64_t(M) + kLBM - 1) / kLBM) * (kLBM / 16);
-        // Distinct inputs (pointer, K).
-        n_in = 0;
-        ws_bytes = 0;
-        for (int i = 0; i < count; ++i) {
-            int found = -1;
-            for (int j = 0; j < n_in; ++j)
-                if (inputs[j].x == tasks[i].x && inputs[j].K == tasks[i].K) found = j;
-            if (found < 0) {
-                found = n_in++;
-                inputs[found] = Input{tasks[i].x, tasks[i].K, ws_bytes};
-                ws_bytes += (image_bytes(tasks[i].K / 32, RB, NL) + 255) / 256 * 256;
-            }
-            img_of[i] = found;
-        }
-        if (!small || ws_bytes <= int64_t(UINT32_MAX)) break;
-        small = false;
+    thread_local SplitPlan plan;
+    plan_split(tasks, count, M, NL, plan);
+    const bool small = plan.small;
+    const int RB = plan.RB;
+    const Input* inputs = plan.inputs;
+    const int* img_of = plan.img_of;
+    const int64_t* part_off = plan.part_off;
+    const int64_t ws_bytes = plan.ws_bytes;
+    void* ws = ext_ws;
+    hipError_t e = hipSuccess;
+    if (ext_ws) {
+        if (ws_bytes > ext_cap) return hipErrorOutOfMemory;
+    } else {
+        int device = 0;
+        e = hipGetDevice(&device);
+        hipMemPool_t pool = nullptr;
+        if (e == hipSuccess) e = library_pool(device, &pool);
+        if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(ws_bytes), pool, stream);
+        if (e != hipSuccess) return e;
     }
-    int64_t part_off[8 * 64];
-    for (int i = 0; i < count; ++i) {
-        part_off[i] = -1;
-        const int ks = split_chunks(tasks[i].K);
-        if (small && ks > 1) {
-            part_off[i] = ws_bytes;
-            ws_bytes += (int64_t(ks) * M * tasks[i].N * 4 + 255) / 256 * 256;
-        }
-    }
-    int device = 0;
-    hipError_t e = hipGetDevice(&device);
-    hipMemPool_t pool = nullptr;
-    if (e == hipSuccess) e = library_pool(device, &pool);
-    void* ws = nullptr;
-    if (e == hipSuccess) e = hipMallocFromPoolAsync(&ws, static_cast<size_t>(ws_bytes), pool, stream);
-    if (e != hipSuccess) return e;
     unsigned char* wsb = static_cast<unsigned char*>(ws);
-    e = run_prep(inputs, n_in, wsb, M, RB, NL, stream);
+    e = run_prep(inputs, plan.n_in, wsb, M, RB, NL, stream);
 
     if (e == hipSuccess && small) {
         int order[8 * 64];
@@ -1000,8 +1038,15 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M64, int NL, h
             e = hipGetLastError();
         }
     }
+    if (ext_ws) return e;
     const hipError_t f = hipFreeAsync(ws, stream);
     return e != hipSuccess ? e : f;
+}
+
+}  // namespace
+
+hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream) {
+    return split_impl(tasks, count, M, NL, stream, nullptr, 0);
 }
 
 hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {

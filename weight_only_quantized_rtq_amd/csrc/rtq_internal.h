@@ -57,6 +57,10 @@ bool grouped_ok(const ProjTask& task);
 // split_ok(). Uses a stream-ordered workspace (hipMallocAsync).
 bool split_ok(const ProjTask& task);
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
+// Workspace bytes launch_split needs for these tasks (0 when they take the
+// direct small-M kernel).
+int64_t split_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int NL);
+
 
 // Small-M path of the split arithmetic (gemm_direct.hip): one launch, whole K
 // per workgroup, x split in the kernel. direct_fits(): M in 1..32, every K in
@@ -74,5 +78,10 @@ void quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64_t K, int 
 // y += bias (broadcast over the M rows) for every task that has a bias, in
 // place, after the GEMM kernels that wrote y (same stream).
 hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream);
+
+// Diagnostics (diag.hip): measured ceilings.
+hipError_t launch_stream_read(const void* buf, int64_t bytes, int unroll, int blocks, uint32_t* sink,
+                              hipStream_t stream);
+hipError_t launch_mfma_loop(int kind, int64_t iters, int blocks, float* sink, hipStream_t stream);
 
 }  // namespace rtq
