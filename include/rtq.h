@@ -238,6 +238,24 @@ rtq_status rtq_gemm_ex(int32_t fmt, const float* x, const void* payload, const v
 rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
                                 void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * rtq_block_project_ex that allocates nothing. Where the split path needs a
+ * workspace (limb images of x and K-chunk partials: M above 32, or a K other
+ * than 256, 512, 1024, 2048) it uses a fixed 32 MiB device array of the
+ * library instead of its memory pool; each GPU the library runs on holds its
+ * own copy of that array until the process ends. The call makes no
+ * hipMalloc / hipFree or other allocating call. A call whose workspace would
+ * exceed 32 MiB returns RTQ_ERR_SHAPE and launches nothing (the 12-block RT-J
+ * projection set at M = 80 needs 22.1 MB with two fp16 limbs, 29.0 MB with
+ * the exact split, 15.2 MB with bf16 activations). Every call on one GPU shares that GPU's array, which keeps the
+ * last call's contents (each call writes all of what it reads): calls that
+ * overlap in time on one GPU (different streams, or different host threads)
+ * race on it and must be ordered by the caller. Results are those of
+ * rtq_block_project_ex, bit for bit. */
+rtq_status rtq_block_project_noalloc(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
+                                     void* stream);
+
 /* Kernel timing (profiling aid). While enabled, every main GEMM kernel launch
  * of the entry points above is bracketed by a pair of HIP events recorded on
  * its stream (events are created on first use and kept for reuse). Enabling

@@ -42,7 +42,7 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
            "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
            "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_gemm_ex",
-           "rtq_block_project_ex", "rtq_diag_stream_read", "rtq_diag_mfma_loop", "rtq_timing_enable",
+           "rtq_block_project_ex", "rtq_block_project_noalloc", "rtq_diag_stream_read", "rtq_diag_mfma_loop", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 # Arithmetic of a GEMM call (the `math` argument; None runs the library's
@@ -105,6 +105,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtq_gemm_ex.restype = ctypes.c_int
     lib.rtq_block_project_ex.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp]
     lib.rtq_block_project_ex.restype = ctypes.c_int
+    lib.rtq_block_project_noalloc.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp]
+    lib.rtq_block_project_noalloc.restype = ctypes.c_int
     lib.rtq_diag_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.rtq_diag_stream_read.restype = ctypes.c_int
     lib.rtq_diag_mfma_loop.argtypes = [i32, i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]

@@ -220,9 +220,11 @@ rtq_status rtq_gemm_f8(const float* x, const uint8_t* codes, float* y, int64_t M
 
 namespace {
 
-// rtq_block_project / _ex: validation, then the grouped launch and the
-// projections the grouped kernels do not take.
-rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
+// rtq_block_project / _ex / _noalloc: validation, then the grouped launch and
+// the projections the grouped kernels do not take. With no_alloc the split
+// path's workspace is the library's fixed scratch array.
+rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream,
+                              bool no_alloc) {
     clear_error();
     if (!math_ok(math)) return fail(RTQ_ERR_FORMAT, "rtq_block_project: unknown arithmetic %d", math);
     if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
@@ -281,10 +283,18 @@ rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t
             return fail(RTQ_ERR_OVERLAP, "rtq_block_project: an output overlaps a projection's input");
     }
     if (M == 0) return RTQ_OK;
+    if (no_alloc && n_grouped) {
+        const int64_t need = rtq::grouped_workspace_bytes(grouped, n_grouped, M, math);
+        if (need < 0 || need > rtq::kScratchBytes)
+            return fail(RTQ_ERR_SHAPE,
+                        "rtq_block_project_noalloc: the call needs %lld bytes of workspace, more than the %lld-byte "
+                        "scratch of the allocation-free entry point",
+                        (long long)need, (long long)rtq::kScratchBytes);
+    }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (n_grouped) {
         const rtq_status s =
-            hip_status(rtq::launch_grouped(grouped, n_grouped, M, math, st), "rtq_block_project launch");
+            hip_status(rtq::launch_grouped(grouped, n_grouped, M, math, st, no_alloc), "rtq_block_project launch");
         if (s != RTQ_OK) return s;
     }
     for (int i = 0; i < n_single; ++i) {
@@ -297,11 +307,16 @@ rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t
 }  // namespace
 
 rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
-    return block_project_impl(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream);
+    return block_project_impl(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream, false);
 }
 
 rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
-    return block_project_impl(blocks, n_blocks, M, math, stream);
+    return block_project_impl(blocks, n_blocks, M, math, stream, false);
+}
+
+rtq_status rtq_block_project_noalloc(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
+                                     void* stream) {
+    return block_project_impl(blocks, n_blocks, M, math, stream, true);
 }
 
 rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N, int64_t K,

@@ -634,7 +634,18 @@ hipError_t launch_grouped_fp32_bias(const ProjTask* tasks, int count, int64_t M,
     return e == hipSuccess ? launch_bias_add(tasks, count, M, stream) : e;
 }
 
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream) {
+int64_t grouped_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int math) {
+    const int nl = split_limbs(math);
+    if (!nl) return 0;
+    thread_local std::vector<ProjTask> split_buf(8 * 64);
+    if (count > static_cast<int>(split_buf.size())) return -1;
+    int n_split = 0;
+    for (int i = 0; i < count; ++i)
+        if (split_ok(tasks[i])) split_buf[n_split++] = tasks[i];
+    return split_workspace_bytes(split_buf.data(), n_split, M, nl);
+}
+
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream, bool no_alloc) {
     const int nl = split_limbs(math);
     if (!nl) return launch_grouped_fp32_bias(tasks, count, M, stream);
     // Split path for every task it takes; the rest (weights past 32-bit
@@ -649,7 +660,8 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math,
         else rest[n_rest++] = tasks[i];
     }
     if (n_split) {
-        const hipError_t e = launch_split(split, n_split, M, nl, stream);
+        const hipError_t e = no_alloc ? launch_split_scratch(split, n_split, M, nl, stream)
+                                      : launch_split(split, n_split, M, nl, stream);
         if (e != hipSuccess) return e;
     }
     return n_rest ? launch_grouped_fp32_bias(rest, n_rest, M, stream) : hipSuccess;

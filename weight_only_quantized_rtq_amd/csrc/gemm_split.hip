@@ -1049,6 +1049,42 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hip
     return split_impl(tasks, count, M, NL, stream, nullptr, 0);
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free variant: the workspace is `scratch`, a fixed device array of
+// the library (one copy per device, each GPU the library runs on holding it
+// for the life of the process). Host code never passes the array's name to a
+// kernel: its device address is resolved once per device, with that device
+// current, and kept.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+hipError_t scratch_address(unsigned char** out) {
+    static std::mutex mu;
+    static unsigned char* addr[64] = {};
+    int device = 0;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[device]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[device] = static_cast<unsigned char*>(p);
+    }
+    *out = addr[device];
+    return hipSuccess;
+}
+
+hipError_t launch_split_scratch(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream) {
+    unsigned char* ws = nullptr;
+    if (split_workspace_bytes(tasks, count, M, NL) > 0) {
+        const hipError_t e = scratch_address(&ws);
+        if (e != hipSuccess) return e;
+    }
+    return split_impl(tasks, count, M, NL, stream, ws, kScratchBytes);
+}
+
 hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
     FinishArgs r{};
     int blocks = 0;

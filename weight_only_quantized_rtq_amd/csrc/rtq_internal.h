@@ -48,8 +48,11 @@ hipError_t launch_gemm(const ProjTask& task, int64_t M, int math, hipStream_t st
 
 // Several projections sharing M, in grouped launches. Every task must satisfy
 // grouped_ok().
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream);
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream,
+                          bool no_alloc = false);
 bool grouped_ok(const ProjTask& task);
+// Workspace bytes launch_grouped needs for these tasks in arithmetic `math`.
+int64_t grouped_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int math);
 
 // Split-limb path (gemm_split.hip): every projection of the call, sharing M,
 // with NL = 3 bf16 limbs (exact), 2 fp16 limbs of the row-scaled x, or 1 (x
@@ -60,7 +63,12 @@ hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hip
 // Workspace bytes launch_split needs for these tasks (0 when they take the
 // direct small-M kernel).
 int64_t split_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int NL);
-
+// launch_split with the library's fixed per-device scratch array as the
+// workspace instead of an allocation (rtq_block_project_noalloc); returns
+// hipErrorOutOfMemory, launching nothing, if the call needs more than
+// kScratchBytes.
+constexpr int64_t kScratchBytes = int64_t(32) << 20;
+hipError_t launch_split_scratch(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
 
 // Small-M path of the split arithmetic (gemm_direct.hip): one launch, whole K
 // per workgroup, x split in the kernel. direct_fits(): M in 1..32, every K in
