@@ -512,12 +512,17 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             const int ic = (i & ~3) + lc;                 // this lane group's step
             const bool live = ic <= i;
             const float* ring = reinterpret_cast<const float*>(smem + L::XRING) + (ic % kRing) * L::XSLOT;
+            // every row tile's sums read first (one wait for all), then zeroed
+            // for a lane group past the last step (its slot holds no sum of this tile)
+            float xv[TM];
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) xv[tm] = ring[wm * TM * 16 + tm * 16 + li];
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
-                const float xv = live ? ring[wm * TM * 16 + tm * 16 + li] : 0.0f;
+                const float xs = live ? xv[tm] : 0.0f;
 #pragma unroll
                 for (int tn = 0; tn < TN; ++tn)
-                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xv, mreg[tn], acc[tm][tn], 0, 0, 0);
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(xs, mreg[tn], acc[tm][tn], 0, 0, 0);
             }
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) mreg[tn] = 0.0f;
