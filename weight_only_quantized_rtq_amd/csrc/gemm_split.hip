@@ -292,7 +292,13 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
 // step ahead (enough when they come from L2), and the x stages run one step
 // ahead; with WL > 0 the weights are copied by DMA into a per-wave LDS ring WL
 // chunks ahead (for weights streamed from HBM) and the x stages XL steps ahead.
-template <int FMT, int WM, int WN, int TM, int TN, int XL, int WL, int NL>
+//
+// STREAM_Y: store y with nontemporal stores. The large-M tiles write hundreds
+// of MB per launch that nothing in the launch reads again; kept in L2 they
+// only evict the limb images that the other column tiles still read. The
+// grouped kernel's K-chunk partials are read by the finish pass right after,
+// so it keeps ordinary stores.
+template <int FMT, int WM, int WN, int TM, int TN, int XL, int WL, int NL, bool STREAM_Y = false>
 __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, int rot, unsigned char* smem) {
     constexpr int BM = WM * TM * 16;
     constexpr int NW = WM * WN;                                   // waves of the workgroup
@@ -626,7 +632,9 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                     if constexpr (FMT == kFmtQ8) v *= sc;
                     v = ldexpf(v, rexp[tm][e]);
                     if (a.bias) v += bv;
-                    a.y[static_cast<int64_t>(row) * N + col] = v;
+                    float* dst = a.y + static_cast<int64_t>(row) * N + col;
+                    if constexpr (STREAM_Y) __builtin_nontemporal_store(v, dst);
+                    else *dst = v;
                 }
             }
         }
@@ -650,7 +658,7 @@ __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, WL ? kLTN : 1, XL, WL, NL>::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int nt = w % tiles_n;
-    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, XL, WL, NL>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
+    split_tile<FMT, kLWM, kLWN, kLTM, kLTN, XL, WL, NL, true>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
 }
 
 // Small M (<= 80): one row block of TM*16 rows and 256 columns per workgroup,
