@@ -8,7 +8,8 @@ what is particular to it, against the CPU oracle (fp64) on the same seeded
 inputs:
   * rows of very different magnitude in one call, each scaled on its own:
     every row meets the bar by itself;
-  * rows longer than the pre-pass keeps in registers (read twice);
+  * rows of one to seventeen 512-wide pieces, and rows longer than the
+    pre-pass keeps in registers (read twice);
   * a non-finite row stays in its row;
   * the small-M direct kernel runs the exact three-limb split in this mode;
   * on random data the 22-bit representation keeps the error near the fp32
@@ -81,10 +82,13 @@ def test_rows_of_any_magnitude_each_meet_the_bar(fmt, M, N, K):
 
 
 @pytest.mark.parametrize("fmt,M,N,K", [("q4", 40, 64, 4096), ("q8", 40, 64, 2080), ("f8", 150, 64, 4096),
-                                       ("q4", 150, 96, 2080), ("q4", 33, 32, 32)])
+                                       ("q4", 150, 96, 2080), ("q4", 33, 32, 32), ("q8", 40, 32, 1536),
+                                       ("f8", 200, 48, 1056), ("q4", 48, 32, 8320)])
 def test_long_and_short_rows(fmt, M, N, K):
-    """K above the pre-pass's register hold (2048: rows read twice), a last
-    512-wide piece cut short (2080), and a single group (32)."""
+    """Rows of the pre-pass (one wave per row, 512-wide pieces): a single
+    group (32), three pieces (1536), a last piece of one group (1056) or cut
+    short (2080), rows above the four pieces it keeps in registers, read
+    twice (4096, and 8320 with a seventeenth piece)."""
     say(f"long rows {fmt} M={M} N={N} K={K}")
     W = synth.weight(42, 0, 0, "w1", N, K)
     ref = oracle.quantize(W, fmt)

@@ -278,6 +278,109 @@ __device__ __forceinline__ void dma4(const void* src, void* lds_base) {
                                      (__attribute__((address_space(3))) void*)lds_base, 4, 0, 0);
 }
 
+// DMA schedule of the x stages and weight chunks when the weights stream
+// through LDS (XL, WL >= 1): NX ops per x stage and NWC per weight chunk (per
+// wave); stage s lands in slot s % (XL + 1), chunk c (steps 2c, 2c + 1) in slot
+// c % (WL + 1).
+//  - Before the loop every slot is free: stages 0..XL and chunks 0..WL are
+//    issued in the order of the step that first needs them (a chunk before the
+//    stage of the same step).
+//  - Iteration j >= 1 issues stage j + XL after its barrier, then, for even
+//    j >= 2, chunk j/2 + WL: the earliest iteration whose barrier follows
+//    every wave's last read of the slot's previous occupant.
+//  - At the top of iteration i a wave waits until at most allowed(i, GS) of
+//    its ops are in flight: the ops issued after step i's stage and chunk
+//    (loads complete in order). A chunk issued one step ahead of the step
+//    before it is needed therefore stays in flight across that step.
+// verify() replays the schedule for every chunk length up to 48 with an
+// in-order completion model and checks that what each step reads has landed,
+// that allowed() leaves exactly the ops issued after it in flight (no stricter
+// wait), that each slot holds what its step reads, that no slot is refilled
+// before the barrier after its last read, and that nothing is left in flight
+// at the end.
+template <int XL, int WL, int NX, int NWC>
+struct DmaSchedule {
+    __host__ __device__ static constexpr int stage_iter(int s) { return s <= XL ? -1 : s - XL; }
+    __host__ __device__ static constexpr int chunk_iter(int c) { return c <= WL ? -1 : 2 * c - 2 * WL; }
+    // position in the issue order
+    __host__ __device__ static constexpr int stage_key(int s) { return s <= XL ? 2 * s + 1 : 4096 + 2 * (s - XL); }
+    __host__ __device__ static constexpr int chunk_key(int c) { return c <= WL ? 4 * c : 4096 + 2 * (2 * c - 2 * WL) + 1; }
+    static constexpr int kMax = XL * NX + (WL + 1) * NWC;
+    static constexpr int kPrologue = XL > 2 * WL ? XL : 2 * WL;     // last step the prologue serves
+    // before the loop, for need = 0..kPrologue: chunk need/2, then stage need
+    __host__ __device__ static constexpr bool pro_chunk(int need, int GS) { return (need & 1) == 0 && need / 2 <= WL && need < GS; }
+    __host__ __device__ static constexpr bool pro_stage(int need, int GS) { return need <= XL && need < GS; }
+    // after the barrier of iteration i: stage i + XL, then chunk i/2 + WL
+    __host__ __device__ static constexpr bool it_stage(int i, int GS) { return i >= 1 && i + XL < GS; }
+    __host__ __device__ static constexpr bool it_chunk(int i, int GS) { return i >= 2 && (i & 1) == 0 && i + 2 * WL < GS; }
+    // Away from both ends the count depends on the parity of i only: the loop
+    // uses these constants there (verify() checks they equal allowed()).
+    __host__ __device__ static constexpr bool steady_at(int i, int GS) { return i > kPrologue && i + kPrologue + 1 < GS; }
+    static constexpr int steady(int parity) { return allowed(2 * kPrologue + 2 + parity, 1 << 20); }
+    __host__ __device__ static constexpr int allowed(int i, int GS) {
+        const int need = stage_key(i) > chunk_key(i / 2) ? stage_key(i) : chunk_key(i / 2);
+        int n = 0;
+        for (int s = i + 1; s <= i + XL; ++s)
+            if (s < GS && stage_iter(s) <= i - 1 && stage_key(s) > need) n += NX;
+        for (int c = i / 2 + 1; c <= i / 2 + WL + 1; ++c)
+            if (2 * c < GS && chunk_iter(c) <= i - 1 && chunk_key(c) > need) n += NWC;
+        return n;
+    }
+    static constexpr bool verify() {
+        if (!(XL >= 1 && WL >= 1 && XL <= 2 * WL)) return false;
+        constexpr int kMaxGS = 48;
+        constexpr int kCap = (kMaxGS + XL + 1) * NX + (kMaxGS / 2 + WL + 2) * NWC;
+        for (int GS = 1; GS <= kMaxGS; ++GS) {
+            int kind[kCap] = {}, idx[kCap] = {};   // unit ops in issue order: 0 stage, 1 chunk
+            int issued = 0, landed = 0;
+            int sslot[XL + 1], cslot[WL + 1];
+            for (int k = 0; k <= XL; ++k) sslot[k] = -1;
+            for (int k = 0; k <= WL; ++k) cslot[k] = -1;
+            bool ok = true;
+            auto issue = [&](int kd, int ix, int step) {   // step: barrier already passed (-1: none)
+                if (kd == 0) {
+                    const int occ = sslot[ix % (XL + 1)];
+                    if (occ >= 0 && occ > step - 1) ok = false;            // read at step occ
+                    sslot[ix % (XL + 1)] = ix;
+                    for (int u = 0; u < NX; ++u) { kind[issued] = 0; idx[issued++] = ix; }
+                } else {
+                    const int occ = cslot[ix % (WL + 1)];
+                    if (occ >= 0 && 2 * occ + 1 > step - 1) ok = false;    // read at steps 2occ, 2occ+1
+                    cslot[ix % (WL + 1)] = ix;
+                    for (int u = 0; u < NWC; ++u) { kind[issued] = 1; idx[issued++] = ix; }
+                }
+            };
+            for (int need = 0; need <= kPrologue; ++need) {
+                if (pro_chunk(need, GS)) issue(1, need / 2, -1);
+                if (pro_stage(need, GS)) issue(0, need, -1);
+            }
+            for (int i = 0; i < GS; ++i) {
+                const int a = allowed(i, GS);
+                if (a < 0 || a > kMax) return false;
+                if (issued - a > landed) landed = issued - a;
+                bool have_s = false, have_c = false;
+                int last = -1;
+                for (int u = 0; u < issued; ++u) {
+                    const bool mine = (kind[u] == 0 && idx[u] == i) || (kind[u] == 1 && idx[u] == i / 2);
+                    if (mine && u >= landed) return false;                 // step i's data in flight
+                    if (mine) last = u;
+                    if (mine && kind[u] == 0) have_s = true;
+                    if (mine && kind[u] == 1) have_c = true;
+                }
+                if (!have_s || !have_c) return false;
+                if (a != issued - (last + 1)) return false;                // no stricter wait than needed
+                if (steady_at(i, GS) && a != steady(i & 1)) return false;
+                if (sslot[i % (XL + 1)] != i || cslot[(i / 2) % (WL + 1)] != i / 2) return false;
+                if (it_stage(i, GS)) issue(0, i + XL, i);
+                if (it_chunk(i, GS)) issue(1, i / 2 + WL, i);
+                if (!ok) return false;
+            }
+            if (allowed(GS - 1, GS) != 0 || landed != issued) return false;   // nothing left in flight
+        }
+        return true;
+    }
+};
+
 // One BM x (WN*TN*16) tile (rows m0.., columns n0..) over the whole K. The
 // workgroup's 4 or 8 waves are laid out WM x WN; each owns TM x TN 16x16 output
 // tiles.
@@ -539,42 +642,32 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     //      LDS stages and weight slots. A stage or slot is refilled only after
     //      the barrier that follows every wave's last read of it. ----
     uint32_t wq[TN][2], wp[TN], cq[TN][2], cp[TN];
-    // Schedule with WL > 0, counted in iterations j (negative j = prologue):
-    // iteration j issues weight chunk j/2 + WL when j is even (NWC ops, first
-    // step j + 2*WL), then the x stage of step j + XL (NX ops), each only if
-    // that step exists. What step i needs (its x stage and chunk i/2) was
-    // therefore issued no later than its x stage, in iteration i - XL (since
-    // XL <= 2*WL), and the ops issued after it are those of iterations
-    // i - XL + 1 .. i - 1: waiting until at most that many are in flight
-    // (loads complete in order) means step i has landed.
+    // With WL > 0 the x stages and weight chunks follow DmaSchedule (above).
     constexpr int NX = L::PER_WAVE + 1;
     constexpr int NWC = TN;
     static_assert(WL == 0 || (kChunk == 2 && TN % 2 == 0), "weight-chunk schedule");
-    auto chunk_at = [&](int j) { return (j & 1) == 0 && j + 2 * WL < GS; };   // iteration j issues a chunk
-    auto stage_at = [&](int j) { return j + XL >= 0 && j + XL < GS; };       // iteration j issues an x stage
+    using Sched = DmaSchedule<XL, WL, NX, NWC>;
+    static_assert(WL == 0 || Sched::verify(), "x-stage / weight-chunk DMA schedule");
     if constexpr (WL == 0) {
         stage_copy(0);
         w_load(0, wq, wp);
     } else {
 #pragma unroll
-        for (int j = -2 * WL; j < 0; ++j) {
-            if (chunk_at(j)) w_chunk_issue(j / 2 + WL);
-            if (stage_at(j)) stage_copy(j + XL);
+        for (int need = 0; need <= Sched::kPrologue; ++need) {
+            if (Sched::pro_chunk(need, GS)) w_chunk_issue(need / 2);
+            if (Sched::pro_stage(need, GS)) stage_copy(need);
         }
     }
     for (int i = 0; i < GS; ++i) {
         if constexpr (WL == 0) {
             wait_vm<0>();                                 // this wave's part of step i has landed
-        } else if (i + 2 * WL <= GS) {
-            // every op of the window exists: (XL-1) x stages and the chunks of
-            // its even iterations
-            if (i & 1) wait_vm<(XL - 1) * NX + (XL / 2) * NWC>();
-            else wait_vm<(XL - 1) * NX + ((XL - 1) / 2) * NWC>();
         } else {
-            int n = 0;
-#pragma unroll
-            for (int d = 1; d < XL; ++d) n += (stage_at(i - d) ? NX : 0) + (chunk_at(i - d) ? NWC : 0);
-            wait_vm_upto<(XL - 1) * NX + (XL / 2) * NWC>(n);
+            if (Sched::steady_at(i, GS)) {
+                if (i & 1) wait_vm<Sched::steady(1)>();
+                else wait_vm<Sched::steady(0)>();
+            } else {
+                wait_vm_upto<Sched::kMax>(Sched::allowed(i, GS));
+            }
         }
         // Barrier without a memory fence: the LDS data of step i came in by DMA
         // and is complete after the wait above (in every wave, after the barrier);
@@ -594,8 +687,8 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             }
         } else {
             w_read(i, cq, cp);
-            if (chunk_at(i)) w_chunk_issue(i / 2 + WL);
-            if (stage_at(i)) stage_copy(i + XL);
+            if (Sched::it_stage(i, GS)) stage_copy(i + XL);
+            if (Sched::it_chunk(i, GS)) w_chunk_issue(i / 2 + WL);
         }
         __builtin_amdgcn_sched_barrier(0);
         compute(i, cq, cp);

@@ -20,34 +20,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33133.43, "write_kib": 36139.523,
+    ("m80", "split16"): {"fetch_kib": 33065.968, "write_kib": 36207.847,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 39100.777, "write_kib": 35746.831,
+    ("m80", "split"): {"fetch_kib": 38781.328, "write_kib": 36100.936,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27850.712, "write_kib": 36677.017,
+    ("m80", "bf16"): {"fetch_kib": 27694.714, "write_kib": 37296.045,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 288 dispatches per counter run
     # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109363.226, "write_kib": 306684.771,
+    ("m65536", "split16"): {"fetch_kib": 109147.872, "write_kib": 233054.289,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
-    ("m65536", "split"): {"fetch_kib": 177234.75, "write_kib": 249509.477,
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
+    ("m65536", "split"): {"fetch_kib": 172386.791, "write_kib": 230867.008,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
-    ("m65536", "bf16"): {"fetch_kib": 57603.607, "write_kib": 274197.758,
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
+    ("m65536", "bf16"): {"fetch_kib": 51787.826, "write_kib": 234036.857,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ade2efcdb4484a314da53206c622a7907bfc79b71cafe3cdca2291114199b6f"},
+         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
 }
 
 
