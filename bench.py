@@ -254,6 +254,28 @@ def measured_ceilings(torch, rtq, gib=4, reps=5):
                 best = sweep[-1]
     del buf
     torch.cuda.empty_cache()
+    # A read of the 12-block weight size (39.4 MB) from 16 buffers cycled like
+    # the weight sets: the ceiling a kernel that streams those weights once
+    # can reach, launch ramp included (64 launches back to back per shape).
+    wsize = block_bytes_flops(1)[0] * 12 // 16 * 16
+    wbufs = [torch.ones(wsize // 4, dtype=torch.float32, device=dev) for _ in range(WEIGHT_SETS)]
+    wbest = None
+    wsweep = []
+    for unroll, blocks in ((4, 512), (8, 2048), (16, 512), (16, 2048), (16, 4096)):
+        for b in wbufs:
+            rtq.diag_stream_read(b, unroll, blocks, sink)
+        ev0.record()
+        for r in range(64):
+            rtq.diag_stream_read(wbufs[r % len(wbufs)], unroll, blocks, sink)
+        ev1.record()
+        ev1.synchronize()
+        us = ev0.elapsed_time(ev1) * 1e3 / 64
+        wsweep.append({"unroll": unroll, "blocks": blocks, "us_per_launch": round(us, 3),
+                       "gbs": round(wsize / us / 1e3, 1)})
+        if wbest is None or wsweep[-1]["gbs"] > wbest["gbs"]:
+            wbest = wsweep[-1]
+    del wbufs
+    torch.cuda.empty_cache()
     fsink = torch.zeros(1, dtype=torch.float32, device=dev)
     mfma = {}
     for kind, name, peak in ((0, "fp16", PEAK_BF16_MFMA_TFLOPS), (1, "bf16", PEAK_BF16_MFMA_TFLOPS),
@@ -269,6 +291,11 @@ def measured_ceilings(torch, rtq, gib=4, reps=5):
                       "instruction": ["v_mfma_f32_16x16x32_f16", "v_mfma_f32_16x16x32_bf16",
                                       "v_mfma_f32_16x16x4_f32"][kind]}
     return {"hbm_read_gbs": best["gbs"], "hbm_frac_of_peak": round(best["gbs"] / PEAK_HBM_GBS, 4),
+            "weight_size_read_gbs": wbest["gbs"], "weight_size_read_us": wbest["us_per_launch"],
+            "weight_size_read_how": f"rtq_diag_stream_read of {wsize} B (the 12-block weight size) from "
+                                    f"{WEIGHT_SETS} buffers cycled, 64 launches back to back between HIP events, "
+                                    "best of 5 shapes",
+            "weight_size_read_sweep": wsweep,
             "hbm_how": f"rtq_diag_stream_read over a {gib} GiB buffer (16-byte loads, best of the sweep), "
                        f"{reps} passes timed with HIP events",
             "hbm_sweep": sweep, "mfma": mfma,
@@ -549,6 +576,7 @@ def main():
         rl = line["roofline"]
         if rl["bound"] == "hbm":
             rl["frac_of_measured_ceiling"] = round(rl["achieved"] / hbm, 5)
+            rl["frac_of_weight_size_read"] = round(rl["achieved"] / ceil["weight_size_read_gbs"], 5)
         unit = {"split16": "fp16", "split": "bf16", "bf16": "bf16", "fp32": "fp32"}[args.math]
         line["weight_frac_of_measured_hbm"] = round(prim["weight_gbs"] / hbm, 5)
         for wl in out:
@@ -574,6 +602,8 @@ def main():
             for pt in line["m_sweep"]["points"]:
                 pt["weight_frac_of_measured_hbm_in_kernel"] = round(
                     pt["weight_gbs_in_kernel"] / line["measured_ceilings"]["hbm_read_gbs"], 4)
+                pt["weight_frac_of_weight_size_read_in_kernel"] = round(
+                    pt["weight_gbs_in_kernel"] / line["measured_ceilings"]["weight_size_read_gbs"], 4)
     if not args.no_cpu_baseline and prim_name == "m80":
         line["cpu_baseline"] = cpu_baseline(4, synth.M_GOLDEN, args.cpu_seconds, recipe=args.recipe)
         if args.recipe == "mixed":
