@@ -144,24 +144,41 @@ def build_sets(torch, rtq, synth, cfg, M, n_sets, xs_per_block, heavy=None, reci
     return sets
 
 
-def time_workload(torch, rtq, sets, M, steps, warmup, math):
-    """Times exactly `steps` steps (wall clock between synchronizations) and,
-    through the library's event timing, the main GEMM kernel launches inside
-    them (HIP events recorded on the launch stream)."""
-    for i in range(warmup):
+def workspace_for(torch, rtq, sets, M, math):
+    """One caller workspace for every weight set of a workload (the largest
+    any call needs), allocated once before timing: the calls then go through
+    rtq_block_project_ws and allocate nothing."""
+    need = max(rtq.block_workspace_bytes(blocks, M, math, packed=packed) for blocks, packed in sets)
+    return torch.empty(max(need, 256), dtype=torch.uint8, device="cuda:0")
+
+
+def time_workload(torch, rtq, sets, M, steps, warmup, math, ws=None):
+    """Times exactly `steps` steps twice. First with nothing else in the
+    stream (wall clock between synchronizations): the step time. Then the same
+    steps again with the library's event timing on, which brackets every main
+    GEMM kernel launch with HIP events on its stream: the kernel time (the
+    events themselves add a few us to each step, so that pass does not give
+    the step time)."""
+    def step(i):
         blocks, packed = sets[i % len(sets)]
-        rtq.block_project(blocks, M, packed=packed, math=math)
+        rtq.block_project(blocks, M, packed=packed, math=math, workspace=ws)
+    for i in range(warmup):
+        step(i)
     torch.cuda.synchronize()
-    rtq.timing_enable(True)
     t0 = time.perf_counter()
     for i in range(steps):
-        blocks, packed = sets[i % len(sets)]
-        rtq.block_project(blocks, M, packed=packed, math=math)
+        step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    rtq.timing_enable(True)
+    t1 = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    wall_events = time.perf_counter() - t1
     kernel_ms, launches = rtq.timing_read()
     rtq.timing_enable(False)
-    return wall, kernel_ms, launches
+    return wall, kernel_ms, launches, wall_events
 
 
 def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
@@ -173,8 +190,15 @@ def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
         M = synth.M_LARGE
         sets = build_sets(torch, rtq, synth, 5, M, 1, xs_per_block=False, recipe=recipe)
     wb, fl = block_bytes_flops(M, recipe)
-    wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup, math)
-    del sets
+    ws = workspace_for(torch, rtq, sets, M, math)
+    wall, kernel_ms, launches, wall_events = time_workload(torch, rtq, sets, M, steps, warmup, math, ws)
+    pool_ms = None
+    if workload == "m80":
+        # the same steps with the library's own per-call workspace (stream-ordered pool allocation)
+        pool_wall, _, _, _ = time_workload(torch, rtq, sets, M, steps, warmup, math, None)
+        pool_ms = pool_wall / steps * 1e3
+    ws_bytes = ws.numel()
+    del sets, ws
     torch.cuda.empty_cache()
     flops_step, bytes_step = fl * nb, wb * nb
     act_bytes = sum(M * k * 4 for k in synth.INPUT_WIDTH.values())    # the four inputs of a block
@@ -192,6 +216,8 @@ def measure(torch, rtq, synth, workload, steps, warmup, math, recipe="mixed"):
         "kernel_weight_gbs": bytes_step / per_step / (launch_ms * 1e-3) / 1e9,
         "flops_per_step": flops_step, "weight_bytes_per_step": bytes_step, "steps": steps,
         "algorithmic_bytes_per_step": alg_step,
+        "ms_per_step_with_kernel_events": wall_events / steps * 1e3,
+        "ms_per_step_pool_workspace": pool_ms, "workspace_bytes": ws_bytes,
     }
 
 
@@ -214,7 +240,8 @@ def m_sweep(torch, rtq, synth, Ms, math, steps=200, warmup=20, recipe="mixed"):
             blocks = [{name: rtq.Projection(weights[s][b][name], xs[b][synth.BLOCK_SHAPES[name][2]], ys[b][name])
                        for name in synth.PROJ_ORDER} for b in range(nb)]
             sets.append((blocks, rtq.pack_blocks(blocks, M)))
-        wall, kernel_ms, launches = time_workload(torch, rtq, sets, M, steps, warmup, math)
+        ws = workspace_for(torch, rtq, sets, M, math)
+        wall, kernel_ms, launches, _ = time_workload(torch, rtq, sets, M, steps, warmup, math, ws)
         _, fl = block_bytes_flops(M, recipe)
         ms = wall / steps * 1e3
         per_launch = kernel_ms / launches
@@ -222,7 +249,7 @@ def m_sweep(torch, rtq, synth, Ms, math, steps=200, warmup=20, recipe="mixed"):
                     "weight_gbs": round(wb * nb / (ms * 1e-3) / 1e9, 1),
                     "kernel_ms_per_launch": round(per_launch, 5),
                     "weight_gbs_in_kernel": round(wb * nb / (launches / steps) / (per_launch * 1e-3) / 1e9, 1)})
-        del sets, xs, ys
+        del sets, xs, ys, ws
     del weights
     torch.cuda.empty_cache()
     return out
@@ -549,6 +576,16 @@ def main():
         "weight_gbs": round(prim["weight_gbs"], 2),
         "weight_hbm_frac": round(prim["weight_gbs"] / PEAK_HBM_GBS, 5),
         "roofline": roofline(prim, args.math, prim_name, args.recipe),
+        "timing": {
+            "step": "wall clock over the timed steps between synchronizations, nothing else in the stream; "
+                    "every call through rtq_block_project_ws with one device workspace allocated before timing",
+            "kernel": "a second pass over the same steps with HIP events recorded around every main GEMM "
+                      "launch on its stream (rtq_timing_enable); the events add to that pass's step time",
+            "ms_per_step_with_kernel_events": round(prim["ms_per_step_with_kernel_events"], 5),
+            "ms_per_step_pool_workspace": (round(prim["ms_per_step_pool_workspace"], 5)
+                                           if prim["ms_per_step_pool_workspace"] else None),
+            "workspace_bytes": prim["workspace_bytes"],
+        },
     }
     for wl, r in out.items():
         if wl == prim_name:

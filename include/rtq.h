@@ -256,6 +256,32 @@ rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64
 rtq_status rtq_block_project_noalloc(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
                                      void* stream);
 
+/* rtq_block_project_ex with a workspace the caller provides and keeps (the
+ * usual pattern of BLAS libraries), for callers that run the same projection
+ * set again and again: the library's own per-call workspace costs a
+ * stream-ordered allocation and free (about 2 us per call on MI355X).
+ *
+ * rtq_block_workspace_bytes validates the call exactly as rtq_block_project_ex
+ * would (same arguments, no stream) and stores in *bytes the workspace it
+ * needs in arithmetic `math`: 0 when it runs no split-path launch that needs
+ * one (M <= 32 with every K one of 256, 512, 1024, 2048 takes the direct
+ * kernel; the fp32-MFMA arithmetic needs none). It launches nothing and makes
+ * no HIP call.
+ *
+ * rtq_block_project_ws: `workspace` is a device buffer of `workspace_bytes`
+ * bytes, 256-byte aligned, at least the size the query returns for the same
+ * call (it may be NULL when that is 0), not overlapping any input or output
+ * of the call; otherwise the call returns RTQ_ERR_SHAPE, RTQ_ERR_NULL,
+ * RTQ_ERR_ALIGN or RTQ_ERR_OVERLAP and launches nothing. The library
+ * allocates nothing and keeps no pointer to the workspace past the call's
+ * work on `stream`. Calls that share one workspace must be ordered by the
+ * caller (the same stream, or events between streams). Results are those of
+ * rtq_block_project_ex, bit for bit. */
+rtq_status rtq_block_workspace_bytes(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
+                                     int64_t* bytes);
+rtq_status rtq_block_project_ws(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* workspace,
+                                int64_t workspace_bytes, void* stream);
+
 /* Kernel timing (profiling aid). While enabled, every main GEMM kernel launch
  * of the entry points above is bracketed by a pair of HIP events recorded on
  * its stream (events are created on first use and kept for reuse). Enabling

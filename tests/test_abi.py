@@ -228,3 +228,73 @@ def test_struct_layout_matches_header(tmp_path):
 def test_recipes_agree_with_names():
     assert set(rtq.RECIPE_MIXED) == set(rtq.PROJ_NAMES)
     assert {n for n, f in rtq.RECIPE_MIXED.items() if f == "q8"} == {"wo", "w2"}
+
+
+E = 0x7f4000000000
+
+
+def _rtj_blocks(n_blocks, M):
+    """The RT-J projection set (mixed recipe) with fake, disjoint device
+    addresses: every input, payload, scale array and output its own 256 MiB."""
+    import synth
+    arr = (rtq._Block * n_blocks)()
+    addr = E
+    for b in range(n_blocks):
+        xs = {}
+        for name in synth.PROJ_ORDER:
+            N, K, xin = synth.BLOCK_SHAPES[name]
+            if xin not in xs:
+                xs[xin] = addr
+                addr += 1 << 28
+            d = getattr(arr[b], name)
+            d.fmt, d.N, d.K = {"q4": rtq.FMT_Q4, "q8": rtq.FMT_Q8}[rtq.RECIPE_MIXED[name]], N, K
+            d.x = xs[xin]
+            d.payload, d.scale, d.y = addr, addr + (1 << 28), addr + (2 << 28)
+            addr += 3 << 28
+    return arr, addr
+
+
+def _image_bytes(K, M, NL):
+    """Limb image of one input as the layout states it: NL planes of 1 KB per
+    (group, 16-row block), then the fp32 group sums, then the int32 row
+    exponents."""
+    G, RB = K // 32, (M + 15) // 16
+    return G * RB * 1024 * NL + G * RB * 16 * 4 + RB * 16 * 4
+
+
+@pytest.mark.parametrize("math,nl", [(rtq.MATH_SPLIT_F16, 2), (rtq.MATH_SPLIT_BF16, 3), (rtq.MATH_BF16, 1)])
+def test_workspace_size_query(lib, math, nl):
+    """12 blocks at M = 80 (grouped route): four limb images per block plus
+    w2's four K-chunk partials, each image 256-byte aligned; the direct route
+    (M <= 32) and the fp32 arithmetic need none."""
+    arr, _ = _rtj_blocks(12, 80)
+    out = ctypes.c_int64(-1)
+    assert lib.rtq_block_workspace_bytes(arr, 12, 80, math, ctypes.byref(out)) == OK
+    want = 12 * (3 * _image_bytes(512, 80, nl) + _image_bytes(2048, 80, nl)) + 12 * 4 * 80 * 512 * 4
+    assert want <= out.value <= want + 48 * 256, (out.value, want)
+    for M, m in ((16, math), (80, rtq.MATH_FP32_MFMA), (0, math)):
+        arr, _ = _rtj_blocks(12, M)
+        assert lib.rtq_block_workspace_bytes(arr, 12, M, m, ctypes.byref(out)) == OK
+        assert out.value == 0, (M, m, out.value)
+    assert lib.rtq_block_workspace_bytes(arr, 12, 80, math, None) == ERR_NULL
+    assert lib.rtq_block_workspace_bytes(arr, 12, 80, 9, ctypes.byref(out)) == ERR_FORMAT
+
+
+def test_workspace_validation(lib):
+    """rtq_block_project_ws rejects, before any HIP call, a workspace that is
+    too small, NULL where one is needed, misaligned, overlapping an input or
+    an output, or of negative size; a call that needs none takes NULL."""
+    math = rtq.MATH_SPLIT_F16
+    arr, end = _rtj_blocks(12, 80)
+    out = ctypes.c_int64(0)
+    assert lib.rtq_block_workspace_bytes(arr, 12, 80, math, ctypes.byref(out)) == OK
+    need = out.value
+    ws = end + (1 << 28)
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, ws, need - 1, None) == ERR_SHAPE
+    assert b"needs" in lib.rtq_last_error()
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, None, need, None) == ERR_NULL
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, ws + 128, need, None) == ERR_ALIGN
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, ws, -1, None) == ERR_SHAPE
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, arr[0].wq.y, need, None) == ERR_OVERLAP
+    assert lib.rtq_block_project_ws(arr, 12, 80, math, arr[3].w1.payload, need, None) == ERR_OVERLAP
+    assert lib.rtq_block_project_ws(arr, 12, 0, math, None, 0, None) == OK      # M = 0: a no-op

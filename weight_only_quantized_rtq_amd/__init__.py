@@ -42,7 +42,8 @@ STATUS = {0: "RTQ_OK", 1: "RTQ_ERR_NULL", 2: "RTQ_ERR_SHAPE", 3: "RTQ_ERR_ALIGN"
 EXPORTS = ("rtq_gemm_q4", "rtq_gemm_q8", "rtq_gemm_f8", "rtq_block_project", "rtq_dequant_q4",
            "rtq_dequant_q8", "rtq_dequant_f8", "rtq_quantize_q4", "rtq_quantize_q8", "rtq_quantize_f8",
            "rtq_quantize_q4_host", "rtq_quantize_q8_host", "rtq_quantize_f8_host", "rtq_gemm_ex",
-           "rtq_block_project_ex", "rtq_block_project_noalloc", "rtq_diag_stream_read", "rtq_diag_mfma_loop", "rtq_timing_enable",
+           "rtq_block_project_ex", "rtq_block_project_noalloc", "rtq_block_workspace_bytes",
+           "rtq_block_project_ws", "rtq_diag_stream_read", "rtq_diag_mfma_loop", "rtq_timing_enable",
            "rtq_timing_read", "rtq_status_string", "rtq_last_error", "rtq_version")
 
 # Arithmetic of a GEMM call (the `math` argument; None runs the library's
@@ -107,6 +108,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.rtq_block_project_ex.restype = ctypes.c_int
     lib.rtq_block_project_noalloc.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp]
     lib.rtq_block_project_noalloc.restype = ctypes.c_int
+    lib.rtq_block_workspace_bytes.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, ctypes.POINTER(i64)]
+    lib.rtq_block_workspace_bytes.restype = ctypes.c_int
+    lib.rtq_block_project_ws.argtypes = [ctypes.POINTER(_Block), i32, i64, i32, vp, i64, vp]
+    lib.rtq_block_project_ws.restype = ctypes.c_int
     lib.rtq_diag_stream_read.argtypes = [vp, i64, i32, i32, vp, vp]
     lib.rtq_diag_stream_read.restype = ctypes.c_int
     lib.rtq_diag_mfma_loop.argtypes = [i32, i64, i32, vp, ctypes.POINTER(ctypes.c_double), vp]
@@ -462,13 +467,31 @@ def pack_blocks(blocks: list[dict[str, Projection]], M: int):
     return arr, keep
 
 
-def block_project(blocks: list[dict[str, Projection]], M: int, stream=None, packed=None,
-                  math: int | None = None) -> None:
-    """Runs every projection of the given blocks (rtq_block_project, or
-    rtq_block_project_ex with the arithmetic `math`). `packed` may hold a
-    pack_blocks() result to reuse across calls."""
+def block_workspace_bytes(blocks: list[dict[str, Projection]], M: int, math: int = MATH_SPLIT_BF16,
+                          packed=None) -> int:
+    """Workspace bytes block_project(..., workspace=) needs for this call
+    (rtq_block_workspace_bytes)."""
     lib = load_library()
     arr, _keep = packed if packed is not None else pack_blocks(blocks, M)
+    out = ctypes.c_int64(0)
+    _check(lib.rtq_block_workspace_bytes(arr, len(arr), M, int(math), ctypes.byref(out)))
+    return out.value
+
+
+def block_project(blocks: list[dict[str, Projection]], M: int, stream=None, packed=None,
+                  math: int | None = None, workspace: torch.Tensor | None = None) -> None:
+    """Runs every projection of the given blocks (rtq_block_project, or
+    rtq_block_project_ex with the arithmetic `math`, or rtq_block_project_ws
+    with a caller-kept device `workspace` tensor of at least
+    block_workspace_bytes() bytes). `packed` may hold a pack_blocks() result
+    to reuse across calls."""
+    lib = load_library()
+    arr, _keep = packed if packed is not None else pack_blocks(blocks, M)
+    if workspace is not None:
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib.rtq_block_project_ws(arr, len(arr), M, int(MATH_SPLIT_BF16 if math is None else math),
+                                        _ptr(workspace), nbytes, _stream(stream)))
+        return
     if math is None:
         _check(lib.rtq_block_project(arr, len(arr), M, _stream(stream)))
     else:

@@ -223,8 +223,13 @@ namespace {
 // rtq_block_project / _ex / _noalloc: validation, then the grouped launch and
 // the projections the grouped kernels do not take. With no_alloc the split
 // path's workspace is the library's fixed scratch array.
+// The block projection behind every block entry point: validate, then
+// launch with the workspace `mode` names (the library's pool, its scratch
+// array, or the caller's `ws` of `ws_bytes`). With size_out set, validate and
+// return the workspace bytes the call needs without launching anything.
 rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream,
-                              bool no_alloc) {
+                              rtq::WsMode mode, void* ws = nullptr, int64_t ws_bytes = 0,
+                              int64_t* size_out = nullptr) {
     clear_error();
     if (!math_ok(math)) return fail(RTQ_ERR_FORMAT, "rtq_block_project: unknown arithmetic %d", math);
     if (!blocks) return fail(RTQ_ERR_NULL, "rtq_block_project: blocks is NULL");
@@ -282,19 +287,40 @@ rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t
         if (it != outs + n_outs && overlaps(*it, r))
             return fail(RTQ_ERR_OVERLAP, "rtq_block_project: an output overlaps a projection's input");
     }
+    const int64_t need = M > 0 && n_grouped ? rtq::grouped_workspace_bytes(grouped, n_grouped, M, math) : 0;
+    if (need < 0) return fail(RTQ_ERR_SHAPE, "rtq_block_project: too many projections for one call");
+    if (size_out) {
+        *size_out = need;
+        return RTQ_OK;
+    }
     if (M == 0) return RTQ_OK;
-    if (no_alloc && n_grouped) {
-        const int64_t need = rtq::grouped_workspace_bytes(grouped, n_grouped, M, math);
-        if (need < 0 || need > rtq::kScratchBytes)
-            return fail(RTQ_ERR_SHAPE,
-                        "rtq_block_project_noalloc: the call needs %lld bytes of workspace, more than the %lld-byte "
-                        "scratch of the allocation-free entry point",
-                        (long long)need, (long long)rtq::kScratchBytes);
+    if (mode == rtq::kWsScratch && need > rtq::kScratchBytes)
+        return fail(RTQ_ERR_SHAPE,
+                    "rtq_block_project_noalloc: the call needs %lld bytes of workspace, more than the %lld-byte "
+                    "scratch of the allocation-free entry point",
+                    (long long)need, (long long)rtq::kScratchBytes);
+    if (mode == rtq::kWsCaller) {
+        if (need > ws_bytes)
+            return fail(RTQ_ERR_SHAPE, "rtq_block_project_ws: the call needs %lld bytes of workspace, %lld given",
+                        (long long)need, (long long)ws_bytes);
+        if (need > 0 && !ws) return fail(RTQ_ERR_NULL, "rtq_block_project_ws: workspace is NULL");
+        if (ws && !aligned(ws, 256)) return fail(RTQ_ERR_ALIGN, "rtq_block_project_ws: workspace is not 256-byte aligned");
+        if (ws && need > 0) {
+            // the workspace must not overlap any input or output of the call
+            const Range w = range_of(ws, need);
+            for (int i = 0; i < n_outs; ++i)
+                if (overlaps(outs[i], w))
+                    return fail(RTQ_ERR_OVERLAP, "rtq_block_project_ws: the workspace overlaps an output");
+            for (int i = 0; i < n_ins; ++i)
+                if (overlaps(ins[i], w))
+                    return fail(RTQ_ERR_OVERLAP, "rtq_block_project_ws: the workspace overlaps an input");
+        }
     }
     const hipStream_t st = static_cast<hipStream_t>(stream);
     if (n_grouped) {
-        const rtq_status s =
-            hip_status(rtq::launch_grouped(grouped, n_grouped, M, math, st, no_alloc), "rtq_block_project launch");
+        const rtq_status s = hip_status(
+            rtq::launch_grouped(grouped, n_grouped, M, math, st, mode, static_cast<unsigned char*>(ws), ws_bytes),
+            "rtq_block_project launch");
         if (s != RTQ_OK) return s;
     }
     for (int i = 0; i < n_single; ++i) {
@@ -307,16 +333,35 @@ rtq_status block_project_impl(const rtq_block* blocks, int32_t n_blocks, int64_t
 }  // namespace
 
 rtq_status rtq_block_project(const rtq_block* blocks, int32_t n_blocks, int64_t M, void* stream) {
-    return block_project_impl(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream, false);
+    return block_project_impl(blocks, n_blocks, M, RTQ_MATH_SPLIT_BF16, stream, rtq::kWsPool);
 }
 
 rtq_status rtq_block_project_ex(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* stream) {
-    return block_project_impl(blocks, n_blocks, M, math, stream, false);
+    return block_project_impl(blocks, n_blocks, M, math, stream, rtq::kWsPool);
 }
 
 rtq_status rtq_block_project_noalloc(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
                                      void* stream) {
-    return block_project_impl(blocks, n_blocks, M, math, stream, true);
+    return block_project_impl(blocks, n_blocks, M, math, stream, rtq::kWsScratch);
+}
+
+rtq_status rtq_block_workspace_bytes(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math,
+                                     int64_t* bytes) {
+    if (!bytes) {
+        clear_error();
+        return fail(RTQ_ERR_NULL, "rtq_block_workspace_bytes: bytes is NULL");
+    }
+    *bytes = 0;
+    return block_project_impl(blocks, n_blocks, M, math, nullptr, rtq::kWsCaller, nullptr, 0, bytes);
+}
+
+rtq_status rtq_block_project_ws(const rtq_block* blocks, int32_t n_blocks, int64_t M, int32_t math, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+    if (workspace_bytes < 0) {
+        clear_error();
+        return fail(RTQ_ERR_SHAPE, "rtq_block_project_ws: workspace_bytes is negative");
+    }
+    return block_project_impl(blocks, n_blocks, M, math, stream, rtq::kWsCaller, workspace, workspace_bytes);
 }
 
 rtq_status rtq_dequant_q4(const uint8_t* payload, const uint16_t* pairs, float* w, int64_t N, int64_t K,

@@ -645,7 +645,8 @@ int64_t grouped_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int
     return split_workspace_bytes(split_buf.data(), n_split, M, nl);
 }
 
-hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream, bool no_alloc) {
+hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream, WsMode mode,
+                          unsigned char* ws, int64_t cap) {
     const int nl = split_limbs(math);
     if (!nl) return launch_grouped_fp32_bias(tasks, count, M, stream);
     // Split path for every task it takes; the rest (weights past 32-bit
@@ -660,8 +661,9 @@ hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math,
         else rest[n_rest++] = tasks[i];
     }
     if (n_split) {
-        const hipError_t e = no_alloc ? launch_split_scratch(split, n_split, M, nl, stream)
-                                      : launch_split(split, n_split, M, nl, stream);
+        const hipError_t e = mode == kWsScratch ? launch_split_scratch(split, n_split, M, nl, stream)
+                             : mode == kWsCaller ? launch_split_ws(split, n_split, M, nl, stream, ws, cap)
+                                                 : launch_split(split, n_split, M, nl, stream);
         if (e != hipSuccess) return e;
     }
     return n_rest ? launch_grouped_fp32_bias(rest, n_rest, M, stream) : hipSuccess;

@@ -1191,6 +1191,12 @@ hipError_t launch_split_scratch(const ProjTask* tasks, int count, int64_t M, int
     return split_impl(tasks, count, M, NL, stream, ws, kScratchBytes);
 }
 
+hipError_t launch_split_ws(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream,
+                           unsigned char* ws, int64_t cap) {
+    if (!ws && split_workspace_bytes(tasks, count, M, NL) > 0) return hipErrorInvalidValue;
+    return split_impl(tasks, count, M, NL, stream, ws, cap);
+}
+
 hipError_t launch_bias_add(const ProjTask* tasks, int count, int64_t M, hipStream_t stream) {
     FinishArgs r{};
     int blocks = 0;

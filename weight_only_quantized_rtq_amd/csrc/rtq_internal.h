@@ -46,10 +46,16 @@ inline int split_limbs(int mode) {
 // Single projection y[M][N] = x[M][K] . dequant(W)^T in arithmetic `math`.
 hipError_t launch_gemm(const ProjTask& task, int64_t M, int math, hipStream_t stream);
 
+// Where the split path's workspace (limb images, K-chunk partials) comes
+// from: a stream-ordered allocation from the library's pool, the library's
+// fixed scratch array, or a caller's device buffer.
+enum WsMode { kWsPool = 0, kWsScratch = 1, kWsCaller = 2 };
+
 // Several projections sharing M, in grouped launches. Every task must satisfy
-// grouped_ok().
+// grouped_ok(). With kWsCaller the workspace is ws (cap bytes, at least
+// grouped_workspace_bytes()).
 hipError_t launch_grouped(const ProjTask* tasks, int count, int64_t M, int math, hipStream_t stream,
-                          bool no_alloc = false);
+                          WsMode mode = kWsPool, unsigned char* ws = nullptr, int64_t cap = 0);
 bool grouped_ok(const ProjTask& task);
 // Workspace bytes launch_grouped needs for these tasks in arithmetic `math`.
 int64_t grouped_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int math);
@@ -57,7 +63,7 @@ int64_t grouped_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int
 // Split-limb path (gemm_split.hip): every projection of the call, sharing M,
 // with NL = 3 bf16 limbs (exact), 2 fp16 limbs of the row-scaled x, or 1 (x
 // rounded to bf16). Tasks must satisfy
-// split_ok(). Uses a stream-ordered workspace (hipMallocAsync).
+// split_ok(). Uses a stream-ordered workspace from the library's pool.
 bool split_ok(const ProjTask& task);
 hipError_t launch_split(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
 // Workspace bytes launch_split needs for these tasks (0 when they take the
@@ -69,6 +75,11 @@ int64_t split_workspace_bytes(const ProjTask* tasks, int count, int64_t M, int N
 // kScratchBytes.
 constexpr int64_t kScratchBytes = int64_t(32) << 20;
 hipError_t launch_split_scratch(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream);
+// launch_split with a caller's workspace of cap bytes (non-null wherever
+// split_workspace_bytes() is positive); hipErrorOutOfMemory, launching
+// nothing, if it is too small.
+hipError_t launch_split_ws(const ProjTask* tasks, int count, int64_t M, int NL, hipStream_t stream,
+                           unsigned char* ws, int64_t cap);
 
 // Small-M path of the split arithmetic (gemm_direct.hip): one launch, whole K
 // per workgroup, x split in the kernel. direct_fits(): M in 1..32, every K in

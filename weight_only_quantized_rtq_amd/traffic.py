@@ -19,35 +19,35 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # (workload, math) -> record; filled from the counter runs described in the
 # profiles folder.
 RECORDS: dict = {
-    # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 33 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33065.968, "write_kib": 36207.847,
+    # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 126 dispatches per counter run
+    ("m80", "split16"): {"fetch_kib": 33087.285, "write_kib": 36090.515,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38781.328, "write_kib": 36100.936,
+    ("m80", "split"): {"fetch_kib": 38775.452, "write_kib": 35986.164,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27694.714, "write_kib": 37296.045,
+    ("m80", "bf16"): {"fetch_kib": 27717.398, "write_kib": 37156.455,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
-    # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 288 dispatches per counter run
-    # (3 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109147.872, "write_kib": 233054.289,
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+    # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 480 dispatches per counter run
+    # (5 steps x 96 projections); algorithmic bytes are the per-launch average
+    ("m65536", "split16"): {"fetch_kib": 109496.123, "write_kib": 233058.093,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
-    ("m65536", "split"): {"fetch_kib": 172386.791, "write_kib": 230867.008,
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+    ("m65536", "split"): {"fetch_kib": 173504.981, "write_kib": 230887.373,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
-    ("m65536", "bf16"): {"fetch_kib": 51787.826, "write_kib": 234036.857,
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+    ("m65536", "bf16"): {"fetch_kib": 51788.863, "write_kib": 234043.021,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "e2ff9c5ad81d0a70b218a6b6662a8a9cae2fea816b0b3e34a9c1a06e7e101103"},
+         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
 }
 
 
