@@ -298,3 +298,26 @@ def test_workspace_validation(lib):
     assert lib.rtq_block_project_ws(arr, 12, 80, math, arr[0].wq.y, need, None) == ERR_OVERLAP
     assert lib.rtq_block_project_ws(arr, 12, 80, math, arr[3].w1.payload, need, None) == ERR_OVERLAP
     assert lib.rtq_block_project_ws(arr, 12, 0, math, None, 0, None) == OK      # M = 0: a no-op
+
+
+def test_small_calls_take_shorter_k_chunks(lib):
+    """A call with few workgroups that runs the finish pass anyway (a w2-shaped
+    K = 2048 projection) walks K in shorter chunks (16, then 8, then 4 groups
+    while it has fewer than 256 workgroups), and its workspace holds those
+    chunks' partials; a call that would need the finish pass only for that
+    keeps whole 16-group chunks."""
+    M = 80
+    out = ctypes.c_int64(-1)
+    # one 512 x 512 int4 projection: no finish pass otherwise, one chunk
+    arr = (rtq._Block * 1)(_block(N=512, K=512))
+    assert lib.rtq_block_workspace_bytes(arr, 1, M, rtq.MATH_SPLIT_F16, ctypes.byref(out)) == OK
+    assert out.value == (_image_bytes(512, M, 2) + 255) // 256 * 256, out.value
+    # one 512 x 2048 int8 projection: 2 column tiles, chunks of 4 groups (16 chunks, 32 workgroups)
+    arr = (rtq._Block * 1)(_block(fmt=rtq.FMT_Q8, N=512, K=2048))
+    assert lib.rtq_block_workspace_bytes(arr, 1, M, rtq.MATH_SPLIT_F16, ctypes.byref(out)) == OK
+    assert out.value == (_image_bytes(2048, M, 2) + 255) // 256 * 256 + 16 * M * 512 * 4, out.value
+    # the 12-block set fills the GPU with 408 workgroups: 16-group chunks, only w2 split
+    arr12, _ = _rtj_blocks(12, M)
+    assert lib.rtq_block_workspace_bytes(arr12, 12, M, rtq.MATH_SPLIT_F16, ctypes.byref(out)) == OK
+    images = 12 * (3 * ((_image_bytes(512, M, 2) + 255) // 256 * 256) + (_image_bytes(2048, M, 2) + 255) // 256 * 256)
+    assert out.value == images + 12 * 4 * M * 512 * 4, out.value

@@ -68,16 +68,16 @@ def check(blocks, blocks2, refs, math, sampled=(0, -1)):
 
 @pytest.mark.parametrize("math", MATHS)
 def test_workspace_call_equals_pool_call_on_two_calls(math):
-    ws = None
-    for seed, n_blocks, M in ((91, 12, 80), (92, 3, 40)):
+    """One workspace, sized for both calls, serves a 12-block call at M = 80
+    and then a 3-block call at M = 40 (whose shorter K chunks need more
+    partials per projection)."""
+    calls = [(n_blocks, M, make_blocks(seed, n_blocks, M)) for seed, n_blocks, M in ((91, 12, 80), (92, 3, 40))]
+    needs = [rtq.block_workspace_bytes(c[2][1], c[1], math) for c in calls]
+    if math == rtq.MATH_FP32_MFMA:
+        assert needs == [0, 0]
+    ws = torch.empty(max(max(needs), 1), dtype=torch.uint8, device=DEV)
+    for n_blocks, M, (blocks, blocks2, refs) in calls:
         say(f"workspace math={math} blocks={n_blocks} M={M}")
-        blocks, blocks2, refs = make_blocks(seed, n_blocks, M)
-        need = rtq.block_workspace_bytes(blocks2, M, math)
-        if math == rtq.MATH_FP32_MFMA:
-            assert need == 0
-        if ws is None:
-            ws = torch.empty(max(need, 1), dtype=torch.uint8, device=DEV)   # kept for the second, smaller call
-        assert ws.numel() >= need
         rtq.block_project(blocks, M, math=math)
         rtq.block_project(blocks2, M, math=math, workspace=ws)
         torch.cuda.synchronize()

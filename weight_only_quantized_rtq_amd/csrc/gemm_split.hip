@@ -762,7 +762,7 @@ struct SplitGroupArgs {
     int count;
     int M;
     int RB;
-    int pad;
+    int chunk_groups;                       // K chunk length in groups (split_chunks)
     const unsigned char* ws;                // workspace holding the limb images
     int tile_begin[seg_begin_slots(kMaxSplitGrouped)];   // first workgroup of each projection
     int tile_coarse[seg_coarse_slots(kMaxSplitGrouped)];
@@ -789,10 +789,18 @@ constexpr int kMaxGroupedTiles = 1 << 30;   // workgroups of one grouped launch
 // (streamed from HBM) WL chunks ahead, per limb count. With eight waves per
 // workgroup one step of x lead is enough (two measured 1-3 % slower).
 template <int NL> struct SmallLead { static constexpr int XL = 1, WL = 1; };
+// K chunks of at most kChunkGroups groups, or shorter (down to kMinChunkGroups)
+// when a call has too few workgroups to fill the GPU and runs the finish pass
+// anyway (a projection with K above 16 groups, or a bias): a small call (one
+// block) then walks its K in parallel chunks at no extra launch. A call that
+// would need the finish pass only for shorter chunks keeps them long: there
+// the extra launch costs more host time than the shorter K walk saves.
 constexpr int kChunkGroups = 16;
-__host__ __device__ inline int split_chunks(int K) {
+constexpr int kMinChunkGroups = 4;
+constexpr int kFillTiles = 256;             // one workgroup per CU
+__host__ __device__ inline int split_chunks(int K, int chunk_groups) {
     const int G = K / 32;
-    return (G + kChunkGroups - 1) / kChunkGroups;
+    return (G + chunk_groups - 1) / chunk_groups;
 }
 
 template <int TM, int NL>
@@ -808,7 +816,7 @@ __global__ __launch_bounds__(64 * kSmallWaves) void split_grouped_kernel(SplitGr
     const int begin = g.tile_begin[i];
     const int K = g.k[i];
     const int G = K / 32;
-    const int ks = split_chunks(K);
+    const int ks = split_chunks(K, g.chunk_groups);
     const int local = w - begin;
     const int cb = local / ks, kc = local % ks;
     const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
@@ -979,6 +987,7 @@ namespace {
 struct SplitPlan {
     bool small = false;     // grouped small-M launch (else one tiled launch per projection)
     int RB = 0;             // 16-row blocks of every image
+    int chunk_groups = kChunkGroups;   // K chunk length of the grouped launch
     int n_in = 0;
     Input inputs[8 * 64];
     int img_of[8 * 64];
@@ -1010,9 +1019,23 @@ void plan_split(const ProjTask* tasks, int count, int M, int NL, SplitPlan& p) {
         if (!p.small || p.ws_bytes <= int64_t(UINT32_MAX)) break;
         p.small = false;
     }
+    // Shorter K chunks while the grouped launch would leave CUs idle.
+    p.chunk_groups = kChunkGroups;
+    bool finishes = false;
+    for (int i = 0; i < count; ++i)
+        finishes = finishes || split_chunks(tasks[i].K, kChunkGroups) > 1 || tasks[i].bias != nullptr;
+    if (p.small && finishes) {
+        for (;;) {
+            int64_t tiles = 0;
+            for (int i = 0; i < count; ++i)
+                tiles += int64_t(tasks[i].N + kSmallBN - 1) / kSmallBN * split_chunks(tasks[i].K, p.chunk_groups);
+            if (tiles >= kFillTiles || p.chunk_groups <= kMinChunkGroups) break;
+            p.chunk_groups /= 2;
+        }
+    }
     for (int i = 0; i < count; ++i) {
         p.part_off[i] = -1;
-        const int ks = split_chunks(tasks[i].K);
+        const int ks = split_chunks(tasks[i].K, p.chunk_groups);
         if (p.small && ks > 1) {
             p.part_off[i] = p.ws_bytes;
             p.ws_bytes += (int64_t(ks) * M * tasks[i].N * 4 + 255) / 256 * 256;
@@ -1085,15 +1108,17 @@ hipError_t split_impl(const ProjTask* tasks, int count, int64_t M64, int NL, hip
             SplitGroupArgs g{};
             g.M = M;
             g.RB = RB;
+            g.chunk_groups = plan.chunk_groups;
             g.ws = wsb;
             int tiles = 0;
             while (done < count && g.count < kMaxSplitGrouped &&
-                   tiles + (tasks[order[done]].N + kSmallBN - 1) / kSmallBN * split_chunks(tasks[order[done]].K) <=
+                   tiles + (tasks[order[done]].N + kSmallBN - 1) / kSmallBN *
+                                   split_chunks(tasks[order[done]].K, plan.chunk_groups) <=
                        kMaxGroupedTiles) {
                 const int ti = order[done++];
                 const ProjTask& t = tasks[ti];
                 const int c = g.count++;
-                const int ks = split_chunks(t.K);
+                const int ks = split_chunks(t.K, plan.chunk_groups);
                 g.img_off[c] = static_cast<uint32_t>(inputs[img_of[ti]].offset);
                 g.payload[c] = t.payload;
                 g.scale[c] = t.scale;
