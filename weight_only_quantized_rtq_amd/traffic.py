@@ -20,34 +20,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm_direct.hip", "gemm.hip", "rtq_internal
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 126 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33087.285, "write_kib": 36090.515,
+    ("m80", "split16"): {"fetch_kib": 33067.394, "write_kib": 36222.072,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38775.452, "write_kib": 35986.164,
+    ("m80", "split"): {"fetch_kib": 38760.826, "write_kib": 35882.621,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27717.398, "write_kib": 37156.455,
+    ("m80", "bf16"): {"fetch_kib": 27667.394, "write_kib": 36894.738,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 480 dispatches per counter run
     # (5 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 109496.123, "write_kib": 233058.093,
+    ("m65536", "split16"): {"fetch_kib": 109570.332, "write_kib": 233049.94,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
-    ("m65536", "split"): {"fetch_kib": 173504.981, "write_kib": 230887.373,
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
+    ("m65536", "split"): {"fetch_kib": 174548.197, "write_kib": 230869.771,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
-    ("m65536", "bf16"): {"fetch_kib": 51788.863, "write_kib": 234043.021,
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
+    ("m65536", "bf16"): {"fetch_kib": 51795.342, "write_kib": 234031.618,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "2ae3b1e85b4feafd25a98aeffac0136d0433149d8663b4203ade024583a8d306"},
+         "sources_sha256": "f6c089cb96dbe52ea1773dfcf9ccd8a3c4e45ff982e15163f8a6124f11b1235c"},
 }
 
 
