@@ -202,12 +202,14 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
             const int col0 = n0 + wave * TN * 16 + tn * 16;
 #pragma unroll
             for (int i = 0; i < PIECES; ++i) {
-                const int o = i * 1024 + lane * 16;                       // byte of the tile's block
-                if (o < PTILE) {
-                    const int r = o / (4 * G), w = o - r * (4 * G);
-                    const uint32_t row = static_cast<uint32_t>(min(col0 + r, N - 1));
-                    pv[tn][i] = *reinterpret_cast<const uint4*>(pairs + row * (4u * G) + w);
-                }
+                // byte of the tile's block; lanes past it (K = 256) load the
+                // first piece again, so that no branch surrounds the load (a
+                // load under a branch kept the pieces in scratch memory)
+                const int o0 = i * 1024 + lane * 16;
+                const int o = o0 < PTILE ? o0 : o0 - PTILE;
+                const int r = o / (4 * G), w = o - r * (4 * G);
+                const uint32_t row = static_cast<uint32_t>(min(col0 + r, N - 1));
+                pv[tn][i] = *reinterpret_cast<const uint4*>(pairs + row * (4u * G) + w);
             }
         }
     };
