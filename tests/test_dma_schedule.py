@@ -12,8 +12,10 @@ the kernel source with g++ and:
     many in flight, a chunk issued one step early, an x stage issued two steps
     ahead into a two-slot ring, a prologue that skips an x stage, and a wait
     count that ignores the order of a step's stage and chunk (waits stricter
-    than needed are rejected too), and the constant steady-state wait used on the
-    first step, where the prologue's loads are still in flight.
+    than needed are rejected too), the constant steady-state wait used on the
+    first step, where the prologue's loads are still in flight, the head's
+    large-GS wait constants taken for too short a K walk, and the tail's wait
+    constants with the step parity swapped.
 """
 import os
 import shutil
@@ -40,8 +42,12 @@ MUTANTS = {
     "prologue_skips_stage": ("return need <= XL && need < GS; }", "return need < XL && need < GS; }"),
     "chunk_before_stage_in_key": ("return c <= WL ? 4 * c : 4096 + 2 * (2 * c - 2 * WL) + 1; }",
                                   "return c <= WL ? 4 * c : 4096 + 2 * (2 * c - 2 * WL) - 1; }"),
-    "steady_from_first_step": ("return i > kPrologue && i + kPrologue + 1 < GS; }",
-                               "return i >= 0 && i + kPrologue + 1 < GS; }"),
+    "steady_from_first_step": ("static constexpr int kSteadyLo = kPrologue + 1;",
+                               "static constexpr int kSteadyLo = 0;"),
+    "head_constant_too_early": ("static constexpr int kBig = 2 * kPrologue + 3;",
+                                "static constexpr int kBig = kPrologue;"),
+    "tail_parity_swapped": ("return allowed(2 * kPrologue + 2 + parity, 2 * kPrologue + 3 + parity + r); }",
+                            "return allowed(2 * kPrologue + 3 - parity, 2 * kPrologue + 4 - parity + r); }"),
 }
 
 

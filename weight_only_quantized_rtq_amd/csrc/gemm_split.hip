@@ -61,6 +61,7 @@
 //  4. Workgroup ids are remapped so that each XCD runs a contiguous range of
 //     tiles: the tiles that share an activation image share that XCD's L2.
 #include <mutex>
+#include <type_traits>
 
 #include "rtq_internal.h"
 #include "split_device.h"
@@ -244,11 +245,24 @@ struct Lds {
     static constexpr int XSLOT = BM <= 96 ? 96 : 128;
     static constexpr int WRING = XRING + kRing * XSLOT * 4;
     static constexpr int WCHUNK = TN * 1024;
-    static constexpr int TOTAL = WRING + (WL > 0 ? NWSLOT * NW * WCHUNK : 0);
+    // the tile's row exponents, copied in 64-row pieces before the first stage
+    static constexpr int EXPS = WRING + (WL > 0 ? NWSLOT * NW * WCHUNK : 0);
+    static constexpr int NEXP = (BM + 63) / 64;
+    static constexpr int TOTAL = EXPS + NEXP * 256;
     static constexpr int COPIES = (BM / 16) * NL;                  // 1 KB copies per stage
     static constexpr int PER_WAVE = (COPIES + NW - 1) / NW;
     static_assert(BM <= XSLOT, "group-sum slot holds every row of the tile");
+    static_assert(NEXP <= NW, "one exponent copy per wave at most");
 };
+
+// f(std::integral_constant<int, i>) for i = B .. E-1, expanded at compile time.
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
 
 // Wait until at most N vector-memory operations of this wave are in flight.
 template <int N>
@@ -313,10 +327,21 @@ struct DmaSchedule {
     // after the barrier of iteration i: stage i + XL, then chunk i/2 + WL
     __host__ __device__ static constexpr bool it_stage(int i, int GS) { return i >= 1 && i + XL < GS; }
     __host__ __device__ static constexpr bool it_chunk(int i, int GS) { return i >= 2 && (i & 1) == 0 && i + 2 * WL < GS; }
-    // Away from both ends the count depends on the parity of i only: the loop
-    // uses these constants there (verify() checks they equal allowed()).
-    __host__ __device__ static constexpr bool steady_at(int i, int GS) { return i > kPrologue && i + kPrologue + 1 < GS; }
+    // Away from both ends (steps kSteadyLo .. steady_hi(GS) - 1) the count
+    // depends on the parity of i only, and every step issues its stage (and,
+    // when even, its chunk): the loop runs those steps in pairs with these
+    // constants (verify() checks them against allowed() and it_*()).
+    static constexpr int kSteadyLo = kPrologue + 1;
+    __host__ __device__ static constexpr int steady_hi(int GS) { return GS - kPrologue - 1; }
+    __host__ __device__ static constexpr bool steady_at(int i, int GS) { return i >= kSteadyLo && i < steady_hi(GS); }
     static constexpr int steady(int parity) { return allowed(2 * kPrologue + 2 + parity, 1 << 20); }
+    // The first kSteadyLo steps (the head) take allowed(h, kBig) once GS >= kBig.
+    static constexpr int kBig = 2 * kPrologue + 3;
+    // Past the head, a step r steps before the last takes tail(r, parity): the
+    // count depends only on r and the parity of the step. At most kTail steps
+    // follow the steady pairs.
+    static constexpr int kTail = kPrologue + 2;
+    static constexpr int tail(int r, int parity) { return allowed(2 * kPrologue + 2 + parity, 2 * kPrologue + 3 + parity + r); }
     __host__ __device__ static constexpr int allowed(int i, int GS) {
         const int need = stage_key(i) > chunk_key(i / 2) ? stage_key(i) : chunk_key(i / 2);
         int n = 0;
@@ -370,6 +395,14 @@ struct DmaSchedule {
                 if (!have_s || !have_c) return false;
                 if (a != issued - (last + 1)) return false;                // no stricter wait than needed
                 if (steady_at(i, GS) && a != steady(i & 1)) return false;
+                if (steady_at(i, GS) && !(it_stage(i, GS) && it_chunk(i, GS) == ((i & 1) == 0))) return false;
+                if (i < kSteadyLo && GS >= kBig && a != allowed(i, kBig)) return false;
+                if (i >= kSteadyLo) {                                      // closed forms of the tail
+                    const int r = GS - 1 - i;
+                    if (a != tail(r, i & 1)) return false;
+                    if (it_stage(i, GS) != (r >= XL)) return false;
+                    if (it_chunk(i, GS) != ((i & 1) == 0 && r >= 2 * WL)) return false;
+                }
                 if (sslot[i % (XL + 1)] != i || cslot[(i / 2) % (WL + 1)] != i / 2) return false;
                 if (it_stage(i, GS)) issue(0, i + XL, i);
                 if (it_chunk(i, GS)) issue(1, i / 2 + WL, i);
@@ -642,6 +675,24 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     //      LDS stages and weight slots. A stage or slot is refilled only after
     //      the barrier that follows every wave's last read of it. ----
     uint32_t wq[TN][2], wp[TN], cq[TN][2], cp[TN];
+    // The epilogue's operands are fetched before any stage: the tile's row
+    // exponents by DMA into LDS (waves 0 .. NEXP-1, 64 rows each), this wave's
+    // int8 scales into registers. These are the oldest loads of the wave, so
+    // the first step's wait covers them without changing the schedule's
+    // in-flight counts below, and the first barrier publishes the exponents
+    // to every wave. (Biases, rare, are read in the epilogue.)
+    if (wave < L::NEXP) {
+        const int* exps = reinterpret_cast<const int*>(a.img + image_exp_offset(G, RB, NL));
+        dma4(exps + min(m0 + wave * 64 + lane, RB * 16 - 1), smem + L::EXPS + wave * 256);
+    }
+    float escale[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        if constexpr (FMT == kFmtQ8)
+            escale[tn] = static_cast<const float*>(a.scale)[min(n0 + wn * TN * 16 + tn * 16 + li, N - 1)];
+        else
+            escale[tn] = 1.0f;
+    }
     // With WL > 0 the x stages and weight chunks follow DmaSchedule (above).
     constexpr int NX = L::PER_WAVE + 1;
     constexpr int NWC = TN;
@@ -658,23 +709,15 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
             if (Sched::pro_stage(need, GS)) stage_copy(need);
         }
     }
-    for (int i = 0; i < GS; ++i) {
-        if constexpr (WL == 0) {
+    // Barrier without a memory fence: the LDS data of step i came in by DMA
+    // and is complete after the wait before it (in every wave, after the
+    // barrier); nothing else writes LDS, and a fence would also wait for later
+    // steps.
+    if constexpr (WL == 0) {
+        for (int i = 0; i < GS; ++i) {
             wait_vm<0>();                                 // this wave's part of step i has landed
-        } else {
-            if (Sched::steady_at(i, GS)) {
-                if (i & 1) wait_vm<Sched::steady(1)>();
-                else wait_vm<Sched::steady(0)>();
-            } else {
-                wait_vm_upto<Sched::kMax>(Sched::allowed(i, GS));
-            }
-        }
-        // Barrier without a memory fence: the LDS data of step i came in by DMA
-        // and is complete after the wait above (in every wave, after the barrier);
-        // nothing else writes LDS, and a fence would also wait for later steps.
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (WL == 0) {
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 cq[tn][0] = wq[tn][0];
@@ -685,33 +728,71 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
                 stage_copy(i + 1);
                 w_load(i + 1, wq, wp);
             }
-        } else {
-            w_read(i, cq, cp);
-            if (Sched::it_stage(i, GS)) stage_copy(i + XL);
-            if (Sched::it_chunk(i, GS)) w_chunk_issue(i / 2 + WL);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(i, cq, cp);
+            min_flush(i);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        compute(i, cq, cp);
-        min_flush(i);
+    } else {
+        // Step i after its wait: barrier, this step's weights from LDS, the
+        // stage / chunk the schedule issues here, the arithmetic.
+        auto step = [&](int i, bool issue_stage, bool issue_chunk) {
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            w_read(i, cq, cp);
+            if (issue_stage) stage_copy(i + XL);
+            if (issue_chunk) w_chunk_issue(i / 2 + WL);
+            __builtin_amdgcn_sched_barrier(0);
+            compute(i, cq, cp);
+            min_flush(i);
+        };
+        // The head (steps 0 .. kSteadyLo - 1, unrolled) and the tail (at most
+        // kTail steps, unrolled by their distance r from the last) take their
+        // waits as constants; only a call with fewer than kBig steps evaluates
+        // allowed() in the head. The steady steps run in pairs of known parity.
+        static_for<0, Sched::kSteadyLo>([&](auto hc) {
+            constexpr int h = decltype(hc)::value;
+            if (h < GS) {
+                if (GS >= Sched::kBig) wait_vm<Sched::allowed(h, Sched::kBig)>();
+                else wait_vm_upto<Sched::kMax>(Sched::allowed(h, GS));
+                step(h, Sched::it_stage(h, GS), Sched::it_chunk(h, GS));
+            }
+        });
+        constexpr int P0 = Sched::kSteadyLo & 1;          // parity of the first step of each pair
+        int i = Sched::kSteadyLo;
+        for (; i + 1 < Sched::steady_hi(GS); i += 2) {
+            wait_vm<Sched::steady(P0)>();
+            step(i, true, P0 == 0);
+            wait_vm<Sched::steady(1 - P0)>();
+            step(i + 1, true, P0 == 1);
+        }
+        static_for<0, Sched::kTail>([&](auto rc) {
+            constexpr int r = Sched::kTail - 1 - decltype(rc)::value;
+            const int j = GS - 1 - r;
+            if (j >= i) {
+                if (j & 1) wait_vm<Sched::tail(r, 1)>();
+                else wait_vm<Sched::tail(r, 0)>();
+                step(j, r >= XL, (j & 1) == 0 && r >= 2 * WL);
+            }
+        });
     }
 
     // ---- epilogue: lane holds D[4*lc + e][li] of each 16x16 tile. Each row
     //      is scaled back by 2^-e[row] (exact) after the int8 scale and before
     //      the bias. ----
     int rexp[TM][4];
-    {
-        const int* exps = reinterpret_cast<const int*>(a.img + image_exp_offset(G, RB, NL));
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) rexp[tm][e] = -exps[min(m0 + wm * TM * 16 + tm * 16 + 4 * lc + e, RB * 16 - 1)];
+    for (int tm = 0; tm < TM; ++tm) {
+        const int4 v = *reinterpret_cast<const int4*>(smem + L::EXPS + (wm * TM * 16 + tm * 16 + 4 * lc) * 4);
+        rexp[tm][0] = -v.x;
+        rexp[tm][1] = -v.y;
+        rexp[tm][2] = -v.z;
+        rexp[tm][3] = -v.w;
     }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + wn * TN * 16 + tn * 16 + li;
         if (col >= N) continue;
-        float sc = 1.0f;
-        if constexpr (FMT == kFmtQ8) sc = static_cast<const float*>(a.scale)[col];
+        const float sc = escale[tn];
         const float bv = a.bias ? a.bias[col] : 0.0f;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
@@ -748,7 +829,9 @@ template <int NL> struct LargeLead { static constexpr int XL = NL == 3 ? 0 : 1, 
 template <int FMT, int NL>
 __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_n) {
     constexpr int XL = LargeLead<NL>::XL, WL = LargeLead<NL>::WL;
-    __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<kLBM, WL ? kLTN : 1, XL, WL, NL>::TOTAL];
+    using L = Lds<kLBM, WL ? kLTN : 1, XL, WL, NL>;
+    static_assert(L::TOTAL * (NL == 1 ? 4 : 3) <= 160 * 1024, "three workgroups per CU (four with one limb)");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[L::TOTAL];
     const int w = xcd_remap_split(blockIdx.x, gridDim.x);
     const int nt = w % tiles_n;
     split_tile<FMT, kLWM, kLWN, kLTM, kLTN, XL, WL, NL, true>(a, (w / tiles_n) * kLBM, nt * kLBN, nt % a.g_cnt, smem);
@@ -804,7 +887,7 @@ __host__ __device__ inline int split_chunks(int K, int chunk_groups) {
 }
 
 template <int TM, int NL>
-__global__ __launch_bounds__(64 * kSmallWaves) void split_grouped_kernel(SplitGroupArgs g) {
+__global__ __launch_bounds__(64 * kSmallWaves, 4) void split_grouped_kernel(SplitGroupArgs g) {
     constexpr int XL = SmallLead<NL>::XL, WL = SmallLead<NL>::WL;
     __shared__ __attribute__((aligned(16))) unsigned char smem[Lds<TM * 16, kSmallTN, XL, WL, NL, kSmallWaves>::TOTAL];
     // Find this workgroup's projection: tiles are numbered projection by
