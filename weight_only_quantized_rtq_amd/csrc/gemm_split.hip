@@ -94,15 +94,11 @@ __host__ __device__ inline int64_t image_bytes(int G, int RB, int NL) {
 
 constexpr int kMaxImages = 48;
 struct PrepArgs {
-    int count;
-    int pad;
+    int M;                              // rows of every image of the launch
+    int RB;                             // their 16-row blocks
     const float* x[kMaxImages];
     unsigned char* img[kMaxImages];
-    int M[kMaxImages];
     int K[kMaxImages];
-    int RB[kMaxImages];
-    int block_begin[seg_begin_slots(kMaxImages + 1)];    // 256-thread blocks per image, prefix
-    int block_coarse[seg_coarse_slots(kMaxImages + 1)];
 };
 static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
@@ -120,13 +116,13 @@ static_assert(sizeof(PrepArgs) <= 4096, "kernel arguments must stay within 4 KiB
 // then chunks (0+1)+(2+3). Rows of K <= 512*kPrepHold stay in registers
 // between the two passes; longer rows are read again.
 constexpr int kPrepHold = 4;
+// Grid: (RB * 4, images); blockIdx.y is the image, blockIdx.x its four rows.
 template <int NL>
 __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
-    const int b = blockIdx.x;
-    const int i = segment_of(p.block_begin, p.block_coarse, p.count, b);
-    const int M = p.M[i], K = p.K[i], RB = p.RB[i];
+    const int i = blockIdx.y;
+    const int M = p.M, K = p.K[i], RB = p.RB;
     const int G = K / 32;
-    const int row = (b - p.block_begin[i]) * 4 + static_cast<int>(threadIdx.x >> 6);   // < RB * 16
+    const int row = static_cast<int>(blockIdx.x) * 4 + static_cast<int>(threadIdx.x >> 6);   // < RB * 16
     const int lane = threadIdx.x & 63;
     const int c = lane & 3;
     const int r = row & 15, rb = row >> 4;
@@ -977,26 +973,23 @@ hipError_t run_prep(const Input* in, int n_in, unsigned char* ws, int M, int RB,
     int done = 0;
     while (done < n_in) {
         PrepArgs p{};
-        int blocks = 0;
-        while (done < n_in && p.count < kMaxImages) {
+        p.M = M;
+        p.RB = RB;
+        int count = 0;
+        while (done < n_in && count < kMaxImages) {
             const Input& u = in[done++];
-            const int c = p.count++;
-            p.x[c] = u.x;
-            p.img[c] = ws + u.offset;
-            p.M[c] = M;
-            p.K[c] = u.K;
-            p.RB[c] = RB;
-            p.block_begin[c] = blocks;
-            blocks += RB * 4;                               // one wave per row
+            p.x[count] = u.x;
+            p.img[count] = ws + u.offset;
+            p.K[count] = u.K;
+            ++count;
         }
-        p.block_begin[p.count] = blocks;
-        seg_fill_coarse(p.block_begin, p.block_coarse, p.count);
+        const dim3 grid(RB * 4, count);                     // one wave per row
         if (NL == 1)
-            prep_kernel<1><<<blocks, 256, 0, stream>>>(p);
+            prep_kernel<1><<<grid, 256, 0, stream>>>(p);
         else if (NL == 2)
-            prep_kernel<2><<<blocks, 256, 0, stream>>>(p);
+            prep_kernel<2><<<grid, 256, 0, stream>>>(p);
         else
-            prep_kernel<3><<<blocks, 256, 0, stream>>>(p);
+            prep_kernel<3><<<grid, 256, 0, stream>>>(p);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
