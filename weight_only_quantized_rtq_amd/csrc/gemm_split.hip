@@ -77,7 +77,9 @@ namespace {
 //   limb 0 = x1 (high), 1 = x2, 2 = x3, with NL = 1 the bf16-rounded x, with
 //   NL = 2 the fp16 limbs h, l of the scaled row; inside a limb, row r (0..15)
 //   and 16-byte chunk c (k = 8c..8c+7 of the group) sit at
-//   (r*4 + (c ^ ((r>>2)&3))) * 16;
+//   (r*4 + (c ^ ((r>>2)&3))) * 16; a chunk holds its eight k in order, except
+//   with NL = 2, where it holds k = 8c + 0, 4, 1, 5, 2, 6, 3, 7 (the order in
+//   which the two-limb code conversions produce the weights);
 //   then the group sums X[g][row] (fp32, RB*16 rows per group);
 //   then the row exponents e[row] (int32, RB*16 rows): row `row` of x was
 //   scaled by 2^e[row] before the split.
@@ -171,7 +173,7 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
             if constexpr (NL == 3) {
                 split2(v[2 * q], v[2 * q + 1], h[q], m[q], l[q]);
             } else if constexpr (NL == 2) {
-                split_f16x2(v[2 * q], v[2 * q + 1], h[q], l[q]);
+                split_f16x2(v[q], v[q + 4], h[q], l[q]);          // k order 0, 4, 1, 5, ...
             } else {
                 h[q] = bf16x2_rne(v[2 * q], v[2 * q + 1]);
                 v[2 * q] = bitsf(h[q] << 16);               // the group sum is over the rounded values
@@ -605,14 +607,14 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             if constexpr (FMT == kFmtQ4) {
-                b[tn] = NL == 2 ? codes4_to_f16(cq[tn][0]) : codes4_to_bf16(cq[tn][0]);
+                b[tn] = NL == 2 ? codes4_to_f16_k04(cq[tn][0]) : codes4_to_bf16(cq[tn][0]);
                 s[tn] = half_bits_to_float(cp[tn] & 0xffffu);
                 const float mn = half_bits_to_float(cp[tn] >> 16);
                 mreg[tn] = lc == (i & 3) ? mn : mreg[tn];
             } else if constexpr (FMT == kFmtF8) {
-                b[tn] = NL == 2 ? codes8f_to_f16(cq[tn][0], cq[tn][1]) : codes8f_to_bf16(cq[tn][0], cq[tn][1]);
+                b[tn] = NL == 2 ? codes8f_to_f16_k04(cq[tn][0], cq[tn][1]) : codes8f_to_bf16(cq[tn][0], cq[tn][1]);
             } else {
-                b[tn] = NL == 2 ? codes8_to_f16(cq[tn][0], cq[tn][1]) : codes8_to_bf16(cq[tn][0], cq[tn][1]);
+                b[tn] = NL == 2 ? codes8_to_f16_k04(cq[tn][0], cq[tn][1]) : codes8_to_bf16(cq[tn][0], cq[tn][1]);
             }
         }
         // the limb products, smallest limb first

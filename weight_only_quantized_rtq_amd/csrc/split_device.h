@@ -143,6 +143,66 @@ __device__ __forceinline__ u32x4 codes8f_to_f16(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// The same conversions in the two-limb k order: word j of the result holds
+// the codes of k = j (low half) and k = j + 4 (high half), so an operand's
+// eight k of a lane run 0, 4, 1, 5, 2, 6, 3, 7. The limb image of the
+// two-limb arithmetic stores x in that order (prep_kernel<2>). For int4 the
+// nibbles of k and k + 4 sit 16 bits apart in the payload word, so one
+// and-or puts both under the fp16 exponent byte 0x64: 1024 + c for the low
+// nibble of a byte, 1024 + 16c for the high nibble (then (t/16) - 64 in one
+// fp16 fma, exact: t/16 = 64 + c).
+__device__ __forceinline__ uint32_t f16x2_fma(uint32_t w, _Float16 m, _Float16 c) {
+    const f16x2 r = __builtin_elementwise_fma(__builtin_bit_cast(f16x2, w), f16x2{m, m}, f16x2{c, c});
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// (w & mask) | e in one v_and_or_b32 (the compiler splits it when both
+// constants are literals); e is passed in a VGPR, the mask in an SGPR.
+__device__ __forceinline__ uint32_t and_or(uint32_t w, uint32_t mask, uint32_t e) {
+    uint32_t r;
+    asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(mask), "v"(e));
+    return r;
+}
+
+__device__ __forceinline__ u32x4 codes4_to_f16_k04(uint32_t w) {
+    const uint32_t e = 0x64006400u;
+    const uint32_t t = w >> 8;
+    u32x4 r;
+    r[0] = f16x2_sub(and_or(w, 0x000f000fu, e), 1024.0f16);                   // k 0, 4
+    r[1] = f16x2_fma(and_or(w, 0x00f000f0u, e), 0.0625f16, -64.0f16);         // k 1, 5
+    r[2] = f16x2_sub(and_or(t, 0x000f000fu, e), 1024.0f16);                   // k 2, 6
+    r[3] = f16x2_fma(and_or(t, 0x00f000f0u, e), 0.0625f16, -64.0f16);         // k 3, 7
+    return r;
+}
+
+// 8 int8 codes (bytes 0..3 of w0, 4..7 of w1) -> fp16 in the k order 0, 4, 1, 5, ...
+__device__ __forceinline__ u32x4 codes8_to_f16_k04(uint32_t w0, uint32_t w1) {
+    const uint32_t t0 = w0 ^ 0x80808080u, t1 = w1 ^ 0x80808080u;
+    const uint32_t lo = __builtin_amdgcn_perm(t1, t0, 0x05010400u);    // bytes: k 0, 4, 1, 5
+    const uint32_t hi = __builtin_amdgcn_perm(t1, t0, 0x07030602u);    // k 2, 6, 3, 7
+    constexpr uint32_t k64 = 0x64646464u;
+    u32x4 r;
+    r[0] = f16x2_sub(__builtin_amdgcn_perm(k64, lo, 0x04010400u), 1152.0f16);
+    r[1] = f16x2_sub(__builtin_amdgcn_perm(k64, lo, 0x04030402u), 1152.0f16);
+    r[2] = f16x2_sub(__builtin_amdgcn_perm(k64, hi, 0x04010400u), 1152.0f16);
+    r[3] = f16x2_sub(__builtin_amdgcn_perm(k64, hi, 0x04030402u), 1152.0f16);
+    return r;
+}
+
+// 8 FP8 E4M3 codes -> fp16 in the k order 0, 4, 1, 5, ... (exact, as above).
+__device__ __forceinline__ u32x4 codes8f_to_f16_k04(uint32_t w0, uint32_t w1) {
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), false);   // k 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w0), true);    // k 2, 3
+    const auto c = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), false);   // k 4, 5
+    const auto d = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w1), true);    // k 6, 7
+    u32x4 r;
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[0], c[0]));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a[1], c[1]));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[0], d[0]));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b[1], d[1]));
+    return r;
+}
+
 __device__ __forceinline__ floatx4 mfma_f16(u32x4 a, u32x4 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c,
                                                   0, 0, 0);
