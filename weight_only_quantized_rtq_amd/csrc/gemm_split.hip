@@ -839,21 +839,29 @@ __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_
 // every projection of the call in one launch.
 constexpr int kMaxSplitGrouped = 96;
 
+// One projection of a grouped launch: 36 bytes, so the kernel reads all of it
+// with two scalar loads (pointers as two dwords keep it dword-aligned).
+struct GroupedProj {
+    uint32_t payload[2];                // packed weights (int4 payload / int8 / FP8 codes)
+    uint32_t scale[2];                  // int4 (scale, min) pairs or int8 row scales
+    uint32_t y[2];                      // output, or the partial buffer [ks][M][N] when K spans ks > 1 chunks
+    uint32_t img_off;                   // byte offset of the projection's limb image in the workspace
+    uint32_t n_fmt;                     // N | format << 30 (a split projection has N < 2^27)
+    int k;
+};
+static_assert(sizeof(GroupedProj) == 36, "grouped descriptor layout");
+
 struct SplitGroupArgs {
     int count;
     int M;
     int RB;
     int chunk_groups;                       // K chunk length in groups (split_chunks)
+    int tiles;                              // workgroups of the launch
+    int pad;
     const unsigned char* ws;                // workspace holding the limb images
     int tile_begin[seg_begin_slots(kMaxSplitGrouped)];   // first workgroup of each projection
     int tile_coarse[seg_coarse_slots(kMaxSplitGrouped)];
-    uint32_t img_off[kMaxSplitGrouped];     // byte offset of the projection's limb image in ws
-    const void* payload[kMaxSplitGrouped];
-    const void* scale[kMaxSplitGrouped];
-    float* y[kMaxSplitGrouped];
-    int n[kMaxSplitGrouped];
-    int k[kMaxSplitGrouped];
-    uint8_t fmt[kMaxSplitGrouped];      // y[] is the partial buffer [ks][M][N] when K spans ks > 1 chunks
+    GroupedProj proj[kMaxSplitGrouped];
 };
 static_assert(sizeof(SplitGroupArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
@@ -892,23 +900,66 @@ __global__ __launch_bounds__(64 * kSmallWaves, 4) void split_grouped_kernel(Spli
     // projection, (column block, K chunk) within one. Consecutive tiles go to
     // one XCD, so the column tiles that read the same activation image share
     // that XCD's L2 instead of each fetching the image from memory.
-    const int w = xcd_remap_split(blockIdx.x, gridDim.x);
-    const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
-    const int begin = g.tile_begin[i];
-    const int K = g.k[i];
+    // Argument loads in three rounds: the header with the coarse table, the
+    // run of the fine table the coarse table points at (which also holds the
+    // projection's first workgroup), and the projection's descriptor. The
+    // launch's size comes with the arguments, not from the dispatch packet.
+    constexpr int NC = seg_coarse_slots(kMaxSplitGrouped);
+    static_assert(NC == 12, "the round-one operand list below names twelve coarse slots");
+    const int count = g.count, tiles = g.tiles;
+    const int M = g.M, RB = g.RB, chunk_groups = g.chunk_groups;
+    const unsigned char* ws = g.ws;
+    int coarse[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) coarse[j] = g.tile_coarse[j];
+    // Each empty asm below takes the round's values as scalar operands, so
+    // the compiler issues all of that round's loads before its one wait
+    // (scalar loads return out of order: any use waits for all of them).
+    asm volatile("" ::"s"(count), "s"(tiles), "s"(M), "s"(RB), "s"(chunk_groups), "s"(ws), "s"(coarse[0]), "s"(coarse[1]), "s"(coarse[2]), "s"(coarse[3]),
+                 "s"(coarse[4]), "s"(coarse[5]), "s"(coarse[6]), "s"(coarse[7]), "s"(coarse[8]), "s"(coarse[9]),
+                 "s"(coarse[10]), "s"(coarse[11]));
+    const int w = xcd_remap_split(blockIdx.x, tiles);
+    int c = 0;
+#pragma unroll
+    for (int j = 1; j < NC; ++j) c += static_cast<int>(j * kSegStride < count) & static_cast<int>(coarse[j] <= w);
+    c = __builtin_amdgcn_readfirstlane(c);
+    asm volatile("" : "+s"(c));
+    const int base = c * kSegStride;
+    int run[kSegStride];
+#pragma unroll
+    for (int j = 0; j < kSegStride; ++j) run[j] = g.tile_begin[base + j];
+    int i = base, begin = run[0];
+#pragma unroll
+    for (int j = 1; j < kSegStride; ++j) {
+        const bool in = base + j < count && run[j] <= w;
+        i += static_cast<int>(in);
+        begin = in ? run[j] : begin;
+    }
+    i = __builtin_amdgcn_readfirstlane(i);
+    asm volatile("" : "+s"(i));
+    const GroupedProj d = g.proj[i];
+    const int K = d.k;
+    const uint32_t n_fmt = d.n_fmt;
+    const uint32_t img_off = d.img_off;
+    auto ptr = [](const uint32_t (&v)[2]) { return reinterpret_cast<void*>((static_cast<uint64_t>(v[1]) << 32) | v[0]); };
+    const void* payload = ptr(d.payload);
+    const void* scale = ptr(d.scale);
+    float* y0 = static_cast<float*>(ptr(d.y));
+    asm volatile("" ::"s"(K), "s"(n_fmt), "s"(img_off), "s"(payload), "s"(scale), "s"(y0));
+    const int N = static_cast<int>(n_fmt & 0x3fffffffu);
+    const int fmt = static_cast<int>(n_fmt >> 30);
     const int G = K / 32;
-    const int ks = split_chunks(K, g.chunk_groups);
+    const int ks = split_chunks(K, chunk_groups);
     const int local = w - begin;
     const int cb = local / ks, kc = local % ks;
     const int g_lo = kc * G / ks, g_hi = (kc + 1) * G / ks;
-    float* y = g.y[i] + static_cast<int64_t>(ks > 1 ? kc : 0) * g.M * g.n[i];
+    float* y = y0 + static_cast<int64_t>(ks > 1 ? kc : 0) * M * N;
     // Biases of grouped projections are added by finish_kernel.
-    const SplitArgs a{g.ws + g.img_off[i], g.payload[i], g.scale[i], y, g.M, g.n[i], K, g.RB, g_lo, g_hi - g_lo,
-                      nullptr};
+    const SplitArgs a{ws + img_off, payload, scale, y, M, N, K, RB, g_lo, g_hi - g_lo, nullptr};
     const int rot = cb % (g_hi - g_lo);
-    if (g.fmt[i] == kFmtQ4)
+    if (fmt == kFmtQ4)
         split_tile<kFmtQ4, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
-    else if (g.fmt[i] == kFmtQ8)
+    else if (fmt == kFmtQ8)
         split_tile<kFmtQ8, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
     else
         split_tile<kFmtF8, 1, kSmallWaves, TM, kSmallTN, XL, WL, NL>(a, 0, cb * kSmallBN, rot, smem);
@@ -1197,14 +1248,19 @@ hipError_t split_impl(const ProjTask* tasks, int count, int64_t M64, int NL, hip
                 const ProjTask& t = tasks[ti];
                 const int c = g.count++;
                 const int ks = split_chunks(t.K, plan.chunk_groups);
-                g.img_off[c] = static_cast<uint32_t>(inputs[img_of[ti]].offset);
-                g.payload[c] = t.payload;
-                g.scale[c] = t.scale;
-                g.y[c] = ks > 1 ? reinterpret_cast<float*>(wsb + part_off[ti]) : t.y;
-                g.n[c] = t.N;
-                g.k[c] = t.K;
+                GroupedProj& d = g.proj[c];
+                auto put = [](uint32_t (&v)[2], const void* p) {
+                    const uint64_t u = reinterpret_cast<uintptr_t>(p);
+                    v[0] = static_cast<uint32_t>(u);
+                    v[1] = static_cast<uint32_t>(u >> 32);
+                };
+                put(d.payload, t.payload);
+                put(d.scale, t.scale);
+                put(d.y, ks > 1 ? static_cast<const void*>(wsb + part_off[ti]) : static_cast<const void*>(t.y));
+                d.img_off = static_cast<uint32_t>(inputs[img_of[ti]].offset);
+                d.n_fmt = static_cast<uint32_t>(t.N) | static_cast<uint32_t>(t.fmt) << 30;
+                d.k = t.K;
                 g.tile_begin[c] = tiles;
-                g.fmt[c] = static_cast<uint8_t>(t.fmt);
                 tiles += (t.N + kSmallBN - 1) / kSmallBN * ks;
                 if (ks > 1 || t.bias) {
                     const float* part = ks > 1 ? reinterpret_cast<const float*>(wsb + part_off[ti]) : t.y;
@@ -1213,6 +1269,7 @@ hipError_t split_impl(const ProjTask* tasks, int count, int64_t M64, int NL, hip
                 }
             }
             seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
+            g.tiles = tiles;
             const int mark = timing_begin(stream);
             if (NL == 1)
                 launch_grouped_tm<1>(tm_small, tiles, g, stream);
