@@ -429,19 +429,27 @@ __device__ __forceinline__ void direct_tile(const float* __restrict__ x, const v
     }
 }
 
+// One projection of a direct launch: 32 bytes, read with one scalar load.
+// Packed to 4-byte alignment (the pointers stay pointers, so the compiler
+// still knows they address global memory).
+struct __attribute__((packed, aligned(4))) DirectProj {
+    const void* payload;
+    const void* scale;
+    float* y;
+    int n;
+    uint32_t k_fmt_x;                   // K | format << 16 | input index << 24
+};
+static_assert(sizeof(DirectProj) == 32, "direct descriptor layout");
+
 struct DirectArgs {
     int count;
     int M;
+    int tiles;                          // workgroups of the launch
+    int pad;
     int tile_begin[seg_begin_slots(kDirectMaxProj)];    // first workgroup of each projection
     int tile_coarse[seg_coarse_slots(kDirectMaxProj)];
     const float* xs[kDirectMaxInputs];
-    const void* payload[kDirectMaxProj];
-    const void* scale[kDirectMaxProj];
-    float* y[kDirectMaxProj];
-    int n[kDirectMaxProj];
-    uint16_t k[kDirectMaxProj];
-    uint8_t x_idx[kDirectMaxProj];
-    uint8_t fmt[kDirectMaxProj];
+    DirectProj proj[kDirectMaxProj];
 };
 static_assert(sizeof(DirectArgs) <= 4096, "kernel arguments must stay within 4 KiB");
 
@@ -457,17 +465,57 @@ __device__ __forceinline__ void direct_dispatch_k(int K, const float* x, const v
 template <int TM, int NL>
 __global__ __launch_bounds__(256) void direct_kernel(DirectArgs g) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[DirectLds<NL, TM>::TOTAL];
-    const int w = xcd_remap_split(blockIdx.x, gridDim.x);
-    const int i = segment_of(g.tile_begin, g.tile_coarse, g.count, w);
-    const int K = g.k[i];
-    const int n0 = (w - g.tile_begin[i]) * direct_tn(K) * 64;
-    const float* x = g.xs[g.x_idx[i]];
-    if (g.fmt[i] == kFmtQ4)
-        direct_dispatch_k<kFmtQ4, NL, TM>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
-    else if (g.fmt[i] == kFmtQ8)
-        direct_dispatch_k<kFmtQ8, NL, TM>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
+    // Argument loads in four rounds: the header with the coarse table, the
+    // run of the fine table it points at (which also holds the projection's
+    // first workgroup), the projection's descriptor, its input pointer. Each
+    // empty asm takes a round's values as scalar operands, so the compiler
+    // issues that round's loads before its one wait (scalar loads return out
+    // of order: any use waits for all of them).
+    constexpr int NC = seg_coarse_slots(kDirectMaxProj);
+    static_assert(NC == 12, "the round-one operand list below names twelve coarse slots");
+    const int count = g.count, tiles = g.tiles, M = g.M;
+    int coarse[NC];
+#pragma unroll
+    for (int j = 0; j < NC; ++j) coarse[j] = g.tile_coarse[j];
+    asm volatile("" ::"s"(count), "s"(tiles), "s"(M), "s"(coarse[0]), "s"(coarse[1]), "s"(coarse[2]), "s"(coarse[3]),
+                 "s"(coarse[4]), "s"(coarse[5]), "s"(coarse[6]), "s"(coarse[7]), "s"(coarse[8]), "s"(coarse[9]),
+                 "s"(coarse[10]), "s"(coarse[11]));
+    const int w = xcd_remap_split(blockIdx.x, tiles);
+    int c = 0;
+#pragma unroll
+    for (int j = 1; j < NC; ++j) c += static_cast<int>(j * kSegStride < count) & static_cast<int>(coarse[j] <= w);
+    c = __builtin_amdgcn_readfirstlane(c);
+    asm volatile("" : "+s"(c));
+    const int base = c * kSegStride;
+    int run[kSegStride];
+#pragma unroll
+    for (int j = 0; j < kSegStride; ++j) run[j] = g.tile_begin[base + j];
+    int i = base, begin = run[0];
+#pragma unroll
+    for (int j = 1; j < kSegStride; ++j) {
+        const bool in = base + j < count && run[j] <= w;
+        i += static_cast<int>(in);
+        begin = in ? run[j] : begin;
+    }
+    i = __builtin_amdgcn_readfirstlane(i);
+    asm volatile("" : "+s"(i));
+    const DirectProj d = g.proj[i];
+    const void* payload = d.payload;
+    const void* scale = d.scale;
+    float* y = d.y;
+    const int N = d.n;
+    const uint32_t kfx = d.k_fmt_x;
+    asm volatile("" ::"s"(payload), "s"(scale), "s"(y), "s"(N), "s"(kfx));
+    const int K = static_cast<int>(kfx & 0xffffu);
+    const int fmt = static_cast<int>((kfx >> 16) & 0xffu);
+    const float* x = g.xs[kfx >> 24];
+    const int n0 = (w - begin) * direct_tn(K) * 64;
+    if (fmt == kFmtQ4)
+        direct_dispatch_k<kFmtQ4, NL, TM>(K, x, payload, scale, y, M, N, n0, smem);
+    else if (fmt == kFmtQ8)
+        direct_dispatch_k<kFmtQ8, NL, TM>(K, x, payload, scale, y, M, N, n0, smem);
     else
-        direct_dispatch_k<kFmtF8, NL, TM>(K, x, g.payload[i], g.scale[i], g.y[i], g.M, g.n[i], n0, smem);
+        direct_dispatch_k<kFmtF8, NL, TM>(K, x, payload, scale, y, M, N, n0, smem);
 }
 
 template <int NL>
@@ -522,19 +570,19 @@ hipError_t launch_direct(const ProjTask* tasks, int count, int64_t M64, int NL, 
                 g.xs[xi] = t.x;
             }
             const int c = g.count++;
-            g.payload[c] = t.payload;
-            g.scale[c] = t.scale;
-            g.y[c] = t.y;
-            g.n[c] = t.N;
-            g.k[c] = static_cast<uint16_t>(t.K);
-            g.x_idx[c] = static_cast<uint8_t>(xi);
-            g.fmt[c] = static_cast<uint8_t>(t.fmt);
+            DirectProj& d = g.proj[c];
+            d.payload = t.payload;
+            d.scale = t.scale;
+            d.y = t.y;
+            d.n = t.N;
+            d.k_fmt_x = static_cast<uint32_t>(t.K) | static_cast<uint32_t>(t.fmt) << 16 | static_cast<uint32_t>(xi) << 24;
             g.tile_begin[c] = tiles;
             tiles += t_tiles;
             ++done;
         }
         if (g.count == 0) return hipErrorInvalidValue;   // one projection alone exceeds a launch
         seg_fill_coarse(g.tile_begin, g.tile_coarse, g.count);
+        g.tiles = tiles;
         const int mark = timing_begin(stream);
         if (NL == 1)
             launch_direct_tm<1>(tm, tiles, g, stream);

@@ -840,11 +840,12 @@ __global__ __launch_bounds__(256) void split_gemm_kernel(SplitArgs a, int tiles_
 constexpr int kMaxSplitGrouped = 96;
 
 // One projection of a grouped launch: 36 bytes, so the kernel reads all of it
-// with two scalar loads (pointers as two dwords keep it dword-aligned).
-struct GroupedProj {
-    uint32_t payload[2];                // packed weights (int4 payload / int8 / FP8 codes)
-    uint32_t scale[2];                  // int4 (scale, min) pairs or int8 row scales
-    uint32_t y[2];                      // output, or the partial buffer [ks][M][N] when K spans ks > 1 chunks
+// with two scalar loads. Packed to 4-byte alignment (the pointers stay
+// pointers, so the compiler still knows they address global memory).
+struct __attribute__((packed, aligned(4))) GroupedProj {
+    const void* payload;                // packed weights (int4 payload / int8 / FP8 codes)
+    const void* scale;                  // int4 (scale, min) pairs or int8 row scales
+    float* y;                           // output, or the partial buffer [ks][M][N] when K spans ks > 1 chunks
     uint32_t img_off;                   // byte offset of the projection's limb image in the workspace
     uint32_t n_fmt;                     // N | format << 30 (a split projection has N < 2^27)
     int k;
@@ -941,10 +942,9 @@ __global__ __launch_bounds__(64 * kSmallWaves, 4) void split_grouped_kernel(Spli
     const int K = d.k;
     const uint32_t n_fmt = d.n_fmt;
     const uint32_t img_off = d.img_off;
-    auto ptr = [](const uint32_t (&v)[2]) { return reinterpret_cast<void*>((static_cast<uint64_t>(v[1]) << 32) | v[0]); };
-    const void* payload = ptr(d.payload);
-    const void* scale = ptr(d.scale);
-    float* y0 = static_cast<float*>(ptr(d.y));
+    const void* payload = d.payload;
+    const void* scale = d.scale;
+    float* y0 = d.y;
     asm volatile("" ::"s"(K), "s"(n_fmt), "s"(img_off), "s"(payload), "s"(scale), "s"(y0));
     const int N = static_cast<int>(n_fmt & 0x3fffffffu);
     const int fmt = static_cast<int>(n_fmt >> 30);
@@ -1249,14 +1249,9 @@ hipError_t split_impl(const ProjTask* tasks, int count, int64_t M64, int NL, hip
                 const int c = g.count++;
                 const int ks = split_chunks(t.K, plan.chunk_groups);
                 GroupedProj& d = g.proj[c];
-                auto put = [](uint32_t (&v)[2], const void* p) {
-                    const uint64_t u = reinterpret_cast<uintptr_t>(p);
-                    v[0] = static_cast<uint32_t>(u);
-                    v[1] = static_cast<uint32_t>(u >> 32);
-                };
-                put(d.payload, t.payload);
-                put(d.scale, t.scale);
-                put(d.y, ks > 1 ? static_cast<const void*>(wsb + part_off[ti]) : static_cast<const void*>(t.y));
+                d.payload = t.payload;
+                d.scale = t.scale;
+                d.y = ks > 1 ? reinterpret_cast<float*>(wsb + part_off[ti]) : t.y;
                 d.img_off = static_cast<uint32_t>(inputs[img_of[ti]].offset);
                 d.n_fmt = static_cast<uint32_t>(t.N) | static_cast<uint32_t>(t.fmt) << 30;
                 d.k = t.K;
