@@ -786,28 +786,53 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
         rexp[tm][2] = -v.z;
         rexp[tm][3] = -v.w;
     }
+    // the int8 scale first: the code sum of a row scaled far down would
+    // overflow if scaled back before it
+    auto value = [&](int tm, int tn, int e, float bv) {
+        float v = acc[tm][tn][e];
+        if constexpr (FMT == kFmtQ8) v *= escale[tn];
+        v = ldexpf(v, rexp[tm][e]);
+        if (a.bias) v += bv;
+        return v;
+    };
+    auto put = [](float* dst, float v) {
+        if constexpr (STREAM_Y) __builtin_nontemporal_store(v, dst);
+        else *dst = v;
+    };
+    // A tile whose rows all lie below M, in an output of less than 2^32
+    // bytes (every tile of the small-M launches, all but the last row block
+    // of the large-M ones), stores without row checks, addressed as the base
+    // plus a 32-bit byte offset per row.
+    if (m0 + BM <= M && static_cast<int64_t>(M) * N < (int64_t(1) << 30)) {
+        unsigned char* ybytes = reinterpret_cast<unsigned char*>(a.y);
+        const uint32_t rstride = static_cast<uint32_t>(N) * 4u;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int col = n0 + wn * TN * 16 + tn * 16 + li;
+            if (col >= N) continue;
+            const float bv = a.bias ? a.bias[col] : 0.0f;
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                uint32_t off = static_cast<uint32_t>(m0 + wm * TM * 16 + tm * 16 + 4 * lc) * rstride +
+                               static_cast<uint32_t>(col) * 4u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e, off += rstride)
+                    put(reinterpret_cast<float*>(ybytes + off), value(tm, tn, e, bv));
+            }
+        }
+        return;
+    }
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int col = n0 + wn * TN * 16 + tn * 16 + li;
         if (col >= N) continue;
-        const float sc = escale[tn];
         const float bv = a.bias ? a.bias[col] : 0.0f;
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int row = m0 + wm * TM * 16 + tm * 16 + 4 * lc + e;
-                if (row < M) {
-                    float v = acc[tm][tn][e];
-                    // the int8 scale first: the code sum of a row scaled far
-                    // down would overflow if scaled back before it
-                    if constexpr (FMT == kFmtQ8) v *= sc;
-                    v = ldexpf(v, rexp[tm][e]);
-                    if (a.bias) v += bv;
-                    float* dst = a.y + static_cast<int64_t>(row) * N + col;
-                    if constexpr (STREAM_Y) __builtin_nontemporal_store(v, dst);
-                    else *dst = v;
-                }
+                if (row < M) put(a.y + static_cast<int64_t>(row) * N + col, value(tm, tn, e, bv));
             }
         }
     }
