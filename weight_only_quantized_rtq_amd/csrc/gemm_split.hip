@@ -788,11 +788,13 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     }
     // the int8 scale first: the code sum of a row scaled far down would
     // overflow if scaled back before it
-    auto value = [&](int tm, int tn, int e, float bv) {
+    // (The call's bias test is taken once, below: a select per store would
+    // cost two instructions.)
+    auto value = [&](auto bias_tag, int tm, int tn, int e, float bv) {
         float v = acc[tm][tn][e];
         if constexpr (FMT == kFmtQ8) v *= escale[tn];
         v = ldexpf(v, rexp[tm][e]);
-        if (a.bias) v += bv;
+        if constexpr (decltype(bias_tag)::value) v += bv;
         return v;
     };
     auto put = [](float* dst, float v) {
@@ -803,39 +805,45 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     // bytes (every tile of the small-M launches, all but the last row block
     // of the large-M ones), stores without row checks, addressed as the base
     // plus a 32-bit byte offset per row.
-    if (m0 + BM <= M && static_cast<int64_t>(M) * N < (int64_t(1) << 30)) {
-        unsigned char* ybytes = reinterpret_cast<unsigned char*>(a.y);
-        const uint32_t rstride = static_cast<uint32_t>(N) * 4u;
+    auto store = [&](auto bias_tag) {
+        if (m0 + BM <= M && static_cast<int64_t>(M) * N < (int64_t(1) << 30)) {
+            unsigned char* ybytes = reinterpret_cast<unsigned char*>(a.y);
+            const uint32_t rstride = static_cast<uint32_t>(N) * 4u;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const int col = n0 + wn * TN * 16 + tn * 16 + li;
+                if (col >= N) continue;
+                float bv = 0.0f;
+                if constexpr (decltype(bias_tag)::value) bv = a.bias[col];
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    uint32_t off = static_cast<uint32_t>(m0 + wm * TM * 16 + tm * 16 + 4 * lc) * rstride +
+                                   static_cast<uint32_t>(col) * 4u;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e, off += rstride)
+                        put(reinterpret_cast<float*>(ybytes + off), value(bias_tag, tm, tn, e, bv));
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int tn = 0; tn < TN; ++tn) {
             const int col = n0 + wn * TN * 16 + tn * 16 + li;
             if (col >= N) continue;
-            const float bv = a.bias ? a.bias[col] : 0.0f;
+            float bv = 0.0f;
+            if constexpr (decltype(bias_tag)::value) bv = a.bias[col];
 #pragma unroll
             for (int tm = 0; tm < TM; ++tm) {
-                uint32_t off = static_cast<uint32_t>(m0 + wm * TM * 16 + tm * 16 + 4 * lc) * rstride +
-                               static_cast<uint32_t>(col) * 4u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e, off += rstride)
-                    put(reinterpret_cast<float*>(ybytes + off), value(tm, tn, e, bv));
+                for (int e = 0; e < 4; ++e) {
+                    const int row = m0 + wm * TM * 16 + tm * 16 + 4 * lc + e;
+                    if (row < M) put(a.y + static_cast<int64_t>(row) * N + col, value(bias_tag, tm, tn, e, bv));
+                }
             }
         }
-        return;
-    }
-#pragma unroll
-    for (int tn = 0; tn < TN; ++tn) {
-        const int col = n0 + wn * TN * 16 + tn * 16 + li;
-        if (col >= N) continue;
-        const float bv = a.bias ? a.bias[col] : 0.0f;
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int row = m0 + wm * TM * 16 + tm * 16 + 4 * lc + e;
-                if (row < M) put(a.y + static_cast<int64_t>(row) * N + col, value(tm, tn, e, bv));
-            }
-        }
-    }
+    };
+    if (a.bias) store(std::true_type{});
+    else store(std::false_type{});
 }
 
 // Large M: 128 x 128 tiles, 4 waves side by side along N, each 128 rows x 32 columns.
