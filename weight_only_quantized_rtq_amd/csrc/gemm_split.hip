@@ -156,8 +156,16 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(v[e]));
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    // Row maximum without the LDS crossbar: DPP rotations inside each row of
+    // 16 lanes, then the four rows' results read as scalars.
+    mx = fmaxf(mx, row_ror<8>(mx));
+    mx = fmaxf(mx, row_ror<4>(mx));
+    mx = fmaxf(mx, row_ror<2>(mx));
+    mx = fmaxf(mx, row_ror<1>(mx));
+    auto lane_f = [](float v, int l) {
+        return bitsf(static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(fbits(v)), l)));
+    };
+    mx = fmaxf(fmaxf(lane_f(mx, 0), lane_f(mx, 16)), fmaxf(lane_f(mx, 32), lane_f(mx, 48)));
     int E = 0;
     (void)frexpf(mx, &E);
     const int ex = 15 - E;
@@ -181,9 +189,10 @@ __global__ __launch_bounds__(256) void prep_kernel(PrepArgs p) {
             }
         }
         float s = ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
-        const float s1 = __shfl_xor(s, 1, 64);
+        // partner lanes c ^ 1, then c ^ 2, inside each quad (DPP quad_perm)
+        const float s1 = bitsf(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(fbits(s)), 0xb1, 0xf, 0xf, true)));
         s = (c & 1) ? s1 + s : s + s1;
-        const float s2 = __shfl_xor(s, 2, 64);
+        const float s2 = bitsf(static_cast<uint32_t>(__builtin_amdgcn_mov_dpp(static_cast<int>(fbits(s)), 0x4e, 0xf, 0xf, true)));
         s = (c & 2) ? s2 + s : s + s2;
         const int g = 16 * j + (lane >> 2);
         if (g < G) {
