@@ -22,34 +22,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h"
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 126 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33435.938, "write_kib": 33544.33,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+    ("m80", "split16"): {"fetch_kib": 33452.848, "write_kib": 32692.677,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 38947.626, "write_kib": 33246.996,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+    ("m80", "split"): {"fetch_kib": 39024.776, "write_kib": 32699.016,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27875.61, "write_kib": 34165.279,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+    ("m80", "bf16"): {"fetch_kib": 27880.925, "write_kib": 32702.768,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 480 dispatches per counter run
     # (5 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 103437.235, "write_kib": 232522.647,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+    ("m65536", "split16"): {"fetch_kib": 105209.388, "write_kib": 261309.155,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
-    ("m65536", "split"): {"fetch_kib": 175770.701, "write_kib": 230805.257,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+    ("m65536", "split"): {"fetch_kib": 183884.651, "write_kib": 268194.763,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
-    ("m65536", "bf16"): {"fetch_kib": 51863.532, "write_kib": 233781.815,
-         "fetch_factor": 1.99986, "write_factor": 1.0,
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+    ("m65536", "bf16"): {"fetch_kib": 52645.354, "write_kib": 264014.337,
+         "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "d0c833ccb33be36ba652725e28b62f4afc7f173978599695644b88c772464ae0"},
+         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
 }
 
 
