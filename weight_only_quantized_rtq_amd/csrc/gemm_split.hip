@@ -815,6 +815,32 @@ __device__ __forceinline__ void split_tile(const SplitArgs& a, int m0, int n0, i
     // of the large-M ones), stores without row checks, addressed as the base
     // plus a 32-bit byte offset per row.
     auto store = [&](auto bias_tag) {
+        constexpr int BN = WN * TN * 16;
+        if (m0 + BM <= M && n0 + BN <= N && static_cast<int64_t>(M) * N < (int64_t(1) << 30)) {
+            // Whole tile inside the output: no checks at all, and each row's
+            // pieces from the wave's column tiles go out back to back, so a
+            // nontemporal line is complete before it leaves.
+            unsigned char* ybytes = reinterpret_cast<unsigned char*>(a.y);
+            const uint32_t rstride = static_cast<uint32_t>(N) * 4u;
+            const int col0 = n0 + wn * TN * 16 + li;
+            float bv[TN];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                bv[tn] = 0.0f;
+                if constexpr (decltype(bias_tag)::value) bv[tn] = a.bias[col0 + tn * 16];
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                uint32_t off = static_cast<uint32_t>(m0 + wm * TM * 16 + tm * 16 + 4 * lc) * rstride +
+                               static_cast<uint32_t>(col0) * 4u;
+#pragma unroll
+                for (int e = 0; e < 4; ++e, off += rstride)
+#pragma unroll
+                    for (int tn = 0; tn < TN; ++tn)
+                        put(reinterpret_cast<float*>(ybytes + off + tn * 64), value(bias_tag, tm, tn, e, bv[tn]));
+            }
+            return;
+        }
         if (m0 + BM <= M && static_cast<int64_t>(M) * N < (int64_t(1) << 30)) {
             unsigned char* ybytes = reinterpret_cast<unsigned char*>(a.y);
             const uint32_t rstride = static_cast<uint32_t>(N) * 4u;
