@@ -22,34 +22,34 @@ KERNEL_SOURCES = ("gemm_split.hip", "gemm.hip", "rtq_internal.h", "rtq_device.h"
 # profiles folder.
 RECORDS: dict = {
     # split_grouped_kernel<5, 2> (two fp16 limbs, eight waves), 12 blocks at M = 80: 126 dispatches per counter run
-    ("m80", "split16"): {"fetch_kib": 33452.848, "write_kib": 32692.677,
+    ("m80", "split16"): {"fetch_kib": 33278.474, "write_kib": 32640.027,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
     # split_grouped_kernel<5, 3> (exact three-limb split), same workload
-    ("m80", "split"): {"fetch_kib": 39024.776, "write_kib": 32699.016,
+    ("m80", "split"): {"fetch_kib": 38914.274, "write_kib": 32640.0,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
     # split_grouped_kernel<5, 1> (bf16 activations), same workload
-    ("m80", "bf16"): {"fetch_kib": 27880.925, "write_kib": 32702.768,
+    ("m80", "bf16"): {"fetch_kib": 27804.402, "write_kib": 32640.0,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 80658432,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
     # split_gemm_kernel<1|2, NL>, 12 blocks at M = 65536: 480 dispatches per counter run
     # (5 steps x 96 projections); algorithmic bytes are the per-launch average
-    ("m65536", "split16"): {"fetch_kib": 105209.388, "write_kib": 261309.155,
+    ("m65536", "split16"): {"fetch_kib": 105071.67, "write_kib": 235620.687,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
-    ("m65536", "split"): {"fetch_kib": 183884.651, "write_kib": 268194.763,
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
+    ("m65536", "split"): {"fetch_kib": 182665.95, "write_kib": 241984.573,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
-    ("m65536", "bf16"): {"fetch_kib": 52645.354, "write_kib": 264014.337,
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
+    ("m65536", "bf16"): {"fetch_kib": 52472.332, "write_kib": 237270.779,
          "fetch_factor": 1.99987, "write_factor": 1.0,
          "algorithmic_bytes": 419840512,
-         "sources_sha256": "37cc3c2978104615a7fb8c34bdb1dd468b4d3470eca46ea6af189c9a40d6c855"},
+         "sources_sha256": "4fc92872de08e16494f50e5e39f6f77fb1d5ec79f9d1d5e3b0d8d4e0ea03491d"},
 }
 
 
