@@ -887,7 +887,9 @@ constexpr int kLBM = kLWM * kLTM * 16;
 constexpr int kLBN = kLWN * kLTN * 16;
 // Prefetch leads of the large-M kernel per limb count. One or two limbs: the
 // x stages run a step ahead and the weights stream through a per-wave LDS ring
-// a chunk ahead, and three workgroups (four with one limb) still fit a CU.
+// a chunk ahead, and three workgroups still fit a CU (with one limb the LDS
+// would admit four, but the kernel's registers hold it to three: at 128 VGPRs
+// it spills).
 // Three limbs (24 KB stages) keep the registers-one-step-ahead schedule, which
 // fits three workgroups where the LDS ring would leave two.
 template <int NL> struct LargeLead { static constexpr int XL = NL == 3 ? 0 : 1, WL = NL == 3 ? 0 : 1; };
