@@ -971,9 +971,10 @@ __global__ __launch_bounds__(64 * kSmallWaves, 4) void split_grouped_kernel(Spli
     // projection, (column block, K chunk) within one. Consecutive tiles go to
     // one XCD, so the column tiles that read the same activation image share
     // that XCD's L2 instead of each fetching the image from memory.
-    // Argument loads in three rounds: the header with the coarse table, the
-    // run of the fine table the coarse table points at (which also holds the
-    // projection's first workgroup), and the projection's descriptor. The
+    // Argument loads in three dependent steps: the header with the coarse
+    // table, the run of the fine table the coarse table points at (which also
+    // holds the projection's first workgroup), and the projection's descriptor
+    // (which the compiler reads in two rounds: four rounds in all). The
     // launch's size comes with the arguments, not from the dispatch packet.
     constexpr int NC = seg_coarse_slots(kMaxSplitGrouped);
     static_assert(NC == 12, "the round-one operand list below names twelve coarse slots");
