@@ -225,7 +225,9 @@ rtq_status rtq_quantize_f8_host(const float* w, uint8_t* codes, int64_t N, int64
  *   pair arrays 16-byte aligned) run the exact three-limb split there.
  * Shapes the split path does not take (int8/FP8 K not a multiple of 32, x or
  * payload not 16-byte aligned, N*K >= 2^32) run on the fp32 kernels in every
- * mode. An unknown mode returns RTQ_ERR_FORMAT. */
+ * mode: correct, but several times slower than the split path (no error is
+ * returned; keep shapes inside these conditions for the fast route). An
+ * unknown mode returns RTQ_ERR_FORMAT. */
 enum { RTQ_MATH_SPLIT_BF16 = 0, RTQ_MATH_FP32_MFMA = 1, RTQ_MATH_BF16 = 2, RTQ_MATH_SPLIT_F16 = 3 };
 
 /* rtq_gemm_q4 / _q8 / _f8 with the format as an argument (fmt = RTQ_FMT_Q4,
